@@ -1,0 +1,296 @@
+/*
+ * lbm_oracle.c -- plain, slow, obviously correct CPU oracle for the D3Q19 BGK
+ * lattice Boltzmann update with halfway bounce-back and Guo body forcing.
+ *
+ * TEST INFRASTRUCTURE ONLY: called by the tests, by the smoke check and by
+ * the benchmark's CPU-baseline leg.  The product (GPU) path never loads it.
+ *
+ * Single-threaded, fp64 throughout (long double for the global sums), built
+ * with -O2 -ffp-contract=off.  Each time step is written exactly as the
+ * lattice Boltzmann equation splits it -- a collision pass over every cell
+ * into a separate post-collision array, then a streaming pass that pulls
+ * from it -- with no fusion, blocking or reordering.
+ *
+ * What the pages fix, and where:
+ *  - BGK lattice Boltzmann equation, dt = 1:  PortLBM page ("PortLBM: A
+ *    Portable Lattice Boltzmann Tool Leveraging SYCL on AMD, NVIDIA, and
+ *    Intel GPUs"), section 3.1, Eq. (1); its split into a collision and a
+ *    streaming step, section 3.3, Eq. (3).
+ *  - Second-order polynomial equilibrium with coefficients 1, 3, 9/2, -3/2:
+ *    PortLBM page, section 3.1, Eq. (2).
+ *  - D3Q19 weights 1/3 (rest), 1/18 (6 axis), 1/36 (12 diagonal) and the
+ *    velocity set inside {-1,0,1}^3: codechina page ("GPU加速LBM流体仿真"),
+ *    sections 2.1 and 2.2.
+ *  - Halfway bounce-back at fluid-solid links: PortLBM page, section 3.1,
+ *    last paragraph; the same per-link rule in every streaming scheme:
+ *    fieldcraft page ("GPU lattice Boltzmann: streaming layout and
+ *    performance"), first section.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *  - Direction order: lexicographic over (c_z, c_y, c_x) of the vectors in
+ *    {-1,0,1}^3 with |c|^2 <= 2 (PortLBM's 2-D raster, Fig. 2, extended to 3-D).
+ *  - Equilibrium: the compressible form w rho (1 + 3 c.u + 9/2 (c.u)^2 - 3/2 u^2)
+ *    with u = (sum c f + F/2) / rho.
+ *  - Forcing: Guo, Zheng and Shi (Phys. Rev. E 65, 046308, 2002),
+ *    F_q = (1 - omega/2) w_q [3 (c_q - u) + 9 (c_q.u) c_q] . F, with F a
+ *    constant force density.
+ *  - tau = +inf means omega = 0: collision is the identity (streaming only).
+ *  - Cells outside a non-periodic face count as solid.
+ */
+#include "lbm_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int32_t C[ORC_Q][3];
+static double W[ORC_Q];
+static int32_t OPP[ORC_Q];
+static int tables_ready = 0;
+
+/* Build the velocity set by enumeration rather than from a typed table. */
+static void build_tables(void)
+{
+    if (tables_ready) return;
+    int q = 0;
+    for (int cz = -1; cz <= 1; ++cz)
+        for (int cy = -1; cy <= 1; ++cy)
+            for (int cx = -1; cx <= 1; ++cx) {
+                int n2 = cx * cx + cy * cy + cz * cz;
+                if (n2 > 2) continue;
+                C[q][0] = cx;
+                C[q][1] = cy;
+                C[q][2] = cz;
+                W[q] = (n2 == 0) ? 1.0 / 3.0 : (n2 == 1) ? 1.0 / 18.0 : 1.0 / 36.0;
+                ++q;
+            }
+    for (int a = 0; a < ORC_Q; ++a)
+        for (int p = 0; p < ORC_Q; ++p)
+            if (C[p][0] == -C[a][0] && C[p][1] == -C[a][1] && C[p][2] == -C[a][2]) OPP[a] = p;
+    tables_ready = 1;
+}
+
+void orc_lattice(int32_t c[ORC_Q][3], double w[ORC_Q], int32_t opp[ORC_Q])
+{
+    build_tables();
+    for (int q = 0; q < ORC_Q; ++q) {
+        for (int a = 0; a < 3; ++a) c[q][a] = C[q][a];
+        w[q] = W[q];
+        opp[q] = OPP[q];
+    }
+}
+
+static double omega_of(const orc_box *b)
+{
+    return isinf(b->tau) ? 0.0 : 1.0 / b->tau;
+}
+
+void orc_equilibrium(double rho, const double u[3], double feq[ORC_Q])
+{
+    build_tables();
+    double usq = u[0] * u[0] + u[1] * u[1] + u[2] * u[2];
+    for (int q = 0; q < ORC_Q; ++q) {
+        double cu = C[q][0] * u[0] + C[q][1] * u[1] + C[q][2] * u[2];
+        feq[q] = W[q] * rho * (1.0 + 3.0 * cu + 4.5 * cu * cu - 1.5 * usq);
+    }
+}
+
+void orc_guo_term(double omega, const double u[3], const double F[3], double out[ORC_Q])
+{
+    build_tables();
+    for (int q = 0; q < ORC_Q; ++q) {
+        double cu = C[q][0] * u[0] + C[q][1] * u[1] + C[q][2] * u[2];
+        double s = 0.0;
+        for (int a = 0; a < 3; ++a) s += (3.0 * (C[q][a] - u[a]) + 9.0 * cu * C[q][a]) * F[a];
+        out[q] = (1.0 - 0.5 * omega) * W[q] * s;
+    }
+}
+
+void orc_cell_moments(const orc_box *b, const double f[ORC_Q], double *rho, double u[3])
+{
+    build_tables();
+    double r = 0.0, j[3] = {0.0, 0.0, 0.0};
+    for (int q = 0; q < ORC_Q; ++q) {
+        r += f[q];
+        for (int a = 0; a < 3; ++a) j[a] += C[q][a] * f[q];
+    }
+    *rho = r;
+    for (int a = 0; a < 3; ++a) u[a] = (j[a] + 0.5 * b->force[a]) / r;
+}
+
+void orc_collide(const orc_box *b, const double f[ORC_Q], double post[ORC_Q])
+{
+    double rho, u[3], feq[ORC_Q], fq[ORC_Q];
+    double omega = omega_of(b);
+    orc_cell_moments(b, f, &rho, u);
+    orc_equilibrium(rho, u, feq);
+    orc_guo_term(omega, u, b->force, fq);
+    for (int q = 0; q < ORC_Q; ++q) post[q] = f[q] - omega * (f[q] - feq[q]) + fq[q];
+}
+
+static int64_t ncells(const orc_box *b)
+{
+    return b->nx * b->ny * b->nz;
+}
+
+static int is_solid(const uint8_t *mask, int64_t cell)
+{
+    return mask != NULL && mask[cell] != 0;
+}
+
+/* Cell index of (x + dx, y + dy, z + dz), wrapped on periodic axes; -1 if it
+ * lies beyond a non-periodic face. */
+static int64_t neighbour(const orc_box *b, int64_t x, int64_t y, int64_t z, int dx, int dy, int dz)
+{
+    int64_t p[3] = {x + dx, y + dy, z + dz};
+    int64_t n[3] = {b->nx, b->ny, b->nz};
+    for (int a = 0; a < 3; ++a) {
+        if (p[a] >= 0 && p[a] < n[a]) continue;
+        if (!b->periodic[a]) return -1;
+        p[a] = (p[a] + n[a]) % n[a];
+    }
+    return p[0] + b->nx * (p[1] + b->ny * p[2]);
+}
+
+int orc_init_equilibrium(const orc_box *b, const uint8_t *mask, const double *rho0,
+                         const double *u0, double *f)
+{
+    build_tables();
+    int64_t N = ncells(b);
+    for (int64_t x = 0; x < N; ++x) {
+        double feq[ORC_Q];
+        if (is_solid(mask, x)) {
+            for (int q = 0; q < ORC_Q; ++q) f[q * N + x] = 0.0;
+            continue;
+        }
+        double rho = rho0 ? rho0[x] : 1.0;
+        double u[3] = {0.0, 0.0, 0.0};
+        if (u0)
+            for (int a = 0; a < 3; ++a) u[a] = u0[a * N + x];
+        orc_equilibrium(rho, u, feq);
+        for (int q = 0; q < ORC_Q; ++q) f[q * N + x] = feq[q];
+    }
+    return 0;
+}
+
+/* Collision pass: post[q][x] for every cell (0 on solid cells). */
+static void collide_all(const orc_box *b, const uint8_t *mask, const double *f, double *post)
+{
+    int64_t N = ncells(b);
+    for (int64_t x = 0; x < N; ++x) {
+        double in[ORC_Q], out[ORC_Q];
+        if (is_solid(mask, x)) {
+            for (int q = 0; q < ORC_Q; ++q) post[q * N + x] = 0.0;
+            continue;
+        }
+        for (int q = 0; q < ORC_Q; ++q) in[q] = f[q * N + x];
+        orc_collide(b, in, out);
+        for (int q = 0; q < ORC_Q; ++q) post[q * N + x] = out[q];
+    }
+}
+
+/* Streaming pass (pull): the value arriving at x along c_q left x - c_q, unless
+ * that cell is solid or outside, in which case the population that left x
+ * along -c_q is reflected back at the link midpoint. */
+static void stream_all(const orc_box *b, const uint8_t *mask, const double *post, double *fnew)
+{
+    int64_t N = ncells(b);
+    for (int64_t z = 0; z < b->nz; ++z)
+        for (int64_t y = 0; y < b->ny; ++y)
+            for (int64_t xx = 0; xx < b->nx; ++xx) {
+                int64_t x = xx + b->nx * (y + b->ny * z);
+                for (int q = 0; q < ORC_Q; ++q) {
+                    if (is_solid(mask, x)) {
+                        fnew[q * N + x] = 0.0;
+                        continue;
+                    }
+                    int64_t src = neighbour(b, xx, y, z, -C[q][0], -C[q][1], -C[q][2]);
+                    if (src < 0 || is_solid(mask, src))
+                        fnew[q * N + x] = post[OPP[q] * N + x];
+                    else
+                        fnew[q * N + x] = post[q * N + src];
+                }
+            }
+}
+
+int orc_run(const orc_box *b, const uint8_t *mask, double *f, int64_t nsteps)
+{
+    build_tables();
+    int64_t N = ncells(b);
+    if (nsteps <= 0) return 0;
+    double *post = (double *)malloc(sizeof(double) * ORC_Q * (size_t)N);
+    if (!post) return -1;
+    for (int64_t t = 0; t < nsteps; ++t) {
+        collide_all(b, mask, f, post);
+        stream_all(b, mask, post, f); /* f is overwritten only after post is complete */
+    }
+    free(post);
+    return 0;
+}
+
+int orc_step_cells(const orc_box *b, const uint8_t *mask, const double *f, int64_t ncell,
+                   const int64_t *cells, double *out)
+{
+    build_tables();
+    int64_t N = ncells(b);
+    for (int64_t k = 0; k < ncell; ++k) {
+        int64_t x = cells[k];
+        double *o = out + k * ORC_Q;
+        if (x < 0 || x >= N) return -1;
+        if (is_solid(mask, x)) {
+            for (int q = 0; q < ORC_Q; ++q) o[q] = 0.0;
+            continue;
+        }
+        int64_t xx = x % b->nx, y = (x / b->nx) % b->ny, z = x / (b->nx * b->ny);
+        for (int q = 0; q < ORC_Q; ++q) {
+            int64_t src = neighbour(b, xx, y, z, -C[q][0], -C[q][1], -C[q][2]);
+            int use_bb = (src < 0 || is_solid(mask, src));
+            int64_t from = use_bb ? x : src;
+            double in[ORC_Q], post[ORC_Q];
+            for (int p = 0; p < ORC_Q; ++p) in[p] = f[p * N + from];
+            orc_collide(b, in, post);
+            o[q] = use_bb ? post[OPP[q]] : post[q];
+        }
+    }
+    return 0;
+}
+
+void orc_moments(const orc_box *b, const uint8_t *mask, const double *f, double *rho, double *u)
+{
+    build_tables();
+    int64_t N = ncells(b);
+    for (int64_t x = 0; x < N; ++x) {
+        if (is_solid(mask, x)) {
+            rho[x] = 0.0;
+            for (int a = 0; a < 3; ++a) u[a * N + x] = 0.0;
+            continue;
+        }
+        double in[ORC_Q], r, v[3];
+        for (int q = 0; q < ORC_Q; ++q) in[q] = f[q * N + x];
+        orc_cell_moments(b, in, &r, v);
+        rho[x] = r;
+        for (int a = 0; a < 3; ++a) u[a * N + x] = v[a];
+    }
+}
+
+void orc_totals(const orc_box *b, const uint8_t *mask, const double *f, double out[5])
+{
+    build_tables();
+    int64_t N = ncells(b);
+    long double m = 0.0L, p[3] = {0.0L, 0.0L, 0.0L}, ke = 0.0L;
+    for (int64_t x = 0; x < N; ++x) {
+        if (is_solid(mask, x)) continue;
+        double in[ORC_Q], r, v[3];
+        for (int q = 0; q < ORC_Q; ++q) {
+            in[q] = f[q * N + x];
+            m += (long double)in[q];
+        }
+        orc_cell_moments(b, in, &r, v);
+        for (int a = 0; a < 3; ++a) p[a] += (long double)r * (long double)v[a];
+        ke += 0.5L * (long double)r * ((long double)v[0] * v[0] + (long double)v[1] * v[1] +
+                                        (long double)v[2] * v[2]);
+    }
+    out[0] = (double)m;
+    for (int a = 0; a < 3; ++a) out[1 + a] = (double)p[a];
+    out[4] = (double)ke;
+}

@@ -1,0 +1,68 @@
+/*
+ * lbm_oracle.h -- C interface of the CPU oracle for the fused D3Q19 BGK
+ * collide-and-stream update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The oracle exists to check the GPU path; only
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load it.  It shares no code, header, table or helper with the GPU library.
+ *
+ * Every array of populations is "canonical": double f[19][N], direction-major,
+ * cell = x + nx*(y + ny*z), directions in the oracle's own order (see
+ * orc_lattice).  f holds the pre-collision populations f(t) of the lattice
+ * Boltzmann equation (PortLBM page, section 3.1, Eq. 1).  Solid cells hold 0.
+ */
+#ifndef LBM_ORACLE_H
+#define LBM_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORC_Q 19
+
+typedef struct {
+    int64_t nx, ny, nz;
+    int32_t periodic[3]; /* 1: periodic axis; 0: halfway bounce-back wall beyond both faces */
+    double tau;          /* BGK relaxation time; +inf gives omega = 0 (no collision) */
+    double force[3];     /* constant body-force density, Guo forcing; zeros = off */
+} orc_box;
+
+/* Velocity set, weights and opposite-direction table. */
+void orc_lattice(int32_t c[ORC_Q][3], double w[ORC_Q], int32_t opp[ORC_Q]);
+
+/* Second-order equilibrium of one cell. */
+void orc_equilibrium(double rho, const double u[3], double feq[ORC_Q]);
+
+/* Guo forcing term of one cell (u includes the F/2 shift). */
+void orc_guo_term(double omega, const double u[3], const double F[3], double out[ORC_Q]);
+
+/* BGK collision of one cell: post = f - omega (f - feq) + F_q. */
+void orc_collide(const orc_box *b, const double f[ORC_Q], double post[ORC_Q]);
+
+/* Density and velocity (u includes F/2) of one cell. */
+void orc_cell_moments(const orc_box *b, const double f[ORC_Q], double *rho, double u[3]);
+
+/* f := equilibrium(rho0, u0) on fluid cells, 0 on solid cells.  rho0 == NULL
+ * means 1 everywhere, u0 == NULL means 0; u0 is [3][N]. mask may be NULL. */
+int orc_init_equilibrium(const orc_box *b, const uint8_t *mask, const double *rho0,
+                         const double *u0, double *f);
+
+/* Advance f by nsteps (collide, then stream with halfway bounce-back). */
+int orc_run(const orc_box *b, const uint8_t *mask, double *f, int64_t nsteps);
+
+/* One step evaluated only at the listed cells: out[k][19] = f(t+1) at cells[k]. */
+int orc_step_cells(const orc_box *b, const uint8_t *mask, const double *f, int64_t ncells,
+                   const int64_t *cells, double *out);
+
+/* rho[N], u[3][N] from f; zeros on solid cells. */
+void orc_moments(const orc_box *b, const uint8_t *mask, const double *f, double *rho, double *u);
+
+/* out = {mass, Px, Py, Pz, kinetic energy} summed over fluid cells in long double. */
+void orc_totals(const orc_box *b, const uint8_t *mask, const double *f, double out[5]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,351 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: exact
+rational identities of the velocity set, the page's printed weights, closed
+forms of textbook flows, a brute-force search for streaming, invariants.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import lbm_inputs as li
+
+Q = 19
+
+
+def _read_table(path):
+    rows = []
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _exact_weights(w):
+    # every weight is k/36 for an integer k; recover k and insist the double is
+    # the correctly rounded k/36.
+    out = []
+    for x in w:
+        k = round(x * 36)
+        assert float(Fraction(k, 36)) == x
+        out.append(Fraction(k, 36))
+    return out
+
+
+# --------------------------------------------------------------- P1 lattice
+
+def test_velocity_set_and_order():
+    c, w, opp = oracle.lattice()
+    vecs = [tuple(v) for v in c.tolist()]
+    expected = [(cx, cy, cz) for cz in (-1, 0, 1) for cy in (-1, 0, 1) for cx in (-1, 0, 1)
+                if cx * cx + cy * cy + cz * cz <= 2]
+    assert vecs == expected                 # lexicographic over (c_z, c_y, c_x)
+    assert len(set(vecs)) == 19
+    assert vecs[9] == (0, 0, 0)
+    for q in range(Q):
+        assert tuple(-c[q]) == tuple(c[opp[q]])
+        assert opp[q] == 18 - q            # a property of this ordering
+
+
+def test_weights_match_page(golden_dir):
+    c, w, _ = oracle.lattice()
+    table = {int(r[0]): (int(r[1]), Fraction(int(r[2]), int(r[3])))
+             for r in _read_table(os.path.join(golden_dir, "d3q19_weights.txt"))}
+    n2 = (c * c).sum(axis=1)
+    for cls, (mult, wt) in table.items():
+        sel = np.nonzero(n2 == cls)[0]
+        assert sel.size == mult
+        for q in sel:
+            assert w[q] == float(wt)
+
+
+def test_velocity_set_isotropy_exact():
+    c, w, _ = oracle.lattice()
+    W = _exact_weights(w)
+    C = c.tolist()
+    assert sum(W) == 1
+    for a in range(3):
+        assert sum(W[q] * C[q][a] for q in range(Q)) == 0
+    for a, b in itertools.product(range(3), repeat=2):
+        s = sum(W[q] * C[q][a] * C[q][b] for q in range(Q))
+        assert s == (Fraction(1, 3) if a == b else 0)
+    for a, b, d in itertools.product(range(3), repeat=3):
+        assert sum(W[q] * C[q][a] * C[q][b] * C[q][d] for q in range(Q)) == 0
+    for a, b, d, e in itertools.product(range(3), repeat=4):
+        s = sum(W[q] * C[q][a] * C[q][b] * C[q][d] * C[q][e] for q in range(Q))
+        iso = Fraction(int(a == b and d == e) + int(a == d and b == e) + int(a == e and b == d), 9)
+        assert s == iso
+
+
+# --------------------------------------------------------- P2 equilibrium
+
+@pytest.mark.parametrize("rho,u", [(1.0, (0.0, 0.0, 0.0)), (1.03, (0.05, -0.02, 0.01)),
+                                   (0.97, (-0.1, 0.07, 0.12))])
+def test_equilibrium_moments(rho, u):
+    c, _, _ = oracle.lattice()
+    u = np.array(u)
+    feq = oracle.equilibrium(rho, u)
+    cf = c.astype(np.float64)
+    tol = 1e-15
+    assert abs(feq.sum() - rho) <= tol * 4
+    np.testing.assert_allclose(cf.T @ feq, rho * u, rtol=0, atol=tol * 4)
+    second = np.einsum("qa,qb,q->ab", cf, cf, feq)
+    np.testing.assert_allclose(second, rho * np.eye(3) / 3 + rho * np.outer(u, u), rtol=0, atol=tol * 8)
+    third = np.einsum("qa,qb,qc,q->abc", cf, cf, cf, feq)
+    d = np.eye(3)
+    want = rho / 3 * (np.einsum("a,bc->abc", u, d) + np.einsum("b,ac->abc", u, d)
+                      + np.einsum("c,ab->abc", u, d))
+    np.testing.assert_allclose(third, want, rtol=0, atol=tol * 8)
+
+
+@pytest.mark.parametrize("tau", [0.51, 0.8, 1.7])
+def test_equilibrium_is_fixed_point(tau):
+    box = oracle.Box(1, 1, 1, tau=tau)
+    for rho, u in [(1.0, (0.02, 0.0, -0.03)), (1.1, (-0.08, 0.05, 0.02))]:
+        feq = oracle.equilibrium(rho, np.array(u))
+        post = oracle.collide(box, feq)
+        assert np.max(np.abs(post - feq)) <= 8 * np.finfo(np.float64).eps * feq.max()
+
+
+def test_guo_term_moments():
+    # zeroth moment 0, first moment (1 - omega/2) F: what makes the momentum
+    # gain per step exactly F with u shifted by F/2.
+    c, _, _ = oracle.lattice()
+    for omega in (0.0, 1.0 / 0.7, 1.0 / 0.55):
+        u = np.array([0.03, -0.01, 0.02])
+        F = np.array([1e-3, -2e-3, 5e-4])
+        g = oracle.guo_term(omega, u, F)
+        assert abs(g.sum()) < 1e-18
+        np.testing.assert_allclose(c.T.astype(float) @ g, (1 - omega / 2) * F, rtol=1e-13, atol=1e-19)
+
+
+# ------------------------------------------------------ P3 conservation
+
+def _random_state(box, seed=3, mask=None):
+    rho, u = li.random_fields(box.nx, box.ny, box.nz, seed=seed)
+    return oracle.init_equilibrium(box, mask, rho, u)
+
+
+def test_mass_momentum_conserved_periodic():
+    box = oracle.Box(8, 6, 5, tau=0.6)
+    f0 = _random_state(box)
+    t0 = oracle.totals(box, f0)
+    f1 = oracle.run(box, f0, 30)
+    t1 = oracle.totals(box, f1)
+    assert abs(t1["mass"] - t0["mass"]) / t0["mass"] < 1e-14
+    assert np.max(np.abs(t1["momentum"] - t0["momentum"])) / t0["mass"] < 1e-14
+
+
+def test_momentum_gain_with_force():
+    F = (1e-4, -3e-5, 2e-5)
+    box = oracle.Box(7, 5, 6, tau=0.75, force=F)
+    f0 = _random_state(box, seed=11)
+    t0 = oracle.totals(box, f0)
+    n = 25
+    f1 = oracle.run(box, f0, n)
+    t1 = oracle.totals(box, f1)
+    assert abs(t1["mass"] - t0["mass"]) / t0["mass"] < 1e-14
+    np.testing.assert_allclose(t1["momentum"] - t0["momentum"], n * box.n * np.array(F),
+                               rtol=1e-9, atol=1e-12)
+
+
+def test_mass_conserved_with_walls_and_mask():
+    box = oracle.Box(9, 7, 6, periodic=(1, 0, 0), tau=0.65, force=(1e-5, 0, 0))
+    mask = li.random_mask(9, 7, 6, fraction=0.25, seed=4)
+    f0 = _random_state(box, seed=5, mask=mask)
+    m0 = oracle.totals(box, f0, mask)["mass"]
+    f1 = oracle.run(box, f0, 20, mask)
+    assert abs(oracle.totals(box, f1, mask)["mass"] - m0) / m0 < 1e-14
+    solid = mask.astype(bool)
+    assert np.all(f1[:, solid] == 0.0)
+
+
+# ------------------------------------------------ P5 / P6 streaming exactness
+
+def _brute_stream(box, f, mask):
+    """Streaming by exhaustive search: the value arriving at x along c_q comes
+    from the cell y with y + c_q == x (wrapping only on periodic axes)."""
+    c, _, opp = oracle.lattice()
+    dims = (box.nx, box.ny, box.nz)
+    cells = [(x, y, z) for z in range(box.nz) for y in range(box.ny) for x in range(box.nx)]
+    lin = {p: i for i, p in enumerate(cells)}
+    out = np.zeros_like(f)
+    for xi, xp in enumerate(cells):
+        if mask is not None and mask[xi]:
+            continue
+        for q in range(Q):
+            src = None
+            for yi, yp in enumerate(cells):
+                ok = True
+                for a in range(3):
+                    t = yp[a] + c[q][a]
+                    if box.periodic[a]:
+                        t %= dims[a]
+                    if t != xp[a]:
+                        ok = False
+                        break
+                if ok:
+                    src = yi
+                    break
+            if src is None or (mask is not None and mask[src]):
+                out[q, xi] = f[opp[q], xi]
+            else:
+                out[q, xi] = f[q, src]
+    del lin
+    return out
+
+
+@pytest.mark.parametrize("periodic,with_mask", [((1, 1, 1), False), ((1, 0, 1), False),
+                                                ((1, 1, 1), True), ((0, 1, 0), True)])
+def test_streaming_matches_brute_force_4cubed(periodic, with_mask):
+    box = oracle.Box(4, 4, 4, periodic=periodic, tau=math.inf)   # omega = 0: no collision
+    rng = np.random.default_rng(123)
+    mask = li.random_mask(4, 4, 4, fraction=0.3, seed=9) if with_mask else None
+    f = rng.uniform(0.01, 1.0, size=(Q, box.n))
+    if mask is not None:
+        f[:, mask.astype(bool)] = 0.0
+    got = oracle.run(box, f, 1, mask)
+    want = _brute_stream(box, f, mask)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("periodic", [(1, 1, 1), (0, 1, 1), (0, 0, 0)])
+def test_streaming_is_permutation(periodic):
+    box = oracle.Box(6, 5, 4, periodic=periodic, tau=math.inf)
+    mask = li.random_mask(6, 5, 4, fraction=0.2, seed=2)
+    rng = np.random.default_rng(5)
+    f = rng.uniform(0.0, 1.0, size=(Q, box.n))
+    f[:, mask.astype(bool)] = 0.0
+    g = oracle.run(box, f, 1, mask)
+    fl = ~mask.astype(bool)
+    assert np.array_equal(np.sort(f[:, fl].ravel()), np.sort(g[:, fl].ravel()))
+    h = oracle.run(box, f, 7, mask)
+    assert np.array_equal(np.sort(f[:, fl].ravel()), np.sort(h[:, fl].ravel()))
+
+
+# --------------------------------------------------------- P8 uniform state
+
+def test_uniform_state_invariant():
+    box = oracle.Box(5, 4, 6, tau=0.7, force=(0, 0, 0))
+    rho = np.full(box.n, 1.02)
+    u = np.tile(np.array([[0.03], [-0.01], [0.02]]), (1, box.n))
+    f0 = oracle.init_equilibrium(box, None, rho, u)
+    f1 = oracle.run(box, f0, 10)
+    assert np.max(np.abs(f1 - f0)) < 1e-15
+
+
+# ------------------------------------------- P4 Poiseuille: closed form + slip
+
+def _poiseuille(tau, steps, g=1e-6, H=64):
+    box = oracle.Box(1, H, 1, periodic=(1, 0, 1), tau=tau, force=(0.0, 0.0, g))
+    f = oracle.init_equilibrium(box)
+    f = oracle.run(box, f, steps)
+    _, u = oracle.moments(box, f)
+    nu = (tau - 0.5) / 3.0
+    yp = np.arange(H) + 0.5          # distance from the wall plane at y = -1/2
+    exact = g * yp * (H - yp) / (2.0 * nu)
+    return u[2], exact, u[0], u[1]
+
+
+def test_poiseuille_gate():
+    # the benchmark channel: H = 64, tau = 0.9, g = 1e-6 along z, from rest.
+    # After 40000 steps the start-up transient is ~3e-6 of u_max.
+    uz, exact, ux, uy = _poiseuille(0.9, 40000, g=1e-6, H=64)
+    assert np.max(np.abs(ux)) == 0.0 and np.max(np.abs(uy)) < 1e-11 * exact.max()
+    assert np.max(np.abs(uz - exact)) / exact.max() < 1e-3
+
+
+@pytest.mark.parametrize("tau", [0.9, 0.6, 1.4])
+def test_poiseuille_bounce_back_slip(tau):
+    # Steady BGK + Guo + halfway bounce-back reproduces the parabola plus a
+    # constant slip u_s = g (16 L - 3) / (24 nu), L = (tau - 1/2)^2.  A narrow
+    # channel (H = 16) lets the transient die out to rounding level.
+    g, H = 1e-6, 16
+    nu = (tau - 0.5) / 3.0
+    steps = int(40.0 * H * H / (math.pi ** 2 * nu))
+    uz, exact, _, _ = _poiseuille(tau, steps, g=g, H=H)
+    lam = (tau - 0.5) ** 2
+    slip = g * (16 * lam - 3) / (24 * nu)
+    np.testing.assert_allclose(uz - exact, np.full_like(uz, slip), rtol=0, atol=1e-9 * exact.max())
+
+
+def test_poiseuille_exact_at_magic_tau():
+    # halfway bounce-back places the wall exactly at the link midpoint when
+    # (tau - 1/2)^2 = 3/16, so the steady profile is the parabola itself.
+    tau, H = 0.5 + math.sqrt(3.0 / 16.0), 16
+    nu = (tau - 0.5) / 3.0
+    uz, exact, _, _ = _poiseuille(tau, int(40.0 * H * H / (math.pi ** 2 * nu)), H=H)
+    assert np.max(np.abs(uz - exact)) < 1e-9 * exact.max()
+
+
+# ------------------------------------------------ P9 / P10 decaying flows
+
+def test_shear_wave_decay():
+    tau, L, A, t = 0.8, 32, 1e-4, 200
+    box = oracle.Box(1, L, 1, tau=tau)
+    rho, u = li.shear_wave(1, L, 1, amp=A)
+    f = oracle.run(box, oracle.init_equilibrium(box, None, rho, u), t)
+    _, uu = oracle.moments(box, f)
+    s = np.sin(2 * np.pi * np.arange(L) / L)
+    amp = (uu[2] @ s) / (s @ s)
+    nu = (tau - 0.5) / 3.0
+    k = 2 * np.pi / L
+    assert abs(amp / A - math.exp(-nu * k * k * t)) < 0.01 * math.exp(-nu * k * k * t)
+
+
+def _tgv_rate_error(n, tau=0.6, u0=1e-3):
+    """Relative error of the measured kinetic-energy decay exponent against
+    the Navier-Stokes law E(t)/E(0) = exp(-6 nu k^2 t), |K|^2 = 3 k^2, over a
+    fixed nu k^2 t (100 steps at n = 32)."""
+    box = oracle.Box(n, n, n, tau=tau)
+    nu = (tau - 0.5) / 3.0
+    k = 2 * np.pi / n
+    t = int(round(100 * (n / 32) ** 2))
+    rho, u = li.taylor_green(n, u0=u0)
+    f0 = oracle.init_equilibrium(box, None, rho, u)
+    e0 = oracle.totals(box, f0)["ke"]
+    e1 = oracle.totals(box, oracle.run(box, f0, t))["ke"]
+    return math.log(e1 / e0) / (-6.0 * nu * k * k * t) - 1.0
+
+
+def test_taylor_green_low_amplitude_decay():
+    # Low amplitude (Re = u0/(nu k) ~ 0.15) so the nonlinear term is negligible:
+    # the decay exponent must approach 6 nu k^2 at second order in k.
+    e16, e32 = _tgv_rate_error(16), _tgv_rate_error(32)
+    assert abs(e32) < 0.04
+    assert 3.6 < e16 / e32 < 4.4
+
+
+# ------------------------------------------------- consistency of helpers
+
+def test_step_cells_equals_run():
+    box = oracle.Box(6, 5, 7, periodic=(1, 0, 1), tau=0.7, force=(2e-5, 0, -1e-5))
+    mask = li.random_mask(6, 5, 7, fraction=0.2, seed=8)
+    f0 = _random_state(box, seed=6, mask=mask)
+    f1 = oracle.run(box, f0, 1, mask)
+    cells = np.arange(box.n)
+    got = oracle.step_cells(box, f0, cells, mask)
+    assert np.array_equal(got.T, f1)
+
+
+def test_moments_and_totals_are_plain_sums():
+    box = oracle.Box(5, 4, 3, tau=0.9, force=(1e-3, 2e-3, -1e-3))
+    mask = li.random_mask(5, 4, 3, fraction=0.3, seed=1)
+    f = _random_state(box, seed=2, mask=mask)
+    c, _, _ = oracle.lattice()
+    rho, u = oracle.moments(box, f, mask)
+    fl = ~mask.astype(bool)
+    r = f.sum(axis=0)
+    j = c.T.astype(float) @ f
+    np.testing.assert_allclose(rho[fl], r[fl], rtol=1e-15)
+    np.testing.assert_allclose(u[:, fl], (j[:, fl] + 0.5 * np.array(box.force)[:, None]) / r[fl], rtol=1e-13)
+    assert np.all(rho[~fl] == 0) and np.all(u[:, ~fl] == 0)
+    tot = oracle.totals(box, f, mask)
+    assert abs(tot["mass"] - f[:, fl].sum()) < 1e-12
