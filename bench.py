@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of the fused D3Q19 BGK step on one MI355X, with its HBM roofline.
+
+    python bench.py [--steps K] [--warmup W] [--workload porous256] [--scheme aa] [--layout stream]
+
+A "step" is one lattice time step: one fused collide-and-stream kernel over
+the whole box (alternating the even and odd kernels of the in-place pattern).
+Default workload: 256^3 periodic porous medium (overlapping spheres,
+r ~ U(6, 12), 2400 spheres -> porosity ~0.61), tau = 0.65, body force 1e-6
+along +x, fp32, one-lattice AA scheme, SoA layout.  Inputs are resident in HBM
+before timing starts.  Prints ONE JSON line.
+
+value = MLUPS over all cells (cells x steps / seconds / 1e6).
+roofline: the dominant kernel's algorithmic bytes per launch (152 B per fluid
+cell for fp32, 304 B for fp64, + 1 B per cell for the mask) over its mean
+launch time from HIP events on the launch stream, against 8 TB/s.
+cpu_baseline: the fp64 CPU oracle, single-threaded, on one step of the same box.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "MLUPS (million lattice updates/s) and % of HBM roofline, D3Q19 fp32, 1 GPU"
+
+
+def workload(name):
+    import lbm_inputs as li
+    if name == "porous256":
+        mask, ns = li.porous_mask(256)
+        return dict(shape=(256, 256, 256), periodic=(1, 1, 1), tau=0.65, force=(1e-6, 0.0, 0.0), mask=mask,
+                    rho=None, u=None, precision="f32", extra={"n_spheres": ns})
+    if name == "porous512":
+        mask, ns = li.porous_mask(512)
+        return dict(shape=(512, 512, 512), periodic=(1, 1, 1), tau=0.65, force=(1e-6, 0.0, 0.0), mask=mask,
+                    rho=None, u=None, precision="f32", extra={"n_spheres": ns})
+    if name == "tgv128":
+        rho, u = li.taylor_green(128, u0=0.04)
+        return dict(shape=(128, 128, 128), periodic=(1, 1, 1), tau=0.6, force=(0.0, 0.0, 0.0), mask=None,
+                    rho=rho, u=u, precision="f32", extra={})
+    if name == "sphere128":
+        return dict(shape=(128, 128, 128), periodic=(1, 1, 1), tau=0.7, force=(1e-6, 0.0, 0.0),
+                    mask=li.sphere_mask(128, radius=16), rho=None, u=None, precision="f32", extra={})
+    if name == "channel_f64":
+        return dict(shape=(64, 64, 256), periodic=(1, 0, 1), tau=0.9, force=(0.0, 0.0, 1e-6), mask=None,
+                    rho=None, u=None, precision="f64", extra={})
+    if name == "periodic256":
+        return dict(shape=(256, 256, 256), periodic=(1, 1, 1), tau=0.65, force=(0.0, 0.0, 0.0), mask=None,
+                    rho=None, u=None, precision="f32", extra={})
+    raise SystemExit(f"unknown workload {name}")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lattice_boltzmann_cfd_d3q19_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".hpp", ".cpp")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name, scheme, layout, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{scheme}_{layout}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != kernel_source_hash():
+        return None
+    key = f"bytes_per_launch_{kernel}"
+    return float(vals[key]) if key in vals else None
+
+
+def cpu_baseline(wl, budget_s=30.0):
+    """Time the single-threaded fp64 oracle on one step of the same box."""
+    import numpy as np
+    import oracle
+    box = oracle.Box(*wl["shape"], periodic=wl["periodic"], tau=wl["tau"], force=wl["force"])
+    f = oracle.init_equilibrium(box, wl["mask"], wl["rho"], wl["u"])
+    steps = 1
+    t0 = time.perf_counter()
+    f = oracle.run(box, f, steps, wl["mask"])
+    dt = time.perf_counter() - t0
+    del f
+    n = box.n
+    return {"value": round(n * steps / dt / 1e6, 3), "unit": "MLUPS", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} step of the full {'x'.join(map(str, wl['shape']))} box, fp64, "
+                      f"single thread, {dt:.1f} s",
+            "host_cpu": _cpu_model(), "host_threads": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="porous256")
+    ap.add_argument("--scheme", default="aa", choices=["aa", "ab"])
+    ap.add_argument("--layout", default="stream", choices=["stream", "bundle", "collision"])
+    ap.add_argument("--per-kernel-steps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if args.steps < 2 or args.steps % 2:
+        raise SystemExit("--steps must be even and >= 2 (the in-place scheme alternates two kernels)")
+
+    import numpy as np
+    import torch
+    from lattice_boltzmann_cfd_d3q19_amd import Lattice
+
+    wl = workload(args.workload)
+    shape = wl["shape"]
+    n = shape[0] * shape[1] * shape[2]
+    mask = wl["mask"]
+    n_fluid = n if mask is None else int(n - np.count_nonzero(mask))
+    prec = wl["precision"]
+    esize = 4 if prec == "f32" else 8
+
+    lat = Lattice(*shape, precision=prec, layout=args.layout, scheme=args.scheme, tau=wl["tau"],
+                  force=wl["force"])
+    lat.set_geometry(None if mask is None else torch.from_numpy(mask), wl["periodic"])
+    lat.init(None if wl["rho"] is None else torch.from_numpy(wl["rho"]),
+             None if wl["u"] is None else torch.from_numpy(wl["u"]))
+    stream = lat.stream
+
+    # warm-up
+    lat.step(args.warmup if args.warmup % 2 == 0 else args.warmup + 1)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    lat.step(args.steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    sec = ms_total / 1e3
+    mlups = n * args.steps / sec / 1e6
+
+    # per-kernel launch durations (events around single steps on the launch stream)
+    per = {}
+    if args.scheme == "aa":
+        names = ["aa_even", "aa_odd"]
+    else:
+        names = ["ab", "ab"]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.per_kernel_steps)]
+    for i in range(args.per_kernel_steps):
+        evs[i][0].record(stream)
+        lat.step(1)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_parity = lat.t - args.per_kernel_steps
+    for i, (a, b) in enumerate(evs):
+        per.setdefault(names[(t_parity + i) % 2], []).append(a.elapsed_time(b))
+    per_ms = {k: float(np.mean(v)) for k, v in per.items()}
+    dominant = max(per_ms, key=per_ms.get)
+    alg_bytes = 2 * 19 * esize * n_fluid + (n if mask is not None else 0)
+    achieved = alg_bytes / (per_ms[dominant] / 1e3) / 1e9
+    step_gbps = alg_bytes * args.steps / sec / 1e9
+
+    traffic = read_traffic(args.workload, args.scheme, args.layout, dominant)
+
+    # state sanity: finite moments after the run
+    rho, _ = lat.moments()
+    finite = bool(torch.isfinite(rho).all().item())
+    torch.cuda.synchronize()
+
+    # plain copy reference (torch copy kernel, 2 GiB moved)
+    src = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del src, dst
+
+    out = {
+        "metric": METRIC,
+        "value": round(mlups, 1),
+        "unit": "MLUPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prec,
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}_{args.scheme}_{args.layout}_{prec}",
+                   "box": list(shape), "scheme": args.scheme, "layout": args.layout, "tau": wl["tau"],
+                   "force": list(wl["force"]), "periodic": list(wl["periodic"]),
+                   "porosity": round(n_fluid / n, 4), **wl["extra"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None if traffic is None else int(traffic),
+                     "traffic_over_alg": None if traffic is None else round(traffic / alg_bytes, 4),
+                     "kernel": dominant, "alg_bytes_per_launch": alg_bytes,
+                     "kernel_ms": {k: round(v, 5) for k, v in per_ms.items()}},
+        "mflups": round(n_fluid * args.steps / sec / 1e6, 1),
+        "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "copy_GBps": round(copy_gbps, 1),
+        "state_finite": finite,
+        "kernel_source": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

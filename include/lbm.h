@@ -1,0 +1,148 @@
+/*
+ * lbm.h -- C ABI of the MI355X (gfx950) D3Q19 BGK collide-and-stream library
+ * (liblbm.so).
+ *
+ * The library advances the lattice Boltzmann equation with BGK relaxation
+ * (PortLBM page, "PortLBM: A Portable Lattice Boltzmann Tool Leveraging SYCL
+ * on AMD, NVIDIA, and Intel GPUs", section 3.1, Eq. 1) on a D3Q19 lattice
+ * (weights 1/3, 1/18, 1/36: codechina page "GPU加速LBM流体仿真", section 2.2),
+ * relaxing toward the second-order equilibrium (PortLBM section 3.1, Eq. 2,
+ * compressible form w rho (1 + 3 c.u + 9/2 (c.u)^2 - 3/2 u^2)), with halfway
+ * bounce-back on a solid mask (PortLBM section 3.1, last paragraph) and an
+ * optional constant body force (Guo, Zheng and Shi 2002 forcing term).
+ * Every step is one fused kernel: gather 19 populations, moments,
+ * equilibrium, forcing, relaxation, scatter 19 populations.
+ *
+ * Propagation schemes (PortLBM section 3.3; fieldcraft page "GPU lattice
+ * Boltzmann: streaming layout and performance", first section):
+ *   LBM_SCHEME_AB  two lattices; each cell pulls from the source lattice and
+ *                  writes post-collision values into the destination one.
+ *   LBM_SCHEME_AA  one lattice, in place.  Even steps read slot (q, x) and
+ *                  write (opposite(q), x); odd steps read (opposite(q), x - c_q)
+ *                  and write (q, x + c_q).  Each cell writes exactly the slots
+ *                  it read.
+ * Population layouts (PortLBM section 3.2, Fig. 2):
+ *   LBM_LAYOUT_STREAM     SoA: all cells of direction 0, then direction 1, ...
+ *   LBM_LAYOUT_BUNDLE     SoAoS: directions grouped in bundles of equal
+ *                         (c_y, c_z) (one stencil row each); cell-major
+ *                         inside a bundle.
+ *   LBM_LAYOUT_COLLISION  AoS: the 19 populations of a cell are contiguous.
+ *
+ * Conventions shared by every entry point:
+ *  - Cell index: cell = x + nx * (y + ny * z), N = nx * ny * nz.
+ *  - Canonical direction order q = 0..18: the vectors of {-1,0,1}^3 with
+ *    |c|^2 <= 2 in lexicographic order over (c_z, c_y, c_x); q = 9 is rest
+ *    and opposite(q) = 18 - q.
+ *  - "Canonical populations" f[19][N] (direction-major) are the
+ *    pre-collision populations f(t) of Eq. 1 at the current time t, whatever
+ *    the scheme stores internally.
+ *  - T is float for LBM_F32 and double for LBM_F64.
+ *  - Every pointer handed to the library is a device pointer on the current
+ *    HIP device; the caller allocates and owns all device memory and keeps it
+ *    alive while a handle refers to it.  The library never allocates or frees
+ *    device memory.
+ *  - All GPU work is enqueued on the handle's stream; no call blocks the host.
+ *    Launch failures are reported as LBM_ERR_HIP; faults inside a kernel
+ *    surface at the caller's next synchronisation of that stream.
+ *  - Argument and state errors are detected on the host before anything is
+ *    enqueued; on error nothing is enqueued and the handle is unchanged.
+ *  - Nothing is printed.  One handle must not be used from two threads at once.
+ */
+#ifndef LBM_H
+#define LBM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lbm_status;
+#define LBM_OK 0
+#define LBM_ERR_INVALID_ARGUMENT (-1) /* bad pointer, size, enum, tau, force, n */
+#define LBM_ERR_UNSUPPORTED (-2)      /* valid request outside what is built (e.g. N >= 2^31) */
+#define LBM_ERR_BAD_STATE (-3)        /* call out of order (step before init, ...) */
+#define LBM_ERR_MISALIGNED (-4)       /* population buffer not 256-byte aligned */
+#define LBM_ERR_HIP (-5)              /* the HIP runtime refused a launch */
+
+#define LBM_F32 0
+#define LBM_F64 1
+
+#define LBM_LAYOUT_STREAM 0
+#define LBM_LAYOUT_BUNDLE 1
+#define LBM_LAYOUT_COLLISION 2
+
+#define LBM_SCHEME_AB 0
+#define LBM_SCHEME_AA 1
+
+typedef struct lbm_desc {
+    int64_t nx, ny, nz;  /* box size in cells, each >= 1 */
+    int32_t precision;   /* LBM_F32 or LBM_F64 */
+    int32_t layout;      /* LBM_LAYOUT_* */
+    int32_t scheme;      /* LBM_SCHEME_* */
+    int32_t reserved;    /* must be 0 */
+    double tau;          /* BGK relaxation time, > 1/2; +INFINITY means omega = 0
+                            (collision-free: steps only stream and bounce back) */
+    double force[3];     /* constant body-force density (Guo forcing); zeros = off */
+} lbm_desc;
+
+typedef struct lbm_sim lbm_sim; /* opaque handle (host memory only) */
+
+/* Size of one population buffer, 19 * N * sizeof(T) bytes, and how many the
+ * scheme needs (2 for AB, 1 for AA).  Host only; never touches the GPU. */
+lbm_status lbm_buffer_bytes(const lbm_desc *desc, size_t *bytes_per_buffer, int32_t *n_buffers);
+
+/* Create a handle over caller-owned population memory.
+ *   buf0, buf1   device buffers of lbm_buffer_bytes() bytes each, 256-byte
+ *                aligned.  AB needs both (distinct, not overlapping); AA
+ *                takes buf0 and requires buf1 == NULL.
+ *   hip_stream   hipStream_t to enqueue on; NULL = the null stream.
+ * The new handle has no geometry (all fluid, fully periodic) and is not
+ * initialised.  Host only. */
+lbm_status lbm_create(const lbm_desc *desc, void *buf0, void *buf1, void *hip_stream,
+                      lbm_sim **out);
+
+/* Solid mask and boundary kind per axis (PortLBM section 3.1, halfway bounce-back).
+ *   mask       device uint8[N], 0 = fluid, nonzero = solid; NULL = no solids.
+ *              Read by every later step; must stay alive and unchanged.
+ *   periodic   host int32[3] for x, y, z: 1 = periodic, 0 = halfway
+ *              bounce-back wall half a cell beyond both faces of that axis.
+ * Invalidates the state: lbm_init_equilibrium must be called again.  Host only. */
+lbm_status lbm_set_geometry(lbm_sim *sim, const uint8_t *mask, const int32_t periodic[3]);
+
+/* f(0) = equilibrium(rho, u) on fluid cells, 0 on solid cells; t := 0.
+ *   rho   device T[N] or NULL (rho = 1).
+ *   u     device T[3][N] (component-major) or NULL (u = 0).
+ * AB stores the streaming pre-image of f(0) in buf0, so that the first fused
+ * pull-collide step acts on f(0) itself. */
+lbm_status lbm_init_equilibrium(lbm_sim *sim, const void *rho, const void *u);
+
+/* Advance n >= 0 time steps (one fused kernel launch each); t += n. */
+lbm_status lbm_step(lbm_sim *sim, int64_t n);
+
+/* Density and velocity of the canonical state f(t):
+ * rho = sum_q f_q, u = (sum_q c_q f_q + F/2) / rho; 0 on solid cells.
+ *   rho   device T[N];   u   device T[3][N] (component-major). */
+lbm_status lbm_moments(lbm_sim *sim, void *rho, void *u);
+
+/* Copy the canonical populations f(t) into device T[19][N]; 0 on solid cells. */
+lbm_status lbm_read_populations(lbm_sim *sim, void *f);
+
+/* Replace the state by canonical populations f (device T[19][N]) at the
+ * current t (checkpoint restore).  Values on solid cells are ignored. */
+lbm_status lbm_write_populations(lbm_sim *sim, const void *f);
+
+/* Release the handle (host memory only); NULL is a no-op. */
+lbm_status lbm_destroy(lbm_sim *sim);
+
+/* Current time step t, or -1 for a NULL handle. */
+int64_t lbm_time(const lbm_sim *sim);
+
+/* Static description of a status code. */
+const char *lbm_status_string(lbm_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,149 @@
+"""ctypes binding of liblbm.so: the C ABI of include/lbm.h, same names.
+
+Argument marshalling only -- every step of the update runs in the HIP
+kernels of liblbm.so.  Pointers are passed as Python ints (device addresses,
+e.g. ``tensor.data_ptr()``); streams as ``torch.cuda.Stream.cuda_stream``.
+Importing this module raises if the library has not been built: there is no
+CPU fallback.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblbm.so")
+
+LBM_OK = 0
+LBM_ERR_INVALID_ARGUMENT = -1
+LBM_ERR_UNSUPPORTED = -2
+LBM_ERR_BAD_STATE = -3
+LBM_ERR_MISALIGNED = -4
+LBM_ERR_HIP = -5
+
+LBM_F32, LBM_F64 = 0, 1
+LBM_LAYOUT_STREAM, LBM_LAYOUT_BUNDLE, LBM_LAYOUT_COLLISION = 0, 1, 2
+LBM_SCHEME_AB, LBM_SCHEME_AA = 0, 1
+
+EXPORTED = ["lbm_buffer_bytes", "lbm_create", "lbm_set_geometry", "lbm_init_equilibrium", "lbm_step",
+            "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_destroy", "lbm_time",
+            "lbm_status_string"]
+
+
+class lbm_desc(ctypes.Structure):
+    _fields_ = [("nx", ctypes.c_int64), ("ny", ctypes.c_int64), ("nz", ctypes.c_int64),
+                ("precision", ctypes.c_int32), ("layout", ctypes.c_int32), ("scheme", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("tau", ctypes.c_double), ("force", ctypes.c_double * 3)]
+
+
+class LbmError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {lbm_status_string(status)} ({status})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m lattice_boltzmann_cfd_d3q19_amd._build` (there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i64, _i32, _st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32
+_Desc_p = ctypes.POINTER(lbm_desc)
+
+_lib.lbm_buffer_bytes.argtypes = [_Desc_p, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_i32)]
+_lib.lbm_buffer_bytes.restype = _st
+_lib.lbm_create.argtypes = [_Desc_p, _vp, _vp, _vp, ctypes.POINTER(_vp)]
+_lib.lbm_create.restype = _st
+_lib.lbm_set_geometry.argtypes = [_vp, _vp, ctypes.POINTER(_i32)]
+_lib.lbm_set_geometry.restype = _st
+_lib.lbm_init_equilibrium.argtypes = [_vp, _vp, _vp]
+_lib.lbm_init_equilibrium.restype = _st
+_lib.lbm_step.argtypes = [_vp, _i64]
+_lib.lbm_step.restype = _st
+_lib.lbm_moments.argtypes = [_vp, _vp, _vp]
+_lib.lbm_moments.restype = _st
+_lib.lbm_read_populations.argtypes = [_vp, _vp]
+_lib.lbm_read_populations.restype = _st
+_lib.lbm_write_populations.argtypes = [_vp, _vp]
+_lib.lbm_write_populations.restype = _st
+_lib.lbm_destroy.argtypes = [_vp]
+_lib.lbm_destroy.restype = _st
+_lib.lbm_time.argtypes = [_vp]
+_lib.lbm_time.restype = _i64
+_lib.lbm_status_string.argtypes = [_st]
+_lib.lbm_status_string.restype = ctypes.c_char_p
+
+
+def library():
+    """The loaded ctypes.CDLL (for symbol checks)."""
+    return _lib
+
+
+def make_desc(nx, ny, nz, precision=LBM_F32, layout=LBM_LAYOUT_STREAM, scheme=LBM_SCHEME_AA, tau=1.0,
+              force=(0.0, 0.0, 0.0)):
+    d = lbm_desc()
+    d.nx, d.ny, d.nz = int(nx), int(ny), int(nz)
+    d.precision, d.layout, d.scheme, d.reserved = int(precision), int(layout), int(scheme), 0
+    d.tau = float(tau)
+    d.force[:] = [float(v) for v in force]
+    return d
+
+
+def _ptr(p):
+    return None if p is None or p == 0 else ctypes.c_void_p(int(p))
+
+
+def lbm_status_string(status):
+    return _lib.lbm_status_string(int(status)).decode()
+
+
+def lbm_buffer_bytes(desc):
+    """Return (status, bytes_per_buffer, n_buffers)."""
+    nb = ctypes.c_size_t(0)
+    n = _i32(0)
+    st = _lib.lbm_buffer_bytes(ctypes.byref(desc), ctypes.byref(nb), ctypes.byref(n))
+    return st, nb.value, n.value
+
+
+def lbm_create(desc, buf0, buf1=None, stream=None):
+    """Return (status, handle)."""
+    h = _vp(None)
+    st = _lib.lbm_create(ctypes.byref(desc), _ptr(buf0), _ptr(buf1), _ptr(stream), ctypes.byref(h))
+    return st, h
+
+
+def lbm_set_geometry(sim, mask, periodic):
+    per = None if periodic is None else (_i32 * 3)(*[int(p) for p in periodic])
+    return _lib.lbm_set_geometry(sim, _ptr(mask), per)
+
+
+def lbm_init_equilibrium(sim, rho=None, u=None):
+    return _lib.lbm_init_equilibrium(sim, _ptr(rho), _ptr(u))
+
+
+def lbm_step(sim, n):
+    return _lib.lbm_step(sim, int(n))
+
+
+def lbm_moments(sim, rho, u):
+    return _lib.lbm_moments(sim, _ptr(rho), _ptr(u))
+
+
+def lbm_read_populations(sim, f):
+    return _lib.lbm_read_populations(sim, _ptr(f))
+
+
+def lbm_write_populations(sim, f):
+    return _lib.lbm_write_populations(sim, _ptr(f))
+
+
+def lbm_destroy(sim):
+    return _lib.lbm_destroy(sim)
+
+
+def lbm_time(sim):
+    return _lib.lbm_time(sim)
+
+
+def check(status, where=""):
+    if status != LBM_OK:
+        raise LbmError(status, where)
+    return status

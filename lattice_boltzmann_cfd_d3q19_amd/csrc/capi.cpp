@@ -1,0 +1,259 @@
+// capi.cpp -- the C ABI of liblbm.so (declared in include/lbm.h).
+//
+// Validation and the state machine live here, on the host; every GPU action
+// is one kernel launch through launch.hpp on the handle's stream.
+//
+// Stored state per scheme (what "canonical f(t)" is read from):
+//   AB: buffer `cur` holds h(t), the post-collision values of step t-1 (for
+//       t = 0: the streaming pre-image of f(0)), so that f(t) = stream(h(t))
+//       and one fused pull-collide step maps h(t) to h(t+1) in the other
+//       buffer.
+//   AA: the single buffer holds f(t) in natural slots when t is even, and the
+//       post-collision values of step t-1 in the swapped slots of the
+//       in-place pattern when t is odd (fieldcraft page, first section).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <new>
+
+#include "../../include/lbm.h"
+#include "d3q19.hpp"
+#include "kernels.hpp"
+#include "launch.hpp"
+
+struct lbm_sim {
+    lbm_desc d;
+    void* buf[2];
+    hipStream_t stream;
+    const uint8_t* mask;
+    int32_t periodic[3];
+    int32_t xcd_remap;
+    bool initialized;
+    int64_t t;
+    int cur;  // AB: index of the buffer holding h(t)
+    double omega;
+};
+
+namespace {
+
+constexpr uintptr_t kAlign = 256;
+
+bool is_finite(double v) { return std::isfinite(v); }
+
+lbm_status validate_desc(const lbm_desc* d)
+{
+    if (d == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (d->nx < 1 || d->ny < 1 || d->nz < 1) return LBM_ERR_INVALID_ARGUMENT;
+    if (d->precision != LBM_F32 && d->precision != LBM_F64) return LBM_ERR_INVALID_ARGUMENT;
+    if (d->layout != LBM_LAYOUT_STREAM && d->layout != LBM_LAYOUT_BUNDLE && d->layout != LBM_LAYOUT_COLLISION)
+        return LBM_ERR_INVALID_ARGUMENT;
+    if (d->scheme != LBM_SCHEME_AB && d->scheme != LBM_SCHEME_AA) return LBM_ERR_INVALID_ARGUMENT;
+    if (d->reserved != 0) return LBM_ERR_INVALID_ARGUMENT;
+    if (std::isnan(d->tau) || !(d->tau > 0.5)) return LBM_ERR_INVALID_ARGUMENT;
+    if (std::isinf(d->tau) && d->tau < 0) return LBM_ERR_INVALID_ARGUMENT;
+    for (int a = 0; a < 3; ++a)
+        if (!is_finite(d->force[a])) return LBM_ERR_INVALID_ARGUMENT;
+    // cell indices are 32-bit inside the kernels; the workgroup count too
+    const double n = (double)d->nx * (double)d->ny * (double)d->nz;
+    if (d->nx > INT32_MAX || d->ny > INT32_MAX || d->nz > INT32_MAX || n >= 2147483648.0)
+        return LBM_ERR_UNSUPPORTED;
+    return LBM_OK;
+}
+
+size_t elem_size(const lbm_desc& d) { return d.precision == LBM_F64 ? 8 : 4; }
+
+uint64_t ncells(const lbm_desc& d) { return (uint64_t)d.nx * (uint64_t)d.ny * (uint64_t)d.nz; }
+
+lbm::LaunchGeom geom_of(const lbm_sim* s)
+{
+    lbm::LaunchGeom g{};
+    g.nx = s->d.nx;
+    g.ny = s->d.ny;
+    g.nz = s->d.nz;
+    for (int a = 0; a < 3; ++a) g.periodic[a] = s->periodic[a];
+    g.mask = s->mask;
+    g.xcd_remap = s->xcd_remap;
+    return g;
+}
+
+lbm::LaunchPhys phys_of(const lbm_sim* s)
+{
+    lbm::LaunchPhys p{};
+    p.omega = s->omega;
+    p.has_force = false;
+    for (int a = 0; a < 3; ++a) {
+        p.force[a] = s->d.force[a];
+        if (s->d.force[a] != 0.0) p.has_force = true;
+    }
+    return p;
+}
+
+// Kind of the stored state at the current time.
+int state_kind(const lbm_sim* s)
+{
+    if (s->d.scheme == LBM_SCHEME_AB) return lbm::kAB;
+    return (s->t % 2 == 0) ? lbm::kAAEven : lbm::kAAOdd;
+}
+
+lbm_status io(lbm_sim* s, int op, void* out0, void* out1, const void* in0, const void* in1)
+{
+    const lbm::LaunchGeom g = geom_of(s);
+    const lbm::LaunchPhys p = phys_of(s);
+    const int st = state_kind(s);
+    void* a = s->d.scheme == LBM_SCHEME_AB ? s->buf[s->cur] : s->buf[0];
+    void* b = (s->d.scheme == LBM_SCHEME_AB && op == lbm::kWriteEq) ? s->buf[1 - s->cur] : nullptr;
+    hipError_t e;
+    if (s->d.precision == LBM_F32)
+        e = lbm::launch_io<float>(s->d.layout, st, op, (float*)a, (float*)b, g, p, (float*)out0, (float*)out1,
+                                  (const float*)in0, (const float*)in1, s->stream);
+    else
+        e = lbm::launch_io<double>(s->d.layout, st, op, (double*)a, (double*)b, g, p, (double*)out0,
+                                   (double*)out1, (const double*)in0, (const double*)in1, s->stream);
+    return e == hipSuccess ? LBM_OK : LBM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+lbm_status lbm_buffer_bytes(const lbm_desc* desc, size_t* bytes_per_buffer, int32_t* n_buffers)
+{
+    const lbm_status v = validate_desc(desc);
+    if (v != LBM_OK) return v;
+    if (bytes_per_buffer == nullptr && n_buffers == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (bytes_per_buffer) *bytes_per_buffer = (size_t)lbm::kQ * ncells(*desc) * elem_size(*desc);
+    if (n_buffers) *n_buffers = desc->scheme == LBM_SCHEME_AB ? 2 : 1;
+    return LBM_OK;
+}
+
+lbm_status lbm_create(const lbm_desc* desc, void* buf0, void* buf1, void* hip_stream, lbm_sim** out)
+{
+    if (out == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    const lbm_status v = validate_desc(desc);
+    if (v != LBM_OK) return v;
+    if (buf0 == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (desc->scheme == LBM_SCHEME_AA && buf1 != nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (desc->scheme == LBM_SCHEME_AB && buf1 == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if ((uintptr_t)buf0 % kAlign != 0 || (buf1 && (uintptr_t)buf1 % kAlign != 0)) return LBM_ERR_MISALIGNED;
+    if (buf1 != nullptr) {
+        const uintptr_t bytes = (uintptr_t)((size_t)lbm::kQ * ncells(*desc) * elem_size(*desc));
+        const uintptr_t p0 = (uintptr_t)buf0, p1 = (uintptr_t)buf1;
+        if (p0 < p1 + bytes && p1 < p0 + bytes) return LBM_ERR_INVALID_ARGUMENT;  // overlap
+    }
+    lbm_sim* s = new (std::nothrow) lbm_sim{};
+    if (s == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    s->d = *desc;
+    s->buf[0] = buf0;
+    s->buf[1] = buf1;
+    s->stream = (hipStream_t)hip_stream;
+    s->mask = nullptr;
+    s->periodic[0] = s->periodic[1] = s->periodic[2] = 1;
+    const char* env = std::getenv("LBM_XCD_REMAP");
+    s->xcd_remap = (env != nullptr && env[0] == '1') ? 1 : 0;
+    s->initialized = false;
+    s->t = 0;
+    s->cur = 0;
+    s->omega = std::isinf(desc->tau) ? 0.0 : 1.0 / desc->tau;
+    *out = s;
+    return LBM_OK;
+}
+
+lbm_status lbm_set_geometry(lbm_sim* sim, const uint8_t* mask, const int32_t periodic[3])
+{
+    if (sim == nullptr || periodic == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    for (int a = 0; a < 3; ++a)
+        if (periodic[a] != 0 && periodic[a] != 1) return LBM_ERR_INVALID_ARGUMENT;
+    sim->mask = mask;
+    for (int a = 0; a < 3; ++a) sim->periodic[a] = periodic[a];
+    sim->initialized = false;
+    sim->t = 0;
+    sim->cur = 0;
+    return LBM_OK;
+}
+
+lbm_status lbm_init_equilibrium(lbm_sim* sim, const void* rho, const void* u)
+{
+    if (sim == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    sim->t = 0;
+    sim->cur = 0;
+    sim->initialized = false;
+    const lbm_status r = io(sim, lbm::kWriteEq, nullptr, nullptr, rho, u);
+    if (r == LBM_OK) sim->initialized = true;
+    return r;
+}
+
+lbm_status lbm_step(lbm_sim* sim, int64_t n)
+{
+    if (sim == nullptr || n < 0) return LBM_ERR_INVALID_ARGUMENT;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    const lbm::LaunchGeom g = geom_of(sim);
+    const lbm::LaunchPhys p = phys_of(sim);
+    for (int64_t i = 0; i < n; ++i) {
+        int kind;
+        void *a, *b = nullptr;
+        if (sim->d.scheme == LBM_SCHEME_AB) {
+            kind = lbm::kAB;
+            a = sim->buf[sim->cur];
+            b = sim->buf[1 - sim->cur];
+        } else {
+            kind = (sim->t % 2 == 0) ? lbm::kAAEven : lbm::kAAOdd;
+            a = sim->buf[0];
+        }
+        hipError_t e;
+        if (sim->d.precision == LBM_F32)
+            e = lbm::launch_step<float>(sim->d.layout, kind, (float*)a, (float*)b, g, p, sim->stream);
+        else
+            e = lbm::launch_step<double>(sim->d.layout, kind, (double*)a, (double*)b, g, p, sim->stream);
+        if (e != hipSuccess) return LBM_ERR_HIP;
+        if (sim->d.scheme == LBM_SCHEME_AB) sim->cur = 1 - sim->cur;
+        sim->t += 1;
+    }
+    return LBM_OK;
+}
+
+lbm_status lbm_moments(lbm_sim* sim, void* rho, void* u)
+{
+    if (sim == nullptr || rho == nullptr || u == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    return io(sim, lbm::kReadMoments, rho, u, nullptr, nullptr);
+}
+
+lbm_status lbm_read_populations(lbm_sim* sim, void* f)
+{
+    if (sim == nullptr || f == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    return io(sim, lbm::kReadF, f, nullptr, nullptr, nullptr);
+}
+
+lbm_status lbm_write_populations(lbm_sim* sim, const void* f)
+{
+    if (sim == nullptr || f == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    return io(sim, lbm::kWriteF, nullptr, nullptr, f, nullptr);
+}
+
+lbm_status lbm_destroy(lbm_sim* sim)
+{
+    delete sim;
+    return LBM_OK;
+}
+
+int64_t lbm_time(const lbm_sim* sim) { return sim == nullptr ? -1 : sim->t; }
+
+const char* lbm_status_string(lbm_status status)
+{
+    switch (status) {
+    case LBM_OK: return "ok";
+    case LBM_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LBM_ERR_UNSUPPORTED: return "unsupported size or option";
+    case LBM_ERR_BAD_STATE: return "call out of order (create, set_geometry, init, then step)";
+    case LBM_ERR_MISALIGNED: return "population buffer not 256-byte aligned";
+    case LBM_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

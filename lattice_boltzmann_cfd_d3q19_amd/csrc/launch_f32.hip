@@ -1,0 +1,9 @@
+// launch_f32.hip -- fp32 instantiation of the step and state-transfer launchers.
+#include "launch_impl.hpp"
+
+namespace lbm {
+template hipError_t launch_step<float>(int, int, float*, float*, const LaunchGeom&, const LaunchPhys&,
+                                       hipStream_t);
+template hipError_t launch_io<float>(int, int, int, float*, float*, const LaunchGeom&, const LaunchPhys&,
+                                     float*, float*, const float*, const float*, hipStream_t);
+}  // namespace lbm

@@ -1,0 +1,9 @@
+// launch_f64.hip -- fp64 instantiation of the step and state-transfer launchers.
+#include "launch_impl.hpp"
+
+namespace lbm {
+template hipError_t launch_step<double>(int, int, double*, double*, const LaunchGeom&, const LaunchPhys&,
+                                        hipStream_t);
+template hipError_t launch_io<double>(int, int, int, double*, double*, const LaunchGeom&, const LaunchPhys&,
+                                      double*, double*, const double*, const double*, hipStream_t);
+}  // namespace lbm

@@ -1,0 +1,151 @@
+// launch_impl.hpp -- launcher templates; instantiated once per precision.
+#pragma once
+
+#include <cmath>
+
+#include "kernels.hpp"
+#include "launch.hpp"
+
+namespace lbm {
+
+struct Shape {
+    dim3 grid, block;
+    Geom g;
+};
+
+// Tile shape: BX = smallest power of two >= nx, clamped to [32, 256], so a
+// wave64 covers one row segment (or two rows of 32); BY fills 256 threads.
+inline Shape make_shape(const LaunchGeom& lg)
+{
+    Shape s{};
+    uint32_t bx = 32;
+    while (bx < 256 && (int64_t)bx < lg.nx) bx *= 2;
+    const uint32_t by = (uint32_t)kBlockThreads / bx;
+    Geom& g = s.g;
+    g.nx = (uint32_t)lg.nx;
+    g.ny = (uint32_t)lg.ny;
+    g.nz = (uint32_t)lg.nz;
+    g.nxy = g.nx * g.ny;
+    g.per_x = lg.periodic[0] != 0;
+    g.per_y = lg.periodic[1] != 0;
+    g.per_z = lg.periodic[2] != 0;
+    g.ntx = (g.nx + bx - 1) / bx;
+    g.nty = (g.ny + by - 1) / by;
+    g.ntiles = g.ntx * g.nty * g.nz;
+    g.xcd_remap = lg.xcd_remap ? 1u : 0u;
+    g.n = (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz;
+    g.mask = lg.mask;
+    s.block = dim3(bx, by, 1);
+    s.grid = dim3(g.ntiles, 1, 1);
+    return s;
+}
+
+template <typename T>
+inline Phys<T> make_phys(const LaunchPhys& lp)
+{
+    Phys<T> p{};
+    p.omega = (T)lp.omega;
+    p.guo = (T)(1.0 - 0.5 * lp.omega);
+    p.fx = (T)lp.force[0];
+    p.fy = (T)lp.force[1];
+    p.fz = (T)lp.force[2];
+    p.hfx = (T)(0.5 * lp.force[0]);
+    p.hfy = (T)(0.5 * lp.force[1]);
+    p.hfz = (T)(0.5 * lp.force[2]);
+    return p;
+}
+
+template <typename T, int L, int K, bool BND, bool FORCE>
+hipError_t launch_step_t(T* a, T* b, const Shape& s, const Phys<T>& p, hipStream_t st)
+{
+    hipLaunchKernelGGL((step_kernel<T, L, K, BND, FORCE>), s.grid, s.block, 0, st, a, b, s.g, p);
+    return hipGetLastError();
+}
+
+template <typename T, int L, int K>
+hipError_t launch_step_k(T* a, T* b, const Shape& s, const Phys<T>& p, bool bnd, bool force, hipStream_t st)
+{
+    if (bnd)
+        return force ? launch_step_t<T, L, K, true, true>(a, b, s, p, st)
+                     : launch_step_t<T, L, K, true, false>(a, b, s, p, st);
+    return force ? launch_step_t<T, L, K, false, true>(a, b, s, p, st)
+                 : launch_step_t<T, L, K, false, false>(a, b, s, p, st);
+}
+
+template <typename T, int L>
+hipError_t launch_step_l(int kind, T* a, T* b, const Shape& s, const Phys<T>& p, bool bnd, bool force,
+                         hipStream_t st)
+{
+    switch (kind) {
+    case kAB: return launch_step_k<T, L, kAB>(a, b, s, p, bnd, force, st);
+    case kAAEven: return launch_step_k<T, L, kAAEven>(a, b, s, p, bnd, force, st);
+    case kAAOdd: return launch_step_k<T, L, kAAOdd>(a, b, s, p, bnd, force, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp,
+                       hipStream_t st)
+{
+    const Shape s = make_shape(lg);
+    const Phys<T> p = make_phys<T>(lp);
+    const bool bnd = lg.mask != nullptr || !lg.periodic[0] || !lg.periodic[1] || !lg.periodic[2];
+    switch (layout) {
+    case kStream: return launch_step_l<T, kStream>(kind, a, b, s, p, bnd, lp.has_force, st);
+    case kBundle: return launch_step_l<T, kBundle>(kind, a, b, s, p, bnd, lp.has_force, st);
+    case kCollision: return launch_step_l<T, kCollision>(kind, a, b, s, p, bnd, lp.has_force, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int L, int S>
+hipError_t launch_io_s(int op, T* a, T* b, const Shape& s, const Phys<T>& p, T* o0, T* o1, const T* i0,
+                       const T* i1, hipStream_t st)
+{
+    switch (op) {
+    case kReadF:
+        hipLaunchKernelGGL((io_kernel<T, L, S, kReadF>), s.grid, s.block, 0, st, a, b, s.g, p, o0, o1, i0, i1);
+        break;
+    case kReadMoments:
+        hipLaunchKernelGGL((io_kernel<T, L, S, kReadMoments>), s.grid, s.block, 0, st, a, b, s.g, p, o0, o1, i0,
+                           i1);
+        break;
+    case kWriteF:
+        hipLaunchKernelGGL((io_kernel<T, L, S, kWriteF>), s.grid, s.block, 0, st, a, b, s.g, p, o0, o1, i0, i1);
+        break;
+    case kWriteEq:
+        hipLaunchKernelGGL((io_kernel<T, L, S, kWriteEq>), s.grid, s.block, 0, st, a, b, s.g, p, o0, o1, i0, i1);
+        break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int L>
+hipError_t launch_io_l(int state, int op, T* a, T* b, const Shape& s, const Phys<T>& p, T* o0, T* o1,
+                       const T* i0, const T* i1, hipStream_t st)
+{
+    switch (state) {
+    case kAB: return launch_io_s<T, L, kAB>(op, a, b, s, p, o0, o1, i0, i1, st);
+    case kAAEven: return launch_io_s<T, L, kAAEven>(op, a, b, s, p, o0, o1, i0, i1, st);
+    case kAAOdd: return launch_io_s<T, L, kAAOdd>(op, a, b, s, p, o0, o1, i0, i1, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_io(int layout, int state, int op, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp,
+                     T* o0, T* o1, const T* i0, const T* i1, hipStream_t st)
+{
+    const Shape s = make_shape(lg);
+    const Phys<T> p = make_phys<T>(lp);
+    switch (layout) {
+    case kStream: return launch_io_l<T, kStream>(state, op, a, b, s, p, o0, o1, i0, i1, st);
+    case kBundle: return launch_io_l<T, kBundle>(state, op, a, b, s, p, o0, o1, i0, i1, st);
+    case kCollision: return launch_io_l<T, kCollision>(state, op, a, b, s, p, o0, o1, i0, i1, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace lbm

@@ -1,0 +1,97 @@
+"""Thin torch-side convenience wrapper over the C ABI.
+
+Torch provides device memory and the stream only; every operation is one
+call into liblbm.so.  Buffers are allocated on the current HIP device.
+"""
+import torch
+
+from . import capi
+
+_PREC = {"f32": (capi.LBM_F32, torch.float32), "f64": (capi.LBM_F64, torch.float64)}
+_LAYOUT = {"stream": capi.LBM_LAYOUT_STREAM, "bundle": capi.LBM_LAYOUT_BUNDLE,
+           "collision": capi.LBM_LAYOUT_COLLISION}
+_SCHEME = {"ab": capi.LBM_SCHEME_AB, "aa": capi.LBM_SCHEME_AA}
+
+Q = 19
+
+
+class Lattice:
+    """One D3Q19 lattice on the GPU.
+
+    precision: "f32" | "f64"; layout: "stream" | "bundle" | "collision";
+    scheme: "ab" (two lattices, fused pull) | "aa" (one lattice, in place).
+    """
+
+    def __init__(self, nx, ny, nz, precision="f32", layout="stream", scheme="aa", tau=1.0,
+                 force=(0.0, 0.0, 0.0), stream=None, device=None):
+        if not torch.cuda.is_available():
+            raise RuntimeError("no HIP device: the lattice runs only on the GPU")
+        self.shape = (int(nx), int(ny), int(nz))
+        self.n = self.shape[0] * self.shape[1] * self.shape[2]
+        prec, self.dtype = _PREC[precision]
+        self.device = torch.device("cuda") if device is None else torch.device(device)
+        self.desc = capi.make_desc(nx, ny, nz, prec, _LAYOUT[layout], _SCHEME[scheme], tau, force)
+        st, nbytes, nbuf = capi.lbm_buffer_bytes(self.desc)
+        capi.check(st, "lbm_buffer_bytes")
+        elems = nbytes // torch.empty((), dtype=self.dtype).element_size()
+        self.buffers = [torch.empty(elems, dtype=self.dtype, device=self.device) for _ in range(nbuf)]
+        self.stream = torch.cuda.current_stream(self.device) if stream is None else stream
+        ptrs = [b.data_ptr() for b in self.buffers] + [None]
+        st, self.handle = capi.lbm_create(self.desc, ptrs[0], ptrs[1], self.stream.cuda_stream)
+        capi.check(st, "lbm_create")
+        self.mask = None
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value is not None:
+            capi.lbm_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- geometry and state -------------------------------------------------
+    def set_geometry(self, mask=None, periodic=(1, 1, 1)):
+        if mask is not None:
+            mask = torch.as_tensor(mask).to(device=self.device, dtype=torch.uint8).contiguous().reshape(-1)
+            if mask.numel() != self.n:
+                raise ValueError("mask must have nx*ny*nz entries")
+        self.mask = mask
+        capi.check(capi.lbm_set_geometry(self.handle, None if mask is None else mask.data_ptr(), periodic),
+                   "lbm_set_geometry")
+
+    def _dev(self, a, shape):
+        t = torch.as_tensor(a).to(device=self.device, dtype=self.dtype).contiguous()
+        return t.reshape(shape)
+
+    def init(self, rho=None, u=None):
+        r = None if rho is None else self._dev(rho, (self.n,))
+        v = None if u is None else self._dev(u, (3, self.n))
+        capi.check(capi.lbm_init_equilibrium(self.handle, None if r is None else r.data_ptr(),
+                                             None if v is None else v.data_ptr()), "lbm_init_equilibrium")
+        self._keep = (r, v)  # alive until the init kernel has run on the stream
+
+    def step(self, n=1):
+        capi.check(capi.lbm_step(self.handle, n), "lbm_step")
+
+    @property
+    def t(self):
+        return capi.lbm_time(self.handle)
+
+    def moments(self):
+        rho = torch.empty(self.n, dtype=self.dtype, device=self.device)
+        u = torch.empty((3, self.n), dtype=self.dtype, device=self.device)
+        capi.check(capi.lbm_moments(self.handle, rho.data_ptr(), u.data_ptr()), "lbm_moments")
+        return rho, u
+
+    def read_populations(self):
+        f = torch.empty((Q, self.n), dtype=self.dtype, device=self.device)
+        capi.check(capi.lbm_read_populations(self.handle, f.data_ptr()), "lbm_read_populations")
+        return f
+
+    def write_populations(self, f):
+        ff = self._dev(f, (Q, self.n))
+        capi.check(capi.lbm_write_populations(self.handle, ff.data_ptr()), "lbm_write_populations")
+        self._keep = (ff,)

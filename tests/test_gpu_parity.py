@@ -1,0 +1,243 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: canonical populations within max-abs 1e-5 (fp32) / 1e-12 (fp64) after
+100 steps from the same seeded inputs; indexing, masks and streaming bit-exact
+(collision-free mode); every layout and scheme bit-identical to one another.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import lbm_inputs as li
+import oracle
+from gpu_util import LAYOUTS, SCHEMES, TOL, cast, host_f, host_moments, make, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+Q = 19
+_ORACLE_CACHE = {}
+
+
+def _oracle_run(key, box, mask, rho, u, n):
+    if key not in _ORACLE_CACHE:
+        f0 = oracle.init_equilibrium(box, mask, rho, u)
+        _ORACLE_CACHE[key] = oracle.run(box, f0, n, mask)
+    return _ORACLE_CACHE[key]
+
+
+# --------------------------------------------------------------- C1 in full
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("scheme", SCHEMES)
+def test_c1_random_periodic_32cubed(layout, scheme):
+    """32^3 periodic, tau = 0.8, no force, seeded random rho/u, 100 steps."""
+    need_gpu()
+    say("c1", layout, scheme)
+    rho, u = li.random_fields(32, 32, 32, seed=1)
+    rho, u = cast(rho, "f32"), cast(u, "f32")
+    box = oracle.Box(32, 32, 32, tau=0.8)
+    want = _oracle_run(("c1",), box, None, rho, u, 100)
+    lat = make((32, 32, 32), "f32", layout, scheme, tau=0.8, rho=rho, u=u)
+    lat.step(100)
+    got = host_f(lat)
+    err = np.max(np.abs(got - want))
+    say("c1 max-abs", err)
+    assert err <= TOL["f32"]
+
+
+# ------------------------------------------- small ragged boxes, all physics
+
+def _case(name):
+    if name == "sphere_force":
+        shape, per, tau, F = (37, 29, 23), (1, 1, 1), 0.7, (1e-5, 0.0, 0.0)
+        mask = li.sphere_mask(37, 29, 23, radius=6)
+    elif name == "channel":
+        shape, per, tau, F = (24, 20, 33), (1, 0, 1), 0.9, (0.0, 0.0, 1e-5)
+        mask = None
+    elif name == "porous":
+        shape, per, tau, F = (40, 36, 28), (1, 1, 1), 0.65, (1e-5, 0.0, 0.0)
+        mask, _ = li.porous_mask(40, 36, 28, n_spheres=12, seed=5, rmin=2.0, rmax=4.0)
+    elif name == "closed_box":
+        shape, per, tau, F = (19, 17, 13), (0, 0, 0), 0.6, (2e-5, -1e-5, 1e-5)
+        mask = li.random_mask(19, 17, 13, fraction=0.15, seed=7)
+    else:
+        raise KeyError(name)
+    return shape, per, tau, F, mask
+
+
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+@pytest.mark.parametrize("name,nsteps", [("sphere_force", 100), ("channel", 101), ("porous", 100),
+                                         ("closed_box", 101)])
+def test_small_boxes_all_layouts_schemes(name, nsteps, precision):
+    need_gpu()
+    shape, per, tau, F, mask = _case(name)
+    rho, u = li.random_fields(*shape, seed=11)
+    rho, u = cast(rho, precision), cast(u, precision)
+    box = oracle.Box(*shape, periodic=per, tau=tau, force=F)
+    want = _oracle_run((name, precision, nsteps), box, mask, rho, u, nsteps)
+    results = {}
+    for layout in LAYOUTS:
+        for scheme in SCHEMES:
+            say(name, precision, layout, scheme, nsteps)
+            lat = make(shape, precision, layout, scheme, tau=tau, force=F, mask=mask, periodic=per, rho=rho, u=u)
+            lat.step(nsteps)
+            assert lat.t == nsteps
+            got = host_f(lat)
+            err = np.max(np.abs(got - want))
+            say("  max-abs", err)
+            assert err <= TOL[precision], (layout, scheme, err)
+            if mask is not None:
+                assert np.all(got[:, mask.astype(bool)] == 0.0)
+            results[(layout, scheme)] = got
+    ref = results[("stream", "ab")]
+    for k, v in results.items():
+        assert np.array_equal(v, ref), f"{k} differs from stream/ab"
+
+
+# ------------------------------------------ streaming bit-exact (omega = 0)
+
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+@pytest.mark.parametrize("nsteps", [1, 2, 3])
+def test_collision_free_streaming_bit_exact(precision, nsteps):
+    """tau = inf makes collision the identity; GPU streaming + bounce-back must
+    then move values exactly as the oracle does, from the GPU's own f(0)."""
+    need_gpu()
+    shape, per = (21, 18, 11), (1, 0, 1)
+    mask = li.random_mask(*shape, fraction=0.2, seed=3)
+    rho, u = li.random_fields(*shape, seed=4)
+    rho, u = cast(rho, precision), cast(u, precision)
+    box = oracle.Box(*shape, periodic=per, tau=math.inf)
+    f0_oracle = oracle.init_equilibrium(box, mask, rho, u)
+    for layout in LAYOUTS:
+        for scheme in SCHEMES:
+            say("omega0", precision, nsteps, layout, scheme)
+            lat = make(shape, precision, layout, scheme, tau=math.inf, mask=mask, periodic=per, rho=rho, u=u)
+            f0 = host_f(lat)
+            rel = 2e-7 if precision == "f32" else 1e-15
+            assert np.max(np.abs(f0 - f0_oracle)) <= rel * np.max(np.abs(f0_oracle))
+            lat.step(nsteps)
+            got = host_f(lat)
+            want = oracle.run(box, f0, nsteps, mask)
+            assert np.array_equal(got, want), (layout, scheme)
+
+
+# --------------------------------------------------- state transfer paths
+
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+def test_write_read_roundtrip_both_parities(precision):
+    need_gpu()
+    shape, per = (33, 9, 14), (0, 1, 1)
+    mask = li.random_mask(*shape, fraction=0.25, seed=9)
+    n = int(np.prod(shape))
+    rng = np.random.default_rng(2)
+    f = cast(rng.uniform(0.01, 0.5, size=(Q, n)), precision).astype(np.float64)
+    f[:, mask.astype(bool)] = 0.0
+    for layout in LAYOUTS:
+        for scheme in SCHEMES:
+            for pre_steps in (0, 1):
+                say("roundtrip", precision, layout, scheme, pre_steps)
+                lat = make(shape, precision, layout, scheme, tau=0.7, mask=mask, periodic=per)
+                lat.step(pre_steps)
+                lat.write_populations(cast(f, precision))
+                got = host_f(lat)
+                assert np.array_equal(got, f), (layout, scheme, pre_steps)
+
+
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+def test_moments_match_oracle(precision):
+    need_gpu()
+    shape, per, F = (26, 22, 17), (1, 1, 0), (3e-5, 1e-5, -2e-5)
+    mask = li.sphere_mask(*shape, radius=5)
+    rho, u = li.random_fields(*shape, seed=12)
+    box = oracle.Box(*shape, periodic=per, tau=0.75, force=F)
+    for layout in LAYOUTS:
+        for scheme in SCHEMES:
+            lat = make(shape, precision, layout, scheme, tau=0.75, force=F, mask=mask, periodic=per,
+                       rho=cast(rho, precision), u=cast(u, precision))
+            lat.step(7)
+            f = host_f(lat)
+            r_gpu, u_gpu = host_moments(lat)
+            r_or, u_or = oracle.moments(box, f, mask)
+            tol = 1e-6 if precision == "f32" else 1e-14
+            assert np.max(np.abs(r_gpu - r_or)) <= tol
+            assert np.max(np.abs(u_gpu - u_or)) <= tol
+            solid = mask.astype(bool)
+            assert np.all(r_gpu[solid] == 0) and np.all(u_gpu[:, solid] == 0)
+
+
+def test_checkpoint_resume_bit_exact():
+    need_gpu()
+    shape, per, F = (30, 20, 10), (1, 1, 1), (1e-5, 0.0, 0.0)
+    mask = li.sphere_mask(*shape, radius=4)
+    rho, u = li.random_fields(*shape, seed=21)
+    rho, u = cast(rho, "f32"), cast(u, "f32")
+    for scheme in SCHEMES:
+        full = make(shape, "f32", "stream", scheme, tau=0.7, force=F, mask=mask, rho=rho, u=u)
+        full.step(10)
+        want = host_f(full)
+        half = make(shape, "f32", "stream", scheme, tau=0.7, force=F, mask=mask, rho=rho, u=u)
+        half.step(5)
+        snap = half.read_populations().clone()
+        resumed = make(shape, "f32", "bundle", scheme, tau=0.7, force=F, mask=mask)
+        resumed.write_populations(snap)
+        resumed.step(5)
+        assert np.array_equal(host_f(resumed), want)
+
+
+# ----------------------------------- full-size boxes: sampled one-step checks
+
+def _sample_cells(mask, n, k, seed):
+    rng = np.random.default_rng(seed)
+    cells = rng.choice(n, size=min(k, n), replace=False)
+    if mask is not None:
+        # add fluid cells touching a solid (where bounce-back acts)
+        m = mask.astype(bool)
+        near = np.nonzero(~m & (np.roll(m, 1) | np.roll(m, -1)))[0]
+        if near.size:
+            cells = np.concatenate([cells, rng.choice(near, size=min(2048, near.size), replace=False)])
+    return np.unique(cells).astype(np.int64)
+
+
+def _full_size(name):
+    if name == "tgv128":
+        shape, per, tau, F, mask = (128, 128, 128), (1, 1, 1), 0.6, (0, 0, 0), None
+        rho, u = li.taylor_green(128, u0=0.04)
+        return shape, per, tau, F, mask, rho, u, "f32"
+    if name == "sphere128":
+        return (128, 128, 128), (1, 1, 1), 0.7, (1e-6, 0, 0), li.sphere_mask(128, radius=16), None, None, "f32"
+    if name == "channel_f64":
+        return (64, 64, 256), (1, 0, 1), 0.9, (0, 0, 1e-6), None, None, None, "f64"
+    if name == "porous256":
+        mask, _ = li.porous_mask(256)
+        return (256, 256, 256), (1, 1, 1), 0.65, (1e-6, 0, 0), mask, None, None, "f32"
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name,layout,scheme", [
+    ("tgv128", "stream", "aa"), ("tgv128", "stream", "ab"),
+    ("sphere128", "stream", "aa"), ("sphere128", "bundle", "aa"), ("sphere128", "collision", "aa"),
+    ("channel_f64", "stream", "aa"), ("channel_f64", "stream", "ab"),
+    ("porous256", "stream", "aa"), ("porous256", "stream", "ab")])
+def test_full_size_sampled_steps(name, layout, scheme):
+    """At the benchmark sizes: advance a few steps, then check two consecutive
+    steps (odd -> even and even -> odd for AA) at sampled cells against the
+    oracle evaluated from the GPU's own state."""
+    need_gpu()
+    shape, per, tau, F, mask, rho, u, prec = _full_size(name)
+    say("full-size", name, layout, scheme)
+    lat = make(shape, prec, layout, scheme, tau=tau, force=F, mask=mask, periodic=per,
+               rho=cast(rho, prec), u=cast(u, prec))
+    box = oracle.Box(*shape, periodic=per, tau=tau, force=F)
+    n = int(np.prod(shape))
+    cells = _sample_cells(mask, n, 4096, seed=sum(name.encode()))
+    lat.step(5)
+    prev = host_f(lat)
+    for _ in range(2):
+        lat.step(1)
+        cur = host_f(lat)
+        want = oracle.step_cells(box, prev, cells, mask)
+        err = np.max(np.abs(cur[:, cells].T - want))
+        say("  one-step max-abs", err, "t =", lat.t)
+        assert err <= (1e-6 if prec == "f32" else 1e-14)
+        prev = cur
+    del prev, cur
