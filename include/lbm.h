@@ -139,6 +139,10 @@ lbm_status lbm_destroy(lbm_sim *sim);
 /* Current time step t, or -1 for a NULL handle. */
 int64_t lbm_time(const lbm_sim *sim);
 
+/* Name of the HIP error behind the handle's last LBM_ERR_HIP ("hipSuccess" if
+ * none; "no handle" for NULL).  Static string; host only. */
+const char *lbm_last_hip_error(const lbm_sim *sim);
+
 /* Static description of a status code. */
 const char *lbm_status_string(lbm_status status);
 

@@ -1,6 +1,6 @@
 """Build liblbm.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m lattice_boltzmann_cfd_d3q19_amd._build [-v]
+    python lattice_boltzmann_cfd_d3q19_amd/_build.py [-v]
 
 Each translation unit is compiled to an object in parallel, then linked into
 lattice_boltzmann_cfd_d3q19_amd/liblbm.so (in-tree, next to the binding).

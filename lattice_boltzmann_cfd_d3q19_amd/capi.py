@@ -25,7 +25,7 @@ LBM_SCHEME_AB, LBM_SCHEME_AA = 0, 1
 
 EXPORTED = ["lbm_buffer_bytes", "lbm_create", "lbm_set_geometry", "lbm_init_equilibrium", "lbm_step",
             "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_destroy", "lbm_time",
-            "lbm_status_string"]
+            "lbm_last_hip_error", "lbm_status_string"]
 
 
 class lbm_desc(ctypes.Structure):
@@ -42,7 +42,16 @@ class LbmError(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m lattice_boltzmann_cfd_d3q19_amd._build` (there is no CPU fallback)")
+                      "`python lattice_boltzmann_cfd_d3q19_amd/_build.py` (there is no CPU fallback)")
+
+# liblbm.so must share one HIP runtime with the process's torch.  torch ships
+# its own libamdhip64 with the same soname (libamdhip64.so.7); loading torch
+# first makes the dynamic loader bind liblbm.so to that copy.  Loading ours
+# first would map a second HIP runtime, which then sees no device.
+try:
+    import torch  # noqa: F401
+except ImportError:  # no torch: the library binds to the system HIP runtime
+    pass
 
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i64, _i32, _st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32
@@ -68,6 +77,8 @@ _lib.lbm_destroy.argtypes = [_vp]
 _lib.lbm_destroy.restype = _st
 _lib.lbm_time.argtypes = [_vp]
 _lib.lbm_time.restype = _i64
+_lib.lbm_last_hip_error.argtypes = [_vp]
+_lib.lbm_last_hip_error.restype = ctypes.c_char_p
 _lib.lbm_status_string.argtypes = [_st]
 _lib.lbm_status_string.restype = ctypes.c_char_p
 
@@ -143,7 +154,13 @@ def lbm_time(sim):
     return _lib.lbm_time(sim)
 
 
-def check(status, where=""):
+def lbm_last_hip_error(sim):
+    return _lib.lbm_last_hip_error(sim).decode()
+
+
+def check(status, where="", sim=None):
     if status != LBM_OK:
+        if status == LBM_ERR_HIP and sim is not None:
+            where = f"{where} [{lbm_last_hip_error(sim)}]"
         raise LbmError(status, where)
     return status

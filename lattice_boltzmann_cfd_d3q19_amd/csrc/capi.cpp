@@ -34,6 +34,7 @@ struct lbm_sim {
     int64_t t;
     int cur;  // AB: index of the buffer holding h(t)
     double omega;
+    hipError_t last_hip;  // status of the last failed launch (hipSuccess if none)
 };
 
 namespace {
@@ -111,7 +112,11 @@ lbm_status io(lbm_sim* s, int op, void* out0, void* out1, const void* in0, const
     else
         e = lbm::launch_io<double>(s->d.layout, st, op, (double*)a, (double*)b, g, p, (double*)out0,
                                    (double*)out1, (const double*)in0, (const double*)in1, s->stream);
-    return e == hipSuccess ? LBM_OK : LBM_ERR_HIP;
+    if (e != hipSuccess) {
+        s->last_hip = e;
+        return LBM_ERR_HIP;
+    }
+    return LBM_OK;
 }
 
 }  // namespace
@@ -157,6 +162,7 @@ lbm_status lbm_create(const lbm_desc* desc, void* buf0, void* buf1, void* hip_st
     s->t = 0;
     s->cur = 0;
     s->omega = std::isinf(desc->tau) ? 0.0 : 1.0 / desc->tau;
+    s->last_hip = hipSuccess;
     *out = s;
     return LBM_OK;
 }
@@ -207,7 +213,10 @@ lbm_status lbm_step(lbm_sim* sim, int64_t n)
             e = lbm::launch_step<float>(sim->d.layout, kind, (float*)a, (float*)b, g, p, sim->stream);
         else
             e = lbm::launch_step<double>(sim->d.layout, kind, (double*)a, (double*)b, g, p, sim->stream);
-        if (e != hipSuccess) return LBM_ERR_HIP;
+        if (e != hipSuccess) {
+            sim->last_hip = e;
+            return LBM_ERR_HIP;
+        }
         if (sim->d.scheme == LBM_SCHEME_AB) sim->cur = 1 - sim->cur;
         sim->t += 1;
     }
@@ -242,6 +251,12 @@ lbm_status lbm_destroy(lbm_sim* sim)
 }
 
 int64_t lbm_time(const lbm_sim* sim) { return sim == nullptr ? -1 : sim->t; }
+
+const char* lbm_last_hip_error(const lbm_sim* sim)
+{
+    if (sim == nullptr) return "no handle";
+    return hipGetErrorName(sim->last_hip);
+}
 
 const char* lbm_status_string(lbm_status status)
 {

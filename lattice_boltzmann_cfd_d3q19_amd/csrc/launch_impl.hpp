@@ -58,8 +58,11 @@ inline Phys<T> make_phys(const LaunchPhys& lp)
 template <typename T, int L, int K, bool BND, bool FORCE>
 hipError_t launch_step_t(T* a, T* b, const Shape& s, const Phys<T>& p, hipStream_t st)
 {
-    hipLaunchKernelGGL((step_kernel<T, L, K, BND, FORCE>), s.grid, s.block, 0, st, a, b, s.g, p);
-    return hipGetLastError();
+    Geom g = s.g;
+    Phys<T> ph = p;
+    void* args[] = {&a, &b, &g, &ph};
+    // hipLaunchKernel reports the status of this launch only (no stale errors)
+    return hipLaunchKernel((const void*)&step_kernel<T, L, K, BND, FORCE>, s.grid, s.block, args, 0, st);
 }
 
 template <typename T, int L, int K>
@@ -99,27 +102,27 @@ hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, c
     }
 }
 
+template <typename T, int L, int S, int OP>
+hipError_t launch_io_t(T* a, T* b, const Shape& s, const Phys<T>& p, T* o0, T* o1, const T* i0, const T* i1,
+                       hipStream_t st)
+{
+    Geom g = s.g;
+    Phys<T> ph = p;
+    void* args[] = {&a, &b, &g, &ph, &o0, &o1, &i0, &i1};
+    return hipLaunchKernel((const void*)&io_kernel<T, L, S, OP>, s.grid, s.block, args, 0, st);
+}
+
 template <typename T, int L, int S>
 hipError_t launch_io_s(int op, T* a, T* b, const Shape& s, const Phys<T>& p, T* o0, T* o1, const T* i0,
                        const T* i1, hipStream_t st)
 {
     switch (op) {
-    case kReadF:
-        hipLaunchKernelGGL((io_kernel<T, L, S, kReadF>), s.grid, s.block, 0, st, a, b, s.g, p, o0, o1, i0, i1);
-        break;
-    case kReadMoments:
-        hipLaunchKernelGGL((io_kernel<T, L, S, kReadMoments>), s.grid, s.block, 0, st, a, b, s.g, p, o0, o1, i0,
-                           i1);
-        break;
-    case kWriteF:
-        hipLaunchKernelGGL((io_kernel<T, L, S, kWriteF>), s.grid, s.block, 0, st, a, b, s.g, p, o0, o1, i0, i1);
-        break;
-    case kWriteEq:
-        hipLaunchKernelGGL((io_kernel<T, L, S, kWriteEq>), s.grid, s.block, 0, st, a, b, s.g, p, o0, o1, i0, i1);
-        break;
+    case kReadF: return launch_io_t<T, L, S, kReadF>(a, b, s, p, o0, o1, i0, i1, st);
+    case kReadMoments: return launch_io_t<T, L, S, kReadMoments>(a, b, s, p, o0, o1, i0, i1, st);
+    case kWriteF: return launch_io_t<T, L, S, kWriteF>(a, b, s, p, o0, o1, i0, i1, st);
+    case kWriteEq: return launch_io_t<T, L, S, kWriteEq>(a, b, s, p, o0, o1, i0, i1, st);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <typename T, int L>

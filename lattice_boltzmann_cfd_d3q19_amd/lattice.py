@@ -70,11 +70,11 @@ class Lattice:
         r = None if rho is None else self._dev(rho, (self.n,))
         v = None if u is None else self._dev(u, (3, self.n))
         capi.check(capi.lbm_init_equilibrium(self.handle, None if r is None else r.data_ptr(),
-                                             None if v is None else v.data_ptr()), "lbm_init_equilibrium")
+                                             None if v is None else v.data_ptr()), "lbm_init_equilibrium", self.handle)
         self._keep = (r, v)  # alive until the init kernel has run on the stream
 
     def step(self, n=1):
-        capi.check(capi.lbm_step(self.handle, n), "lbm_step")
+        capi.check(capi.lbm_step(self.handle, n), "lbm_step", self.handle)
 
     @property
     def t(self):
@@ -83,15 +83,15 @@ class Lattice:
     def moments(self):
         rho = torch.empty(self.n, dtype=self.dtype, device=self.device)
         u = torch.empty((3, self.n), dtype=self.dtype, device=self.device)
-        capi.check(capi.lbm_moments(self.handle, rho.data_ptr(), u.data_ptr()), "lbm_moments")
+        capi.check(capi.lbm_moments(self.handle, rho.data_ptr(), u.data_ptr()), "lbm_moments", self.handle)
         return rho, u
 
     def read_populations(self):
         f = torch.empty((Q, self.n), dtype=self.dtype, device=self.device)
-        capi.check(capi.lbm_read_populations(self.handle, f.data_ptr()), "lbm_read_populations")
+        capi.check(capi.lbm_read_populations(self.handle, f.data_ptr()), "lbm_read_populations", self.handle)
         return f
 
     def write_populations(self, f):
         ff = self._dev(f, (Q, self.n))
-        capi.check(capi.lbm_write_populations(self.handle, ff.data_ptr()), "lbm_write_populations")
+        capi.check(capi.lbm_write_populations(self.handle, ff.data_ptr()), "lbm_write_populations", self.handle)
         self._keep = (ff,)

@@ -122,3 +122,11 @@ def test_null_handle_and_status_strings():
     for code in (0, -1, -2, -3, -4, -5):
         assert capi.lbm_status_string(code) and capi.lbm_status_string(code) != "unknown status"
     assert capi.lbm_status_string(42) == "unknown status"
+
+
+def test_single_hip_runtime_in_process():
+    # torch bundles its own libamdhip64 (same soname); the library must bind to
+    # it rather than map a second HIP runtime (which would see no device).
+    maps = open("/proc/self/maps").read()
+    libs = {os.path.realpath(p) for p in re.findall(r"(/\S*libamdhip64\S*)", maps)}
+    assert len(libs) == 1, libs
