@@ -51,6 +51,10 @@ def workload(name):
     if name == "channel_f64":
         return dict(shape=(64, 64, 256), periodic=(1, 0, 1), tau=0.9, force=(0.0, 0.0, 1e-6), mask=None,
                     rho=None, u=None, precision="f64", extra={})
+    if name == "periodic256_mask0":
+        import numpy as np
+        return dict(shape=(256, 256, 256), periodic=(1, 1, 1), tau=0.65, force=(1e-6, 0.0, 0.0),
+                    mask=np.zeros(256 ** 3, np.uint8), rho=None, u=None, precision="f32", extra={})
     if name == "periodic256":
         return dict(shape=(256, 256, 256), periodic=(1, 1, 1), tau=0.65, force=(0.0, 0.0, 0.0), mask=None,
                     rho=None, u=None, precision="f32", extra={})

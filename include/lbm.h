@@ -130,8 +130,21 @@ lbm_status lbm_moments(lbm_sim *sim, void *rho, void *u);
 lbm_status lbm_read_populations(lbm_sim *sim, void *f);
 
 /* Replace the state by canonical populations f (device T[19][N]) at the
- * current t (checkpoint restore).  Values on solid cells are ignored. */
+ * current t (checkpoint restore).  Values on solid cells are ignored.
+ * Internally populations are stored shifted by their lattice weights
+ * (f_q - w_q); a write/read round trip returns f bit for bit when every f_q
+ * lies within a factor of two of w_q (any state with |u| below ~0.15), and
+ * otherwise within one unit in the last place of max(|f_q|, w_q). */
 lbm_status lbm_write_populations(lbm_sim *sim, const void *f);
+
+/* Exact checkpoint: copy out (save) or replace (load) the stored state,
+ * device T[19][N] in canonical order holding f_q - w_q (the populations minus
+ * their lattice weights, the form the kernels keep); 0 on solid cells for
+ * save, ignored there for load.  save followed by load restores the state bit
+ * for bit, so n steps, save, load into a fresh handle, n more steps equals 2n
+ * steps exactly. */
+lbm_status lbm_save_state(lbm_sim *sim, void *s);
+lbm_status lbm_load_state(lbm_sim *sim, const void *s);
 
 /* Release the handle (host memory only); NULL is a no-op. */
 lbm_status lbm_destroy(lbm_sim *sim);

@@ -24,8 +24,8 @@ LBM_LAYOUT_STREAM, LBM_LAYOUT_BUNDLE, LBM_LAYOUT_COLLISION = 0, 1, 2
 LBM_SCHEME_AB, LBM_SCHEME_AA = 0, 1
 
 EXPORTED = ["lbm_buffer_bytes", "lbm_create", "lbm_set_geometry", "lbm_init_equilibrium", "lbm_step",
-            "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_destroy", "lbm_time",
-            "lbm_last_hip_error", "lbm_status_string"]
+            "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_save_state",
+            "lbm_load_state", "lbm_destroy", "lbm_time", "lbm_last_hip_error", "lbm_status_string"]
 
 
 class lbm_desc(ctypes.Structure):
@@ -73,6 +73,10 @@ _lib.lbm_read_populations.argtypes = [_vp, _vp]
 _lib.lbm_read_populations.restype = _st
 _lib.lbm_write_populations.argtypes = [_vp, _vp]
 _lib.lbm_write_populations.restype = _st
+_lib.lbm_save_state.argtypes = [_vp, _vp]
+_lib.lbm_save_state.restype = _st
+_lib.lbm_load_state.argtypes = [_vp, _vp]
+_lib.lbm_load_state.restype = _st
 _lib.lbm_destroy.argtypes = [_vp]
 _lib.lbm_destroy.restype = _st
 _lib.lbm_time.argtypes = [_vp]
@@ -144,6 +148,14 @@ def lbm_read_populations(sim, f):
 
 def lbm_write_populations(sim, f):
     return _lib.lbm_write_populations(sim, _ptr(f))
+
+
+def lbm_save_state(sim, s):
+    return _lib.lbm_save_state(sim, _ptr(s))
+
+
+def lbm_load_state(sim, s):
+    return _lib.lbm_load_state(sim, _ptr(s))
 
 
 def lbm_destroy(sim):

@@ -244,6 +244,20 @@ lbm_status lbm_write_populations(lbm_sim* sim, const void* f)
     return io(sim, lbm::kWriteF, nullptr, nullptr, f, nullptr);
 }
 
+lbm_status lbm_save_state(lbm_sim* sim, void* s)
+{
+    if (sim == nullptr || s == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    return io(sim, lbm::kReadS, s, nullptr, nullptr, nullptr);
+}
+
+lbm_status lbm_load_state(lbm_sim* sim, const void* s)
+{
+    if (sim == nullptr || s == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    return io(sim, lbm::kWriteS, nullptr, nullptr, s, nullptr);
+}
+
 lbm_status lbm_destroy(lbm_sim* sim)
 {
     delete sim;

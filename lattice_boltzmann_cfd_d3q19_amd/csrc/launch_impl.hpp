@@ -121,6 +121,8 @@ hipError_t launch_io_s(int op, T* a, T* b, const Shape& s, const Phys<T>& p, T* 
     case kReadMoments: return launch_io_t<T, L, S, kReadMoments>(a, b, s, p, o0, o1, i0, i1, st);
     case kWriteF: return launch_io_t<T, L, S, kWriteF>(a, b, s, p, o0, o1, i0, i1, st);
     case kWriteEq: return launch_io_t<T, L, S, kWriteEq>(a, b, s, p, o0, o1, i0, i1, st);
+    case kReadS: return launch_io_t<T, L, S, kReadS>(a, b, s, p, o0, o1, i0, i1, st);
+    case kWriteS: return launch_io_t<T, L, S, kWriteS>(a, b, s, p, o0, o1, i0, i1, st);
     default: return hipErrorInvalidValue;
     }
 }

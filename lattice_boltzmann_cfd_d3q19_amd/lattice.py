@@ -95,3 +95,14 @@ class Lattice:
         ff = self._dev(f, (Q, self.n))
         capi.check(capi.lbm_write_populations(self.handle, ff.data_ptr()), "lbm_write_populations", self.handle)
         self._keep = (ff,)
+
+    def save_state(self):
+        """Exact checkpoint: stored values f - w, canonical order [19][N]."""
+        s = torch.empty((Q, self.n), dtype=self.dtype, device=self.device)
+        capi.check(capi.lbm_save_state(self.handle, s.data_ptr()), "lbm_save_state", self.handle)
+        return s
+
+    def load_state(self, s):
+        ss = self._dev(s, (Q, self.n))
+        capi.check(capi.lbm_load_state(self.handle, ss.data_ptr()), "lbm_load_state", self.handle)
+        self._keep = (ss,)

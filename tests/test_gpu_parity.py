@@ -113,7 +113,7 @@ def test_collision_free_streaming_bit_exact(precision, nsteps):
             say("omega0", precision, nsteps, layout, scheme)
             lat = make(shape, precision, layout, scheme, tau=math.inf, mask=mask, periodic=per, rho=rho, u=u)
             f0 = host_f(lat)
-            rel = 2e-7 if precision == "f32" else 1e-15
+            rel = 4e-7 if precision == "f32" else 1e-15
             assert np.max(np.abs(f0 - f0_oracle)) <= rel * np.max(np.abs(f0_oracle))
             lat.step(nsteps)
             got = host_f(lat)
@@ -125,22 +125,33 @@ def test_collision_free_streaming_bit_exact(precision, nsteps):
 
 @pytest.mark.parametrize("precision", ["f32", "f64"])
 def test_write_read_roundtrip_both_parities(precision):
+    """Lattice states (f_q within a factor 2 of w_q) round-trip bit for bit;
+    arbitrary values within one unit in the last place of max(|f_q|, w_q)."""
     need_gpu()
     shape, per = (33, 9, 14), (0, 1, 1)
     mask = li.random_mask(*shape, fraction=0.25, seed=9)
     n = int(np.prod(shape))
+    rho, u = li.random_fields(*shape, seed=2, drho=0.05, du=0.08)
+    box = oracle.Box(*shape, periodic=per, tau=0.7)
+    lattice_state = cast(oracle.init_equilibrium(box, mask, rho, u), precision).astype(np.float64)
     rng = np.random.default_rng(2)
-    f = cast(rng.uniform(0.01, 0.5, size=(Q, n)), precision).astype(np.float64)
-    f[:, mask.astype(bool)] = 0.0
+    arbitrary = cast(rng.uniform(0.0, 0.5, size=(Q, n)), precision).astype(np.float64)
+    arbitrary[:, mask.astype(bool)] = 0.0
+    ftype = np.float32 if precision == "f32" else np.float64
     for layout in LAYOUTS:
         for scheme in SCHEMES:
             for pre_steps in (0, 1):
                 say("roundtrip", precision, layout, scheme, pre_steps)
                 lat = make(shape, precision, layout, scheme, tau=0.7, mask=mask, periodic=per)
                 lat.step(pre_steps)
-                lat.write_populations(cast(f, precision))
+                lat.write_populations(cast(lattice_state, precision))
+                assert np.array_equal(host_f(lat), lattice_state), (layout, scheme, pre_steps)
+                lat.write_populations(cast(arbitrary, precision))
                 got = host_f(lat)
-                assert np.array_equal(got, f), (layout, scheme, pre_steps)
+                _, w, _ = oracle.lattice()
+                big = np.maximum(np.abs(arbitrary), w[:, None]).astype(ftype)
+                ulp = np.spacing(big).astype(np.float64)
+                assert np.all(np.abs(got - arbitrary) <= ulp), (layout, scheme, pre_steps)
 
 
 @pytest.mark.parametrize("precision", ["f32", "f64"])
@@ -166,6 +177,8 @@ def test_moments_match_oracle(precision):
 
 
 def test_checkpoint_resume_bit_exact():
+    """n steps, save_state, load into a fresh handle (another layout), n steps
+    == 2n steps bit for bit; through canonical populations, within rounding."""
     need_gpu()
     shape, per, F = (30, 20, 10), (1, 1, 1), (1e-5, 0.0, 0.0)
     mask = li.sphere_mask(*shape, radius=4)
@@ -177,11 +190,16 @@ def test_checkpoint_resume_bit_exact():
         want = host_f(full)
         half = make(shape, "f32", "stream", scheme, tau=0.7, force=F, mask=mask, rho=rho, u=u)
         half.step(5)
-        snap = half.read_populations().clone()
+        snap = half.save_state().clone()
+        pops = half.read_populations().clone()
         resumed = make(shape, "f32", "bundle", scheme, tau=0.7, force=F, mask=mask)
-        resumed.write_populations(snap)
+        resumed.load_state(snap)
         resumed.step(5)
         assert np.array_equal(host_f(resumed), want)
+        approx = make(shape, "f32", "collision", scheme, tau=0.7, force=F, mask=mask)
+        approx.write_populations(pops)
+        approx.step(5)
+        assert np.max(np.abs(host_f(approx) - want)) <= 1e-6
 
 
 # ----------------------------------- full-size boxes: sampled one-step checks
