@@ -27,6 +27,10 @@
  *                         (c_y, c_z) (one stencil row each); cell-major
  *                         inside a bundle.
  *   LBM_LAYOUT_COLLISION  AoS: the 19 populations of a cell are contiguous.
+ *   LBM_LAYOUT_COMPACT    SoA over fluid cells only: population q of the i-th
+ *                         fluid cell (in cell order) at q * S + i.  Needs a
+ *                         workspace (lbm_set_workspace) for its neighbour
+ *                         tables; in porous media it moves only fluid bytes.
  *
  * Conventions shared by every entry point:
  *  - Cell index: cell = x + nx * (y + ny * z), N = nx * ny * nz.
@@ -72,6 +76,7 @@ typedef int32_t lbm_status;
 #define LBM_LAYOUT_STREAM 0
 #define LBM_LAYOUT_BUNDLE 1
 #define LBM_LAYOUT_COLLISION 2
+#define LBM_LAYOUT_COMPACT 3
 
 #define LBM_SCHEME_AB 0
 #define LBM_SCHEME_AA 1
@@ -89,9 +94,15 @@ typedef struct lbm_desc {
 
 typedef struct lbm_sim lbm_sim; /* opaque handle (host memory only) */
 
-/* Size of one population buffer, 19 * N * sizeof(T) bytes, and how many the
- * scheme needs (2 for AB, 1 for AA).  Host only; never touches the GPU. */
+/* Size of one population buffer, 19 * N * sizeof(T) bytes (compact layout:
+ * 19 * roundup(N, 64) * sizeof(T), room for an all-fluid box), and how many
+ * the scheme needs (2 for AB, 1 for AA).  Host only; never touches the GPU. */
 lbm_status lbm_buffer_bytes(const lbm_desc *desc, size_t *bytes_per_buffer, int32_t *n_buffers);
+
+/* Device workspace the layout needs for geometry tables: 0 for the dense
+ * layouts; for LBM_LAYOUT_COMPACT about 4 bytes per cell of the box padded by
+ * one halo layer plus 4 bytes per cell (index tables).  Host only. */
+lbm_status lbm_workspace_bytes(const lbm_desc *desc, size_t *bytes);
 
 /* Create a handle over caller-owned population memory.
  *   buf0, buf1   device buffers of lbm_buffer_bytes() bytes each, 256-byte
@@ -102,6 +113,13 @@ lbm_status lbm_buffer_bytes(const lbm_desc *desc, size_t *bytes_per_buffer, int3
  * initialised.  Host only. */
 lbm_status lbm_create(const lbm_desc *desc, void *buf0, void *buf1, void *hip_stream,
                       lbm_sim **out);
+
+/* Attach caller-owned device workspace (256-byte aligned, at least
+ * lbm_workspace_bytes() bytes; NULL detaches).  The library writes its
+ * geometry tables there at lbm_init_equilibrium and reads them every step;
+ * it must stay alive and untouched.  Invalidates the state (re-init).
+ * Host only. */
+lbm_status lbm_set_workspace(lbm_sim *sim, void *ws, size_t bytes);
 
 /* Solid mask and boundary kind per axis (PortLBM section 3.1, halfway bounce-back).
  *   mask       device uint8[N], 0 = fluid, nonzero = solid; NULL = no solids.
@@ -115,7 +133,10 @@ lbm_status lbm_set_geometry(lbm_sim *sim, const uint8_t *mask, const int32_t per
  *   rho   device T[N] or NULL (rho = 1).
  *   u     device T[3][N] (component-major) or NULL (u = 0).
  * AB stores the streaming pre-image of f(0) in buf0, so that the first fused
- * pull-collide step acts on f(0) itself. */
+ * pull-collide step acts on f(0) itself.  LBM_LAYOUT_COMPACT first builds its
+ * neighbour tables from the mask and the periodic flags in the workspace
+ * (LBM_ERR_BAD_STATE without one) and then waits once on the stream to learn
+ * the fluid-cell count: the only call that blocks the host. */
 lbm_status lbm_init_equilibrium(lbm_sim *sim, const void *rho, const void *u);
 
 /* Advance n >= 0 time steps (one fused kernel launch each); t += n. */
@@ -151,6 +172,10 @@ lbm_status lbm_destroy(lbm_sim *sim);
 
 /* Current time step t, or -1 for a NULL handle. */
 int64_t lbm_time(const lbm_sim *sim);
+
+/* Fluid cells counted by the compact layout's table build; -1 before init or
+ * for a dense layout. */
+int64_t lbm_fluid_cells(const lbm_sim *sim);
 
 /* Name of the HIP error behind the handle's last LBM_ERR_HIP ("hipSuccess" if
  * none; "no handle" for NULL).  Static string; host only. */

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblbm.so")
-SOURCES = ["launch_f32.hip", "launch_f64.hip", "capi.cpp"]
+SOURCES = ["launch_f32.hip", "launch_f64.hip", "compact_build.hip", "capi.cpp"]
 ARCH = os.environ.get("LBM_OFFLOAD_ARCH", "gfx950")
 
 

@@ -20,12 +20,13 @@ LBM_ERR_MISALIGNED = -4
 LBM_ERR_HIP = -5
 
 LBM_F32, LBM_F64 = 0, 1
-LBM_LAYOUT_STREAM, LBM_LAYOUT_BUNDLE, LBM_LAYOUT_COLLISION = 0, 1, 2
+LBM_LAYOUT_STREAM, LBM_LAYOUT_BUNDLE, LBM_LAYOUT_COLLISION, LBM_LAYOUT_COMPACT = 0, 1, 2, 3
 LBM_SCHEME_AB, LBM_SCHEME_AA = 0, 1
 
-EXPORTED = ["lbm_buffer_bytes", "lbm_create", "lbm_set_geometry", "lbm_init_equilibrium", "lbm_step",
+EXPORTED = ["lbm_buffer_bytes", "lbm_workspace_bytes", "lbm_create", "lbm_set_workspace", "lbm_set_geometry", "lbm_init_equilibrium", "lbm_step",
             "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_save_state",
-            "lbm_load_state", "lbm_destroy", "lbm_time", "lbm_last_hip_error", "lbm_status_string"]
+            "lbm_load_state", "lbm_destroy", "lbm_time", "lbm_fluid_cells", "lbm_last_hip_error",
+            "lbm_status_string"]
 
 
 class lbm_desc(ctypes.Structure):
@@ -59,6 +60,12 @@ _Desc_p = ctypes.POINTER(lbm_desc)
 
 _lib.lbm_buffer_bytes.argtypes = [_Desc_p, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_i32)]
 _lib.lbm_buffer_bytes.restype = _st
+_lib.lbm_workspace_bytes.argtypes = [_Desc_p, ctypes.POINTER(ctypes.c_size_t)]
+_lib.lbm_workspace_bytes.restype = _st
+_lib.lbm_set_workspace.argtypes = [_vp, _vp, ctypes.c_size_t]
+_lib.lbm_set_workspace.restype = _st
+_lib.lbm_fluid_cells.argtypes = [_vp]
+_lib.lbm_fluid_cells.restype = _i64
 _lib.lbm_create.argtypes = [_Desc_p, _vp, _vp, _vp, ctypes.POINTER(_vp)]
 _lib.lbm_create.restype = _st
 _lib.lbm_set_geometry.argtypes = [_vp, _vp, ctypes.POINTER(_i32)]
@@ -116,6 +123,21 @@ def lbm_buffer_bytes(desc):
     n = _i32(0)
     st = _lib.lbm_buffer_bytes(ctypes.byref(desc), ctypes.byref(nb), ctypes.byref(n))
     return st, nb.value, n.value
+
+
+def lbm_workspace_bytes(desc):
+    """Return (status, bytes)."""
+    nb = ctypes.c_size_t(0)
+    st = _lib.lbm_workspace_bytes(ctypes.byref(desc), ctypes.byref(nb))
+    return st, nb.value
+
+
+def lbm_set_workspace(sim, ws, nbytes):
+    return _lib.lbm_set_workspace(sim, _ptr(ws), int(nbytes))
+
+
+def lbm_fluid_cells(sim):
+    return _lib.lbm_fluid_cells(sim)
 
 
 def lbm_create(desc, buf0, buf1=None, stream=None):

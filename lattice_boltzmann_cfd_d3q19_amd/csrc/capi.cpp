@@ -1,7 +1,7 @@
 // capi.cpp -- the C ABI of liblbm.so (declared in include/lbm.h).
 //
 // Validation and the state machine live here, on the host; every GPU action
-// is one kernel launch through launch.hpp on the handle's stream.
+// is a kernel launch through launch.hpp on the handle's stream.
 //
 // Stored state per scheme (what "canonical f(t)" is read from):
 //   AB: buffer `cur` holds h(t), the post-collision values of step t-1 (for
@@ -11,6 +11,7 @@
 //   AA: the single buffer holds f(t) in natural slots when t is even, and the
 //       post-collision values of step t-1 in the swapped slots of the
 //       in-place pattern when t is odd (fieldcraft page, first section).
+// Either way the values are stored shifted by the lattice weights (f - w).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -29,7 +30,9 @@ struct lbm_sim {
     hipStream_t stream;
     const uint8_t* mask;
     int32_t periodic[3];
-    int32_t xcd_remap;
+    void* ws;  // caller-owned workspace (compact layout tables)
+    size_t ws_bytes;
+    lbm::CompactTables tables;
     bool initialized;
     int64_t t;
     int cur;  // AB: index of the buffer holding h(t)
@@ -41,24 +44,27 @@ namespace {
 
 constexpr uintptr_t kAlign = 256;
 
-bool is_finite(double v) { return std::isfinite(v); }
+bool compact(const lbm_desc& d) { return d.layout == LBM_LAYOUT_COMPACT; }
 
 lbm_status validate_desc(const lbm_desc* d)
 {
     if (d == nullptr) return LBM_ERR_INVALID_ARGUMENT;
     if (d->nx < 1 || d->ny < 1 || d->nz < 1) return LBM_ERR_INVALID_ARGUMENT;
     if (d->precision != LBM_F32 && d->precision != LBM_F64) return LBM_ERR_INVALID_ARGUMENT;
-    if (d->layout != LBM_LAYOUT_STREAM && d->layout != LBM_LAYOUT_BUNDLE && d->layout != LBM_LAYOUT_COLLISION)
+    if (d->layout != LBM_LAYOUT_STREAM && d->layout != LBM_LAYOUT_BUNDLE && d->layout != LBM_LAYOUT_COLLISION &&
+        d->layout != LBM_LAYOUT_COMPACT)
         return LBM_ERR_INVALID_ARGUMENT;
     if (d->scheme != LBM_SCHEME_AB && d->scheme != LBM_SCHEME_AA) return LBM_ERR_INVALID_ARGUMENT;
     if (d->reserved != 0) return LBM_ERR_INVALID_ARGUMENT;
     if (std::isnan(d->tau) || !(d->tau > 0.5)) return LBM_ERR_INVALID_ARGUMENT;
-    if (std::isinf(d->tau) && d->tau < 0) return LBM_ERR_INVALID_ARGUMENT;
     for (int a = 0; a < 3; ++a)
-        if (!is_finite(d->force[a])) return LBM_ERR_INVALID_ARGUMENT;
-    // cell indices are 32-bit inside the kernels; the workgroup count too
+        if (!std::isfinite(d->force[a])) return LBM_ERR_INVALID_ARGUMENT;
+    // cell indices are 32-bit inside the kernels; so is the padded index of
+    // the compact layout's neighbour table
     const double n = (double)d->nx * (double)d->ny * (double)d->nz;
     if (d->nx > INT32_MAX || d->ny > INT32_MAX || d->nz > INT32_MAX || n >= 2147483648.0)
+        return LBM_ERR_UNSUPPORTED;
+    if (compact(*d) && (double)(d->nx + 2) * (double)(d->ny + 2) * (double)(d->nz + 2) >= 4294967295.0)
         return LBM_ERR_UNSUPPORTED;
     return LBM_OK;
 }
@@ -66,6 +72,13 @@ lbm_status validate_desc(const lbm_desc* d)
 size_t elem_size(const lbm_desc& d) { return d.precision == LBM_F64 ? 8 : 4; }
 
 uint64_t ncells(const lbm_desc& d) { return (uint64_t)d.nx * (uint64_t)d.ny * (uint64_t)d.nz; }
+
+// Population buffer size; the compact layout reserves room for an all-fluid box.
+size_t buffer_bytes(const lbm_desc& d)
+{
+    const uint64_t cells = compact(d) ? (ncells(d) + 63) / 64 * 64 : ncells(d);
+    return (size_t)lbm::kQ * cells * elem_size(d);
+}
 
 lbm::LaunchGeom geom_of(const lbm_sim* s)
 {
@@ -75,7 +88,6 @@ lbm::LaunchGeom geom_of(const lbm_sim* s)
     g.nz = s->d.nz;
     for (int a = 0; a < 3; ++a) g.periodic[a] = s->periodic[a];
     g.mask = s->mask;
-    g.xcd_remap = s->xcd_remap;
     return g;
 }
 
@@ -98,24 +110,60 @@ int state_kind(const lbm_sim* s)
     return (s->t % 2 == 0) ? lbm::kAAEven : lbm::kAAOdd;
 }
 
+lbm_status hip_status(lbm_sim* s, hipError_t e)
+{
+    if (e == hipSuccess) return LBM_OK;
+    s->last_hip = e;
+    return LBM_ERR_HIP;
+}
+
 lbm_status io(lbm_sim* s, int op, void* out0, void* out1, const void* in0, const void* in1)
 {
     const lbm::LaunchGeom g = geom_of(s);
     const lbm::LaunchPhys p = phys_of(s);
     const int st = state_kind(s);
     void* a = s->d.scheme == LBM_SCHEME_AB ? s->buf[s->cur] : s->buf[0];
-    void* b = (s->d.scheme == LBM_SCHEME_AB && op == lbm::kWriteEq) ? s->buf[1 - s->cur] : nullptr;
     hipError_t e;
+    if (compact(s->d)) {
+        if (s->d.precision == LBM_F32)
+            e = lbm::launch_io_compact<float>(st, op, (float*)a, g, s->tables, p, (float*)out0, (float*)out1,
+                                              (const float*)in0, (const float*)in1, s->stream);
+        else
+            e = lbm::launch_io_compact<double>(st, op, (double*)a, g, s->tables, p, (double*)out0, (double*)out1,
+                                               (const double*)in0, (const double*)in1, s->stream);
+        return hip_status(s, e);
+    }
+    void* b = (s->d.scheme == LBM_SCHEME_AB && op == lbm::kWriteEq) ? s->buf[1 - s->cur] : nullptr;
     if (s->d.precision == LBM_F32)
         e = lbm::launch_io<float>(s->d.layout, st, op, (float*)a, (float*)b, g, p, (float*)out0, (float*)out1,
                                   (const float*)in0, (const float*)in1, s->stream);
     else
         e = lbm::launch_io<double>(s->d.layout, st, op, (double*)a, (double*)b, g, p, (double*)out0,
                                    (double*)out1, (const double*)in0, (const double*)in1, s->stream);
-    if (e != hipSuccess) {
-        s->last_hip = e;
-        return LBM_ERR_HIP;
-    }
+    return hip_status(s, e);
+}
+
+// Compact layout: build the tables, then learn the fluid count (one wait).
+lbm_status build_compact(lbm_sim* s)
+{
+    if (s->ws == nullptr) return LBM_ERR_BAD_STATE;
+    const lbm::CompactLayoutBytes lay = lbm::compact_workspace_layout(s->d.nx, s->d.ny, s->d.nz);
+    char* base = (char*)s->ws;
+    lbm::CompactTables& t = s->tables;
+    t.header = (uint32_t*)(base + lay.header);
+    t.rows = (uint32_t*)(base + lay.rows);
+    t.idxp = (uint32_t*)(base + lay.idxp);
+    t.cellp = (uint32_t*)(base + lay.cellp);
+    t.nf = 0;
+    t.stride = 0;
+    hipError_t e = lbm::launch_compact_build(geom_of(s), t, s->stream);
+    if (e != hipSuccess) return hip_status(s, e);
+    uint32_t nf = 0;
+    e = hipMemcpyAsync(&nf, t.header, sizeof(nf), hipMemcpyDeviceToHost, s->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(s->stream);
+    if (e != hipSuccess) return hip_status(s, e);
+    t.nf = nf;
+    t.stride = ((uint64_t)nf + 63) / 64 * 64;
     return LBM_OK;
 }
 
@@ -128,8 +176,17 @@ lbm_status lbm_buffer_bytes(const lbm_desc* desc, size_t* bytes_per_buffer, int3
     const lbm_status v = validate_desc(desc);
     if (v != LBM_OK) return v;
     if (bytes_per_buffer == nullptr && n_buffers == nullptr) return LBM_ERR_INVALID_ARGUMENT;
-    if (bytes_per_buffer) *bytes_per_buffer = (size_t)lbm::kQ * ncells(*desc) * elem_size(*desc);
+    if (bytes_per_buffer) *bytes_per_buffer = buffer_bytes(*desc);
     if (n_buffers) *n_buffers = desc->scheme == LBM_SCHEME_AB ? 2 : 1;
+    return LBM_OK;
+}
+
+lbm_status lbm_workspace_bytes(const lbm_desc* desc, size_t* bytes)
+{
+    const lbm_status v = validate_desc(desc);
+    if (v != LBM_OK) return v;
+    if (bytes == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    *bytes = compact(*desc) ? lbm::compact_workspace_layout(desc->nx, desc->ny, desc->nz).total : 0;
     return LBM_OK;
 }
 
@@ -144,7 +201,7 @@ lbm_status lbm_create(const lbm_desc* desc, void* buf0, void* buf1, void* hip_st
     if (desc->scheme == LBM_SCHEME_AB && buf1 == nullptr) return LBM_ERR_INVALID_ARGUMENT;
     if ((uintptr_t)buf0 % kAlign != 0 || (buf1 && (uintptr_t)buf1 % kAlign != 0)) return LBM_ERR_MISALIGNED;
     if (buf1 != nullptr) {
-        const uintptr_t bytes = (uintptr_t)((size_t)lbm::kQ * ncells(*desc) * elem_size(*desc));
+        const uintptr_t bytes = (uintptr_t)buffer_bytes(*desc);
         const uintptr_t p0 = (uintptr_t)buf0, p1 = (uintptr_t)buf1;
         if (p0 < p1 + bytes && p1 < p0 + bytes) return LBM_ERR_INVALID_ARGUMENT;  // overlap
     }
@@ -156,14 +213,29 @@ lbm_status lbm_create(const lbm_desc* desc, void* buf0, void* buf1, void* hip_st
     s->stream = (hipStream_t)hip_stream;
     s->mask = nullptr;
     s->periodic[0] = s->periodic[1] = s->periodic[2] = 1;
-    const char* env = std::getenv("LBM_XCD_REMAP");
-    s->xcd_remap = (env != nullptr && env[0] == '1') ? 1 : 0;
+    s->ws = nullptr;
+    s->ws_bytes = 0;
     s->initialized = false;
     s->t = 0;
     s->cur = 0;
     s->omega = std::isinf(desc->tau) ? 0.0 : 1.0 / desc->tau;
     s->last_hip = hipSuccess;
     *out = s;
+    return LBM_OK;
+}
+
+lbm_status lbm_set_workspace(lbm_sim* sim, void* ws, size_t bytes)
+{
+    if (sim == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (ws != nullptr && (uintptr_t)ws % kAlign != 0) return LBM_ERR_MISALIGNED;
+    size_t need = 0;
+    lbm_workspace_bytes(&sim->d, &need);
+    if (ws != nullptr && bytes < need) return LBM_ERR_INVALID_ARGUMENT;
+    sim->ws = ws;
+    sim->ws_bytes = ws == nullptr ? 0 : bytes;
+    sim->initialized = false;
+    sim->t = 0;
+    sim->cur = 0;
     return LBM_OK;
 }
 
@@ -183,9 +255,14 @@ lbm_status lbm_set_geometry(lbm_sim* sim, const uint8_t* mask, const int32_t per
 lbm_status lbm_init_equilibrium(lbm_sim* sim, const void* rho, const void* u)
 {
     if (sim == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (compact(sim->d) && sim->ws == nullptr) return LBM_ERR_BAD_STATE;
     sim->t = 0;
     sim->cur = 0;
     sim->initialized = false;
+    if (compact(sim->d)) {
+        const lbm_status b = build_compact(sim);
+        if (b != LBM_OK) return b;
+    }
     const lbm_status r = io(sim, lbm::kWriteEq, nullptr, nullptr, rho, u);
     if (r == LBM_OK) sim->initialized = true;
     return r;
@@ -209,14 +286,17 @@ lbm_status lbm_step(lbm_sim* sim, int64_t n)
             a = sim->buf[0];
         }
         hipError_t e;
-        if (sim->d.precision == LBM_F32)
+        if (compact(sim->d)) {
+            if (sim->d.precision == LBM_F32)
+                e = lbm::launch_step_compact<float>(kind, (float*)a, (float*)b, g, sim->tables, p, sim->stream);
+            else
+                e = lbm::launch_step_compact<double>(kind, (double*)a, (double*)b, g, sim->tables, p, sim->stream);
+        } else if (sim->d.precision == LBM_F32) {
             e = lbm::launch_step<float>(sim->d.layout, kind, (float*)a, (float*)b, g, p, sim->stream);
-        else
+        } else {
             e = lbm::launch_step<double>(sim->d.layout, kind, (double*)a, (double*)b, g, p, sim->stream);
-        if (e != hipSuccess) {
-            sim->last_hip = e;
-            return LBM_ERR_HIP;
         }
+        if (e != hipSuccess) return hip_status(sim, e);
         if (sim->d.scheme == LBM_SCHEME_AB) sim->cur = 1 - sim->cur;
         sim->t += 1;
     }
@@ -266,6 +346,12 @@ lbm_status lbm_destroy(lbm_sim* sim)
 
 int64_t lbm_time(const lbm_sim* sim) { return sim == nullptr ? -1 : sim->t; }
 
+int64_t lbm_fluid_cells(const lbm_sim* sim)
+{
+    if (sim == nullptr || !sim->initialized || !compact(sim->d)) return -1;
+    return (int64_t)sim->tables.nf;
+}
+
 const char* lbm_last_hip_error(const lbm_sim* sim)
 {
     if (sim == nullptr) return "no handle";
@@ -278,8 +364,8 @@ const char* lbm_status_string(lbm_status status)
     case LBM_OK: return "ok";
     case LBM_ERR_INVALID_ARGUMENT: return "invalid argument";
     case LBM_ERR_UNSUPPORTED: return "unsupported size or option";
-    case LBM_ERR_BAD_STATE: return "call out of order (create, set_geometry, init, then step)";
-    case LBM_ERR_MISALIGNED: return "population buffer not 256-byte aligned";
+    case LBM_ERR_BAD_STATE: return "call out of order (create, [set_workspace, set_geometry], init, then step)";
+    case LBM_ERR_MISALIGNED: return "device buffer not 256-byte aligned";
     case LBM_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
     }

@@ -1,0 +1,155 @@
+// compact_build.hip -- device construction of the compact layout's tables
+// (row counts, their exclusive scan, per-row compact indices, periodic halo).
+#include "kernels_compact.hpp"
+#include "launch.hpp"
+
+namespace lbm {
+
+// ------------------------------------------------------- table building
+
+// Fluid cells per x-row; one workgroup per row r = y + ny z.
+__global__ void __launch_bounds__(kBlockThreads) compact_count_rows(const uint8_t* __restrict__ mask, uint32_t nx,
+                                                                    uint32_t* __restrict__ row_count)
+{
+    __shared__ uint32_t part[kBlockThreads / 64];
+    const uint32_t r = blockIdx.x;
+    uint32_t cnt = 0;
+    for (uint32_t x = threadIdx.x; x < nx; x += kBlockThreads)
+        cnt += (mask == nullptr || mask[(uint64_t)r * nx + x] == 0) ? 1u : 0u;
+    // wave64 reduction, then across the four waves
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_down(cnt, o, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x / 64] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < kBlockThreads / 64; ++w) t += part[w];
+        row_count[r] = t;
+    }
+}
+
+// Exclusive scan of the row counts in place (one workgroup of 1024), total in
+// *total.  Each thread owns a contiguous chunk of rows.
+__global__ void __launch_bounds__(1024) compact_scan_rows(uint32_t* __restrict__ rows, uint32_t nrows,
+                                                          uint32_t* __restrict__ total)
+{
+    __shared__ uint32_t sums[1024];
+    const uint32_t t = threadIdx.x;
+    const uint32_t chunk = (nrows + 1023u) / 1024u;
+    const uint32_t lo = min(nrows, t * chunk), hi = min(nrows, lo + chunk);
+    uint32_t s = 0;
+    for (uint32_t r = lo; r < hi; ++r) s += rows[r];
+    sums[t] = s;
+    __syncthreads();
+    // Hillis-Steele inclusive scan over the 1024 chunk sums
+    for (uint32_t o = 1; o < 1024; o <<= 1) {
+        const uint32_t v = t >= o ? sums[t - o] : 0u;
+        __syncthreads();
+        sums[t] += v;
+        __syncthreads();
+    }
+    uint32_t run = sums[t] - s;  // exclusive prefix of this chunk
+    for (uint32_t r = lo; r < hi; ++r) {
+        const uint32_t v = rows[r];
+        rows[r] = run;
+        run += v;
+    }
+    if (t == 1023) *total = sums[1023];
+}
+
+// Compact indices of the cells of row r (one workgroup per row), in x order.
+__global__ void __launch_bounds__(kBlockThreads) compact_fill_rows(const uint8_t* __restrict__ mask, uint32_t nx,
+                                                                   uint32_t ny, uint32_t px, uint32_t pxy,
+                                                                   const uint32_t* __restrict__ row_start,
+                                                                   uint32_t* __restrict__ idxp,
+                                                                   uint32_t* __restrict__ cellp)
+{
+    __shared__ uint32_t wave_tot[kBlockThreads / 64];
+    const uint32_t r = blockIdx.x;
+    const uint32_t y = r % ny, z = r / ny;
+    uint32_t base = row_start[r];
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x / 64;
+    for (uint32_t x0 = 0; x0 < nx; x0 += kBlockThreads) {
+        const uint32_t x = x0 + threadIdx.x;
+        const bool inside = x < nx;
+        const bool fluid = inside && (mask == nullptr || mask[(uint64_t)r * nx + x] == 0);
+        const uint64_t bal = __ballot(fluid);
+        const uint32_t below = __popcll(bal & ((1ull << lane) - 1ull));  // fluid lanes before this one
+        if (lane == 0) wave_tot[wave] = __popcll(bal);
+        __syncthreads();
+        uint32_t before = 0, all = 0;
+        for (uint32_t w = 0; w < kBlockThreads / 64; ++w) {
+            before += w < wave ? wave_tot[w] : 0u;
+            all += wave_tot[w];
+        }
+        if (inside) {
+            const uint32_t p = (x + 1) + px * (y + 1) + pxy * (z + 1);
+            if (fluid) {
+                const uint32_t i = base + before + below;
+                idxp[p] = i;
+                cellp[i] = p;
+            } else {
+                idxp[p] = kInvalid;
+            }
+        }
+        base += all;
+        __syncthreads();
+    }
+}
+
+// Halo of idxp: periodic image or kInvalid (beyond a wall).
+__global__ void __launch_bounds__(kBlockThreads) compact_fill_halo(uint32_t nx, uint32_t ny, uint32_t nz,
+                                                                   uint32_t per_x, uint32_t per_y, uint32_t per_z,
+                                                                   uint32_t px, uint32_t pxy, uint64_t npad,
+                                                                   uint32_t* __restrict__ idxp)
+{
+    const uint64_t p = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+    if (p >= npad) return;
+    const uint32_t pp = (uint32_t)p;
+    const int32_t gx = (int32_t)(pp % px) - 1;
+    const int32_t gy = (int32_t)((pp / px) % (ny + 2)) - 1;
+    const int32_t gz = (int32_t)(pp / pxy) - 1;
+    const bool ox = gx < 0 || gx >= (int32_t)nx, oy = gy < 0 || gy >= (int32_t)ny, oz = gz < 0 || gz >= (int32_t)nz;
+    if (!ox && !oy && !oz) return;  // interior: filled per row
+    if ((ox && !per_x) || (oy && !per_y) || (oz && !per_z)) {
+        idxp[pp] = kInvalid;
+        return;
+    }
+    const uint32_t ix = (uint32_t)((gx + (int32_t)nx) % (int32_t)nx);
+    const uint32_t iy = (uint32_t)((gy + (int32_t)ny) % (int32_t)ny);
+    const uint32_t iz = (uint32_t)((gz + (int32_t)nz) % (int32_t)nz);
+    idxp[pp] = idxp[(ix + 1) + px * (iy + 1) + pxy * (iz + 1)];
+}
+
+
+CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz)
+{
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    CompactLayoutBytes b{};
+    const size_t nrows = (size_t)ny * (size_t)nz;
+    const size_t npad = (size_t)(nx + 2) * (size_t)(ny + 2) * (size_t)(nz + 2);
+    const size_t n64 = ((size_t)nx * (size_t)ny * (size_t)nz + 63) / 64 * 64;
+    b.header = 0;
+    b.rows = 256;
+    b.idxp = b.rows + up(4 * nrows);
+    b.cellp = b.idxp + up(4 * npad);
+    b.total = b.cellp + up(4 * n64);
+    return b;
+}
+
+hipError_t launch_compact_build(const LaunchGeom& lg, const CompactTables& t, hipStream_t st)
+{
+    const uint32_t nx = (uint32_t)lg.nx, ny = (uint32_t)lg.ny, nz = (uint32_t)lg.nz;
+    const uint32_t nrows = ny * nz;
+    const uint32_t px = nx + 2, pxy = (nx + 2) * (ny + 2);
+    const uint64_t npad = (uint64_t)pxy * (nz + 2);
+    hipLaunchKernelGGL(compact_count_rows, dim3(nrows), dim3(kBlockThreads), 0, st, lg.mask, nx, t.rows);
+    hipLaunchKernelGGL(compact_scan_rows, dim3(1), dim3(1024), 0, st, t.rows, nrows, t.header);
+    hipLaunchKernelGGL(compact_fill_rows, dim3(nrows), dim3(kBlockThreads), 0, st, lg.mask, nx, ny, px, pxy,
+                       (const uint32_t*)t.rows, t.idxp, t.cellp);
+    hipLaunchKernelGGL(compact_fill_halo, dim3((uint32_t)((npad + kBlockThreads - 1) / kBlockThreads)),
+                       dim3(kBlockThreads), 0, st, nx, ny, nz, (uint32_t)(lg.periodic[0] != 0),
+                       (uint32_t)(lg.periodic[1] != 0), (uint32_t)(lg.periodic[2] != 0), px, pxy, npad, t.idxp);
+    return hipGetLastError();
+}
+
+}  // namespace lbm

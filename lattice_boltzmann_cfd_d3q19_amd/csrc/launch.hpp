@@ -10,7 +10,6 @@ struct LaunchGeom {
     int64_t nx, ny, nz;
     int32_t periodic[3];
     const uint8_t* mask;
-    int32_t xcd_remap;
 };
 
 struct LaunchPhys {
@@ -29,5 +28,32 @@ hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& g, co
 template <typename T>
 hipError_t launch_io(int layout, int state, int op, T* a, T* b, const LaunchGeom& g, const LaunchPhys& p,
                      T* out0, T* out1, const T* in0, const T* in1, hipStream_t s);
+
+// Tables of the fluid-compacted layout, carved out of the caller's workspace.
+struct CompactTables {
+    uint32_t* header;  // [0] = fluid cell count, written by the build
+    uint32_t* rows;    // per x-row fluid counts, then their exclusive scan
+    uint32_t* idxp;    // halo-padded cell -> compact index (kInvalid: solid / wall)
+    uint32_t* cellp;   // compact index -> padded cell
+    uint32_t nf;       // fluid cells (known on the host after the build)
+    uint64_t stride;   // population stride, nf rounded up to 64
+};
+
+// Byte offsets of the tables inside a workspace, and its size.
+struct CompactLayoutBytes {
+    size_t header, rows, idxp, cellp, total;
+};
+CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz);
+
+// Build the compact tables from the mask and the periodic flags.
+hipError_t launch_compact_build(const LaunchGeom& g, const CompactTables& t, hipStream_t s);
+
+template <typename T>
+hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& g, const CompactTables& t,
+                               const LaunchPhys& p, hipStream_t s);
+
+template <typename T>
+hipError_t launch_io_compact(int state, int op, T* a, const LaunchGeom& g, const CompactTables& t,
+                             const LaunchPhys& p, T* out0, T* out1, const T* in0, const T* in1, hipStream_t s);
 
 }  // namespace lbm

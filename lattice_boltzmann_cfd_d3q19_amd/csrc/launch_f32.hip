@@ -6,4 +6,8 @@ template hipError_t launch_step<float>(int, int, float*, float*, const LaunchGeo
                                        hipStream_t);
 template hipError_t launch_io<float>(int, int, int, float*, float*, const LaunchGeom&, const LaunchPhys&,
                                      float*, float*, const float*, const float*, hipStream_t);
+template hipError_t launch_step_compact<float>(int, float*, float*, const LaunchGeom&, const CompactTables&,
+                                               const LaunchPhys&, hipStream_t);
+template hipError_t launch_io_compact<float>(int, int, float*, const LaunchGeom&, const CompactTables&,
+                                             const LaunchPhys&, float*, float*, const float*, const float*, hipStream_t);
 }  // namespace lbm

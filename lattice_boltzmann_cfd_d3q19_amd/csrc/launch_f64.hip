@@ -6,4 +6,8 @@ template hipError_t launch_step<double>(int, int, double*, double*, const Launch
                                         hipStream_t);
 template hipError_t launch_io<double>(int, int, int, double*, double*, const LaunchGeom&, const LaunchPhys&,
                                       double*, double*, const double*, const double*, hipStream_t);
+template hipError_t launch_step_compact<double>(int, double*, double*, const LaunchGeom&, const CompactTables&,
+                                               const LaunchPhys&, hipStream_t);
+template hipError_t launch_io_compact<double>(int, int, double*, const LaunchGeom&, const CompactTables&,
+                                             const LaunchPhys&, double*, double*, const double*, const double*, hipStream_t);
 }  // namespace lbm

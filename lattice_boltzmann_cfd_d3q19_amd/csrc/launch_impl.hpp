@@ -4,6 +4,7 @@
 #include <cmath>
 
 #include "kernels.hpp"
+#include "kernels_compact.hpp"
 #include "launch.hpp"
 
 namespace lbm {
@@ -32,7 +33,6 @@ inline Shape make_shape(const LaunchGeom& lg)
     g.ntx = (g.nx + bx - 1) / bx;
     g.nty = (g.ny + by - 1) / by;
     g.ntiles = g.ntx * g.nty * g.nz;
-    g.xcd_remap = lg.xcd_remap ? 1u : 0u;
     g.n = (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz;
     g.mask = lg.mask;
     s.block = dim3(bx, by, 1);
@@ -149,6 +149,89 @@ hipError_t launch_io(int layout, int state, int op, T* a, T* b, const LaunchGeom
     case kStream: return launch_io_l<T, kStream>(state, op, a, b, s, p, o0, o1, i0, i1, st);
     case kBundle: return launch_io_l<T, kBundle>(state, op, a, b, s, p, o0, o1, i0, i1, st);
     case kCollision: return launch_io_l<T, kCollision>(state, op, a, b, s, p, o0, o1, i0, i1, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// ------------------------------------------------------------ compact
+
+inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
+{
+    CompactGeom g{};
+    g.idxp = t.idxp;
+    g.cellp = t.cellp;
+    g.nf = t.nf;
+    g.px = (uint32_t)lg.nx + 2;
+    g.pxy = (uint32_t)((lg.nx + 2) * (lg.ny + 2));
+    g.s = t.stride;
+    return g;
+}
+
+template <typename T, int K, bool FORCE>
+hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, hipStream_t st)
+{
+    if (g.nf == 0) return hipSuccess;
+    void* args[] = {&a, &b, &g, &p};
+    const dim3 grid((g.nf + kBlockThreads - 1) / kBlockThreads), block(kBlockThreads);
+    return hipLaunchKernel((const void*)&step_compact_kernel<T, K, FORCE>, grid, block, args, 0, st);
+}
+
+template <typename T, int K>
+hipError_t launch_step_compact_k(T* a, T* b, CompactGeom g, Phys<T> p, bool force, hipStream_t st)
+{
+    return force ? launch_step_compact_t<T, K, true>(a, b, g, p, st)
+                 : launch_step_compact_t<T, K, false>(a, b, g, p, st);
+}
+
+template <typename T>
+hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& lg, const CompactTables& t,
+                               const LaunchPhys& lp, hipStream_t st)
+{
+    const CompactGeom g = compact_geom(lg, t);
+    const Phys<T> p = make_phys<T>(lp);
+    switch (kind) {
+    case kAB: return launch_step_compact_k<T, kAB>(a, b, g, p, lp.has_force, st);
+    case kAAEven: return launch_step_compact_k<T, kAAEven>(a, b, g, p, lp.has_force, st);
+    case kAAOdd: return launch_step_compact_k<T, kAAOdd>(a, b, g, p, lp.has_force, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int S, int OP>
+hipError_t launch_io_compact_t(T* a, CompactGeom cg, const Shape& s, Phys<T> p, T* o0, T* o1, const T* i0,
+                               const T* i1, hipStream_t st)
+{
+    Geom g = s.g;
+    void* args[] = {&a, &cg, &g, &p, &o0, &o1, &i0, &i1};
+    return hipLaunchKernel((const void*)&io_compact_kernel<T, S, OP>, s.grid, s.block, args, 0, st);
+}
+
+template <typename T, int S>
+hipError_t launch_io_compact_s(int op, T* a, CompactGeom cg, const Shape& s, Phys<T> p, T* o0, T* o1,
+                               const T* i0, const T* i1, hipStream_t st)
+{
+    switch (op) {
+    case kReadF: return launch_io_compact_t<T, S, kReadF>(a, cg, s, p, o0, o1, i0, i1, st);
+    case kReadMoments: return launch_io_compact_t<T, S, kReadMoments>(a, cg, s, p, o0, o1, i0, i1, st);
+    case kWriteF: return launch_io_compact_t<T, S, kWriteF>(a, cg, s, p, o0, o1, i0, i1, st);
+    case kWriteEq: return launch_io_compact_t<T, S, kWriteEq>(a, cg, s, p, o0, o1, i0, i1, st);
+    case kReadS: return launch_io_compact_t<T, S, kReadS>(a, cg, s, p, o0, o1, i0, i1, st);
+    case kWriteS: return launch_io_compact_t<T, S, kWriteS>(a, cg, s, p, o0, o1, i0, i1, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_io_compact(int state, int op, T* a, const LaunchGeom& lg, const CompactTables& t,
+                             const LaunchPhys& lp, T* o0, T* o1, const T* i0, const T* i1, hipStream_t st)
+{
+    const Shape s = make_shape(lg);
+    const CompactGeom cg = compact_geom(lg, t);
+    const Phys<T> p = make_phys<T>(lp);
+    switch (state) {
+    case kAB: return launch_io_compact_s<T, kAB>(op, a, cg, s, p, o0, o1, i0, i1, st);
+    case kAAEven: return launch_io_compact_s<T, kAAEven>(op, a, cg, s, p, o0, o1, i0, i1, st);
+    case kAAOdd: return launch_io_compact_s<T, kAAOdd>(op, a, cg, s, p, o0, o1, i0, i1, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -9,7 +9,7 @@ from . import capi
 
 _PREC = {"f32": (capi.LBM_F32, torch.float32), "f64": (capi.LBM_F64, torch.float64)}
 _LAYOUT = {"stream": capi.LBM_LAYOUT_STREAM, "bundle": capi.LBM_LAYOUT_BUNDLE,
-           "collision": capi.LBM_LAYOUT_COLLISION}
+           "collision": capi.LBM_LAYOUT_COLLISION, "compact": capi.LBM_LAYOUT_COMPACT}
 _SCHEME = {"ab": capi.LBM_SCHEME_AB, "aa": capi.LBM_SCHEME_AA}
 
 Q = 19
@@ -18,8 +18,9 @@ Q = 19
 class Lattice:
     """One D3Q19 lattice on the GPU.
 
-    precision: "f32" | "f64"; layout: "stream" | "bundle" | "collision";
-    scheme: "ab" (two lattices, fused pull) | "aa" (one lattice, in place).
+    precision: "f32" | "f64"; layout: "stream" | "bundle" | "collision" |
+    "compact" (SoA over fluid cells only); scheme: "ab" (two lattices, fused
+    pull) | "aa" (one lattice, in place).
     """
 
     def __init__(self, nx, ny, nz, precision="f32", layout="stream", scheme="aa", tau=1.0,
@@ -40,6 +41,12 @@ class Lattice:
         st, self.handle = capi.lbm_create(self.desc, ptrs[0], ptrs[1], self.stream.cuda_stream)
         capi.check(st, "lbm_create")
         self.mask = None
+        st, wbytes = capi.lbm_workspace_bytes(self.desc)
+        capi.check(st, "lbm_workspace_bytes")
+        self.workspace = None
+        if wbytes:
+            self.workspace = torch.empty(wbytes, dtype=torch.uint8, device=self.device)
+            capi.check(capi.lbm_set_workspace(self.handle, self.workspace.data_ptr(), wbytes), "lbm_set_workspace")
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value is not None:
@@ -79,6 +86,11 @@ class Lattice:
     @property
     def t(self):
         return capi.lbm_time(self.handle)
+
+    @property
+    def fluid_cells(self):
+        """Fluid cells counted by the compact layout (-1 for dense layouts)."""
+        return capi.lbm_fluid_cells(self.handle)
 
     def moments(self):
         rho = torch.empty(self.n, dtype=self.dtype, device=self.device)

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-LAYOUTS = ("stream", "bundle", "collision")
+LAYOUTS = ("stream", "bundle", "collision", "compact")
 SCHEMES = ("ab", "aa")
 TOL = {"f32": 1e-5, "f64": 1e-12}
 

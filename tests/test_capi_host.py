@@ -59,7 +59,7 @@ def test_buffer_bytes_match_page_byte_model(golden_dir):
 
 
 @pytest.mark.parametrize("field,value", [
-    ("nx", 0), ("ny", -3), ("nz", 0), ("precision", 2), ("layout", 3), ("scheme", 5), ("reserved", 1),
+    ("nx", 0), ("ny", -3), ("nz", 0), ("precision", 2), ("layout", 4), ("scheme", 5), ("reserved", 1),
     ("tau", 0.5), ("tau", 0.2), ("tau", float("nan")), ("tau", -math.inf)])
 def test_invalid_desc_rejected(field, value):
     d = capi.make_desc(8, 8, 8)
@@ -130,3 +130,27 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     libs = {os.path.realpath(p) for p in re.findall(r"(/\S*libamdhip64\S*)", maps)}
     assert len(libs) == 1, libs
+
+
+def test_workspace_rules():
+    dense = capi.make_desc(10, 8, 6, layout=capi.LBM_LAYOUT_STREAM)
+    comp = capi.make_desc(10, 8, 6, layout=capi.LBM_LAYOUT_COMPACT)
+    st, wd = capi.lbm_workspace_bytes(dense)
+    assert st == capi.LBM_OK and wd == 0
+    st, wc = capi.lbm_workspace_bytes(comp)
+    # index table over the halo-padded box + one index per cell + row table
+    assert st == capi.LBM_OK and wc >= 4 * (12 * 10 * 8) + 4 * 480 + 4 * 48
+    st, nb, _ = capi.lbm_buffer_bytes(comp)
+    assert nb == 19 * 512 * 4          # room for an all-fluid box, rounded to 64 cells
+    st, h = capi.lbm_create(comp, FAKE)
+    assert st == capi.LBM_OK
+    try:
+        assert capi.lbm_fluid_cells(h) == -1
+        assert capi.lbm_init_equilibrium(h) == capi.LBM_ERR_BAD_STATE     # no workspace yet
+        assert capi.lbm_set_workspace(h, FAKE + 4, wc) == capi.LBM_ERR_MISALIGNED
+        assert capi.lbm_set_workspace(h, FAKE, wc - 1) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert capi.lbm_set_workspace(h, FAKE, wc) == capi.LBM_OK
+        assert capi.lbm_set_workspace(h, None, 0) == capi.LBM_OK
+        assert capi.lbm_init_equilibrium(h) == capi.LBM_ERR_BAD_STATE
+    finally:
+        capi.lbm_destroy(h)

@@ -192,10 +192,11 @@ def test_checkpoint_resume_bit_exact():
         half.step(5)
         snap = half.save_state().clone()
         pops = half.read_populations().clone()
-        resumed = make(shape, "f32", "bundle", scheme, tau=0.7, force=F, mask=mask)
-        resumed.load_state(snap)
-        resumed.step(5)
-        assert np.array_equal(host_f(resumed), want)
+        for other in ("bundle", "compact"):
+            resumed = make(shape, "f32", other, scheme, tau=0.7, force=F, mask=mask)
+            resumed.load_state(snap)
+            resumed.step(5)
+            assert np.array_equal(host_f(resumed), want), other
         approx = make(shape, "f32", "collision", scheme, tau=0.7, force=F, mask=mask)
         approx.write_populations(pops)
         approx.step(5)
@@ -234,6 +235,8 @@ def _full_size(name):
 @pytest.mark.parametrize("name,layout,scheme", [
     ("tgv128", "stream", "aa"), ("tgv128", "stream", "ab"),
     ("sphere128", "stream", "aa"), ("sphere128", "bundle", "aa"), ("sphere128", "collision", "aa"),
+    ("sphere128", "compact", "aa"), ("channel_f64", "compact", "ab"), ("porous256", "compact", "aa"),
+    ("porous256", "compact", "ab"),
     ("channel_f64", "stream", "aa"), ("channel_f64", "stream", "ab"),
     ("porous256", "stream", "aa"), ("porous256", "stream", "ab")])
 def test_full_size_sampled_steps(name, layout, scheme):
@@ -259,3 +262,47 @@ def test_full_size_sampled_steps(name, layout, scheme):
         assert err <= (1e-6 if prec == "f32" else 1e-14)
         prev = cur
     del prev, cur
+
+
+# --------------------------------------------- compact layout index tables
+
+@pytest.mark.parametrize("periodic", [(1, 1, 1), (0, 1, 0), (1, 0, 1)])
+def test_compact_tables_bit_exact(periodic):
+    """The device-built tables of the compact layout equal a numpy construction:
+    fluid cells ranked in cell order; halo cells hold their periodic image or
+    the invalid marker beyond a wall."""
+    need_gpu()
+    import torch
+    shape = (37, 21, 13)
+    nx, ny, nz = shape
+    mask = li.random_mask(*shape, fraction=0.3, seed=17)
+    lat = make(shape, "f32", "compact", "aa", tau=0.7, mask=mask, periodic=periodic)
+    torch.cuda.synchronize()
+    fluid = mask == 0
+    nf = int(fluid.sum())
+    assert lat.fluid_cells == nf
+    rank = np.full(mask.size, 0xFFFFFFFF, np.uint64)
+    rank[fluid] = np.arange(nf)
+    px, py, pz = nx + 2, ny + 2, nz + 2
+    gz, gy, gx = np.meshgrid(np.arange(pz) - 1, np.arange(py) - 1, np.arange(px) - 1, indexing="ij")
+    ok = np.ones(gx.shape, bool)
+    coords = []
+    for g, n, per in ((gx, nx, periodic[0]), (gy, ny, periodic[1]), (gz, nz, periodic[2])):
+        out = (g < 0) | (g >= n)
+        if not per:
+            ok &= ~out
+        coords.append(np.mod(g, n))
+    cell = coords[0] + nx * (coords[1] + ny * coords[2])
+    want_idxp = np.where(ok, rank[cell], 0xFFFFFFFF).astype(np.uint32).reshape(-1)
+    ws = lat.workspace.cpu().numpy().view(np.uint32)
+    # header (256 B), then the row table, then idxp, then cellp (256-B aligned)
+    rows_words = ((4 * ny * nz + 255) // 256 * 256) // 4
+    off = 256 // 4 + rows_words
+    got_idxp = ws[off:off + want_idxp.size]
+    assert np.array_equal(got_idxp, want_idxp)
+    cell_off = off + ((4 * want_idxp.size + 255) // 256 * 256) // 4
+    pid = np.nonzero(want_idxp.reshape(pz, py, px)[1:-1, 1:-1, 1:-1].reshape(-1) != 0xFFFFFFFF)[0]
+    zz, rem = np.divmod(pid, nx * ny)
+    yy, xx = np.divmod(rem, nx)
+    want_cellp = ((xx + 1) + px * (yy + 1) + px * py * (zz + 1)).astype(np.uint32)
+    assert np.array_equal(ws[cell_off:cell_off + nf], want_cellp)

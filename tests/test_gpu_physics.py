@@ -118,7 +118,7 @@ def test_sphere_128_all_layouts_2000_steps():
     need_gpu()
     mask = li.sphere_mask(128, radius=16)
     states = {}
-    for layout in ("stream", "bundle", "collision"):
+    for layout in ("stream", "bundle", "collision", "compact"):
         lat = make((128,) * 3, "f32", layout, "aa", tau=0.7, force=(1e-6, 0.0, 0.0), mask=mask)
         m0 = _mass(lat)
         lat.step(2000)
@@ -130,7 +130,8 @@ def test_sphere_128_all_layouts_2000_steps():
         _, u = host_moments(lat)
         say("sphere", layout, "mean u_x", u[0].mean())
         assert u[0].mean() > 0
-    assert torch.equal(states["stream"], states["bundle"]) and torch.equal(states["stream"], states["collision"])
+    for layout in ("bundle", "collision", "compact"):
+        assert torch.equal(states["stream"], states[layout]), layout
 
 
 def test_porous_256_schemes_agree_1000_steps():
@@ -138,14 +139,15 @@ def test_porous_256_schemes_agree_1000_steps():
     need_gpu()
     mask, _ = li.porous_mask(256)
     out = {}
-    for scheme in ("aa", "ab"):
-        lat = make((256,) * 3, "f32", "stream", scheme, tau=0.65, force=(1e-6, 0.0, 0.0), mask=mask)
+    for scheme, layout in (("aa", "stream"), ("ab", "stream"), ("aa", "compact")):
+        lat = make((256,) * 3, "f32", layout, scheme, tau=0.65, force=(1e-6, 0.0, 0.0), mask=mask)
         m0 = _mass(lat)
         lat.step(1000)
         m1 = _mass(lat)
-        say("porous", scheme, "mass drift", (m1 - m0) / m0)
+        say("porous", scheme, layout, "mass drift", (m1 - m0) / m0)
         assert abs(m1 - m0) / m0 <= 1e-6
-        out[scheme] = lat.read_populations().cpu()
+        out[(scheme, layout)] = lat.read_populations().cpu()
         del lat
         torch.cuda.empty_cache()
-    assert torch.equal(out["aa"], out["ab"])
+    assert torch.equal(out[("aa", "stream")], out[("ab", "stream")])
+    assert torch.equal(out[("aa", "stream")], out[("aa", "compact")])
