@@ -176,33 +176,21 @@ __device__ __forceinline__ uint32_t link_bits(const Geom& g, const Cell& c)
 
 // ------------------------------------------------------------- collision
 
-// Weights in T whose exact sum is 1, so that collision conserves mass up to
-// unbiased rounding.  Rounding 1/3, 1/18 and 1/36 to fp32 independently leaves
-// a sum of 1 + 1.5e-8, and relaxation then gains that fraction of the mass in
-// every cell at every step (a measurable drift: 1e-6 of the mass within 50
-// steps at omega = 1/0.6).  Instead w36 is an fp32 value with an even
-// significand (14913080 * 2^-29, 3.3e-8 below 1/36), w18 = 2 w36 and
-// w0 = 1 - 24 w36; all three are exact floats summing exactly to 1.  In fp64,
-// 1 - 24 fl(1/36) is itself exact.
+// Lattice weights, each correctly rounded to T.  No set of fp32 weights can
+// make both sum_q w_q = 1 and 3 sum_q w_q c_q c_q = 1 exact, so conservation is
+// secured another way: storage is shifted (s = f - w, below), which turns the
+// mass error of the weight sum into drho * (sum w - 1), and the equilibrium's
+// odd part is built so that its first moment is rho u exactly (odd_parts).
+// An earlier choice, weights nudged to sum exactly to 1, left 36 w36 = 1 -
+// 6e-8 and so removed omega * 6e-8 of the momentum in every collision (the
+// 128^3 Taylor-Green energy then fell 2e-5 below the fp64 result per 100
+// steps).
 template <typename T>
-struct Weights;
-
-template <>
-struct Weights<float> {
-    static constexpr float w36 = 14913080.0f / 536870912.0f;
-    static constexpr float w18 = 2.0f * w36;
-    static constexpr float w0 = 1.0f - 24.0f * w36;
+struct Weights {
+    static constexpr T w36 = T(1) / T(36);
+    static constexpr T w18 = T(1) / T(18);
+    static constexpr T w0 = T(1) / T(3);
 };
-
-template <>
-struct Weights<double> {
-    static constexpr double w36 = 1.0 / 36.0;
-    static constexpr double w18 = 2.0 * w36;
-    static constexpr double w0 = 1.0 - 24.0 * w36;
-};
-
-static_assert(Weights<float>::w0 + 6.0f * Weights<float>::w18 == 1.0f - 12.0f * Weights<float>::w36,
-              "fp32 weights do not sum to one");
 
 template <typename T>
 __device__ __forceinline__ T wq(int q)
@@ -246,10 +234,12 @@ __device__ __forceinline__ void moments(const T (&s)[kQ], const Phys<T>& p, T& d
         jy = jy + p.hfy;
         jz = jz + p.hfz;
     }
-    const T inv = T(1) / rho;
-    ux = jx * inv;
-    uy = jy * inv;
-    uz = jz * inv;
+    // three correctly rounded divisions: j * (1 / rho) rounds twice and, in
+    // fp32, biases the velocity enough to lift the 128^3 Taylor-Green energy
+    // by 1e-8 per step against the fp64 result; j / rho removes that drift
+    ux = jx / rho;
+    uy = jy / rho;
+    uz = jz / rho;
 }
 
 template <int q, typename T>
@@ -265,17 +255,47 @@ __device__ __forceinline__ T cdot(T ax, T ay, T az)
     return r;
 }
 
-// Shifted equilibrium of directions q and opposite(q), feq - w, from its parts
-// even and odd under c -> -c:  w (drho + rho (9/2 (c.u)^2 - 3/2 u^2)) +- w rho 3 (c.u).
+constexpr bool is_diagonal(int q) { return sq(kCx[q]) + sq(kCy[q]) + sq(kCz[q]) == 2; }
+
+// Odd parts o_q (s_q gets +o_q, s_opp(q) gets -o_q) of the shifted equilibrium
+// for the nine pairs q < 9.  Diagonal pairs: w rho 3 (c.u).  Axis pairs (q = 8,
+// 6, 2, along -x, -y, -z): whatever makes sum_q c_q feq_q = rho u hold in T up
+// to unbiased rounding, rho u_a / 2 minus the diagonal pairs' share; with exact
+// weights this equals w18 rho 3 (c.u), the textbook value.
+template <typename T>
+__device__ __forceinline__ void odd_parts(T rho, T ux, T uy, T uz, T (&o)[9])
+{
+    T sx = T(0), sy = T(0), sz = T(0);
+#pragma unroll
+    for (int q = 0; q < 9; ++q) {
+        if (!is_diagonal(q)) continue;
+        T cu = T(0);
+        if (kCx[q] > 0) cu = cu + ux;
+        if (kCx[q] < 0) cu = cu - ux;
+        if (kCy[q] > 0) cu = cu + uy;
+        if (kCy[q] < 0) cu = cu - uy;
+        if (kCz[q] > 0) cu = cu + uz;
+        if (kCz[q] < 0) cu = cu - uz;
+        o[q] = Weights<T>::w36 * (rho * (T(3) * cu));
+        if (kCx[q] > 0) sx = sx + o[q];
+        if (kCx[q] < 0) sx = sx - o[q];
+        if (kCy[q] > 0) sy = sy + o[q];
+        if (kCy[q] < 0) sy = sy - o[q];
+        if (kCz[q] > 0) sz = sz + o[q];
+        if (kCz[q] < 0) sz = sz - o[q];
+    }
+    static_assert(kCx[8] == -1 && kCy[6] == -1 && kCz[2] == -1, "axis pairs are q = 8, 6, 2");
+    o[8] = -(T(0.5) * rho * ux - sx);
+    o[6] = -(T(0.5) * rho * uy - sy);
+    o[2] = -(T(0.5) * rho * uz - sz);
+}
+
+// Even part of the shifted equilibrium of pair q: w (drho + rho (9/2 (c.u)^2 - 3/2 u^2)).
 template <int q, typename T>
-__device__ __forceinline__ void seq_pair(T drho, T rho, T ux, T uy, T uz, T k15, T& eq, T& eo)
+__device__ __forceinline__ T even_part(T drho, T rho, T ux, T uy, T uz, T k15)
 {
     const T cu = cdot<q>(ux, uy, uz);
-    const T w = wq<T>(q);
-    const T even = w * (drho + rho * (T(4.5) * cu * cu - k15));
-    const T odd = w * (rho * (T(3) * cu));
-    eq = even + odd;
-    eo = even - odd;
+    return wq<T>(q) * (drho + rho * (T(4.5) * cu * cu - k15));
 }
 
 template <typename T>
@@ -286,23 +306,22 @@ __device__ __forceinline__ T k15_of(T ux, T uy, T uz)
 
 template <int q, typename T, bool FORCE>
 __device__ __forceinline__ void relax_pair(T (&s)[kQ], const Phys<T>& p, T drho, T rho, T ux, T uy, T uz, T k15,
-                                           T uF)
+                                           T uF, T odd)
 {
     constexpr int o = opp(q);
-    T eq, eo;
-    seq_pair<q>(drho, rho, ux, uy, uz, k15, eq, eo);
-    T nq = fma(p.omega, eq - s[q], s[q]);
-    T no = fma(p.omega, eo - s[o], s[o]);
+    const T even = even_part<q>(drho, rho, ux, uy, uz, k15);
+    T nq = fma(p.omega, (even + odd) - s[q], s[q]);
+    T no = fma(p.omega, (even - odd) - s[o], s[o]);
     if constexpr (FORCE) {
         // Guo term: (1 - omega/2) w [3 (c - u) + 9 (c.u) c] . F, split into the
         // parts even and odd under c -> -c.
         const T cu = cdot<q>(ux, uy, uz);
         const T cF = cdot<q>(p.fx, p.fy, p.fz);
         const T gw = p.guo * wq<T>(q);
-        const T even = gw * (T(9) * cu * cF - T(3) * uF);
-        const T odd = gw * (T(3) * cF);
-        nq = nq + (even + odd);
-        no = no + (even - odd);
+        const T geven = gw * (T(9) * cu * cF - T(3) * uF);
+        const T godd = gw * (T(3) * cF);
+        nq = nq + (geven + godd);
+        no = no + (geven - godd);
     }
     s[q] = nq;
     s[o] = no;
@@ -317,15 +336,17 @@ __device__ __forceinline__ void collide(T (&s)[kQ], const Phys<T>& p)
     const T k15 = k15_of(ux, uy, uz);
     T uF = T(0);
     if constexpr (FORCE) uF = ux * p.fx + uy * p.fy + uz * p.fz;
-    relax_pair<0, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF);
-    relax_pair<1, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF);
-    relax_pair<2, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF);
-    relax_pair<3, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF);
-    relax_pair<4, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF);
-    relax_pair<5, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF);
-    relax_pair<6, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF);
-    relax_pair<7, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF);
-    relax_pair<8, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF);
+    T od[9];
+    odd_parts(rho, ux, uy, uz, od);
+    relax_pair<0, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[0]);
+    relax_pair<1, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[1]);
+    relax_pair<2, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[2]);
+    relax_pair<3, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[3]);
+    relax_pair<4, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[4]);
+    relax_pair<5, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[5]);
+    relax_pair<6, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[6]);
+    relax_pair<7, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[7]);
+    relax_pair<8, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[8]);
     // rest population: shifted equilibrium w0 (drho - rho 3/2 u^2)
     const T e9 = wq<T>(9) * (drho - rho * k15);
     T n9 = fma(p.omega, e9 - s[9], s[9]);
@@ -333,21 +354,31 @@ __device__ __forceinline__ void collide(T (&s)[kQ], const Phys<T>& p)
     s[9] = n9;
 }
 
-// Shifted equilibrium populations of (rho, u): s_q = feq_q(rho, u) - w_q.
+// Shifted equilibrium populations of (rho, u): s_q = feq_q(rho, u) - w_q, built
+// exactly as in the collision.
 template <typename T>
 __device__ __forceinline__ void shifted_equilibrium(T rho, T ux, T uy, T uz, T (&s)[kQ])
 {
     const T drho = rho - T(1);
     const T k15 = k15_of(ux, uy, uz);
-    seq_pair<0>(drho, rho, ux, uy, uz, k15, s[0], s[18]);
-    seq_pair<1>(drho, rho, ux, uy, uz, k15, s[1], s[17]);
-    seq_pair<2>(drho, rho, ux, uy, uz, k15, s[2], s[16]);
-    seq_pair<3>(drho, rho, ux, uy, uz, k15, s[3], s[15]);
-    seq_pair<4>(drho, rho, ux, uy, uz, k15, s[4], s[14]);
-    seq_pair<5>(drho, rho, ux, uy, uz, k15, s[5], s[13]);
-    seq_pair<6>(drho, rho, ux, uy, uz, k15, s[6], s[12]);
-    seq_pair<7>(drho, rho, ux, uy, uz, k15, s[7], s[11]);
-    seq_pair<8>(drho, rho, ux, uy, uz, k15, s[8], s[10]);
+    T od[9];
+    odd_parts(rho, ux, uy, uz, od);
+#define LBM_SEQ_PAIR(q)                                                      \
+    {                                                                        \
+        const T e = even_part<q>(drho, rho, ux, uy, uz, k15);                \
+        s[q] = e + od[q];                                                    \
+        s[opp(q)] = e - od[q];                                               \
+    }
+    LBM_SEQ_PAIR(0)
+    LBM_SEQ_PAIR(1)
+    LBM_SEQ_PAIR(2)
+    LBM_SEQ_PAIR(3)
+    LBM_SEQ_PAIR(4)
+    LBM_SEQ_PAIR(5)
+    LBM_SEQ_PAIR(6)
+    LBM_SEQ_PAIR(7)
+    LBM_SEQ_PAIR(8)
+#undef LBM_SEQ_PAIR
     s[9] = wq<T>(9) * (drho - rho * k15);
 }
 

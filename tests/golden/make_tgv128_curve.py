@@ -27,7 +27,7 @@ def main():
         if t:
             f = oracle.run(box, f, 50)
         tot = oracle.totals(box, f)
-        rows.append((t, tot["ke"], tot["mass"]))
+        rows.append((t, float(tot["ke"]), float(tot["mass"])))
         print(t, tot["ke"], tot["mass"], flush=True)
     with open(os.path.join(HERE, "tgv128_ke_curve.txt"), "w") as fh:
         fh.write("# 3-D Taylor-Green vortex, 128^3 periodic, u0 = 0.04, rho = 1 + 3 p', tau = 0.6,\n")
