@@ -28,9 +28,15 @@
  *                         inside a bundle.
  *   LBM_LAYOUT_COLLISION  AoS: the 19 populations of a cell are contiguous.
  *   LBM_LAYOUT_COMPACT    SoA over fluid cells only: population q of the i-th
- *                         fluid cell (in cell order) at q * S + i.  Needs a
- *                         workspace (lbm_set_workspace) for its neighbour
+ *                         fluid cell (in cell order) at P(q) * S + i, S = the
+ *                         fluid count rounded up to 64, with the planes of
+ *                         opposite directions side by side: P(q) = 2q for
+ *                         q < 9, 2(18 - q) + 1 for q > 9, P(9) = 18.  Needs
+ *                         a workspace (lbm_set_workspace) for its neighbour
  *                         tables; in porous media it moves only fluid bytes.
+ *                         Limits (else LBM_ERR_UNSUPPORTED): 4 (nx+2)(ny+2)
+ *                         (nz+2) < 2^32 and 2 * 64-rounded N * sizeof(T) <
+ *                         2^32 (32-bit byte offsets inside the kernels).
  *
  * Conventions shared by every entry point:
  *  - Cell index: cell = x + nx * (y + ny * z), N = nx * ny * nz.

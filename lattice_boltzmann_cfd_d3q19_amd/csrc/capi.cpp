@@ -46,6 +46,8 @@ constexpr uintptr_t kAlign = 256;
 
 bool compact(const lbm_desc& d) { return d.layout == LBM_LAYOUT_COMPACT; }
 
+uint64_t ncells_of(const lbm_desc& d) { return (uint64_t)d.nx * (uint64_t)d.ny * (uint64_t)d.nz; }
+
 lbm_status validate_desc(const lbm_desc* d)
 {
     if (d == nullptr) return LBM_ERR_INVALID_ARGUMENT;
@@ -64,7 +66,12 @@ lbm_status validate_desc(const lbm_desc* d)
     const double n = (double)d->nx * (double)d->ny * (double)d->nz;
     if (d->nx > INT32_MAX || d->ny > INT32_MAX || d->nz > INT32_MAX || n >= 2147483648.0)
         return LBM_ERR_UNSUPPORTED;
-    if (compact(*d) && (double)(d->nx + 2) * (double)(d->ny + 2) * (double)(d->nz + 2) >= 4294967295.0)
+    // the compact kernels address the padded index table and each two-plane
+    // block of populations with 32-bit byte offsets
+    if (compact(*d) && 4.0 * (double)(d->nx + 2) * (double)(d->ny + 2) * (double)(d->nz + 2) >= 4294967296.0)
+        return LBM_ERR_UNSUPPORTED;
+    if (compact(*d) && 2.0 * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)((ncells_of(*d) + 63) / 64 * 64) >=
+                           4294967296.0)
         return LBM_ERR_UNSUPPORTED;
     return LBM_OK;
 }

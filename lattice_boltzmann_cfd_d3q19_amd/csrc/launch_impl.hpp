@@ -163,7 +163,7 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     g.nf = t.nf;
     g.px = (uint32_t)lg.nx + 2;
     g.pxy = (uint32_t)((lg.nx + 2) * (lg.ny + 2));
-    g.s = t.stride;
+    g.s = (uint32_t)t.stride;
     return g;
 }
 
@@ -176,11 +176,25 @@ hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, hipStream
     return hipLaunchKernel((const void*)&step_compact_kernel<T, K, FORCE>, grid, block, args, 0, st);
 }
 
+template <typename T, bool FORCE>
+hipError_t launch_even_compact_t(T* a, CompactGeom g, Phys<T> p, hipStream_t st)
+{
+    if (g.nf == 0) return hipSuccess;
+    uint32_t s = g.s;
+    void* args[] = {&a, &s, &p};
+    const dim3 grid((s + kBlockThreads - 1) / kBlockThreads), block(kBlockThreads);
+    return hipLaunchKernel((const void*)&even_compact_kernel<T, FORCE>, grid, block, args, 0, st);
+}
+
 template <typename T, int K>
 hipError_t launch_step_compact_k(T* a, T* b, CompactGeom g, Phys<T> p, bool force, hipStream_t st)
 {
-    return force ? launch_step_compact_t<T, K, true>(a, b, g, p, st)
-                 : launch_step_compact_t<T, K, false>(a, b, g, p, st);
+    if constexpr (K == kAAEven) {
+        return force ? launch_even_compact_t<T, true>(a, g, p, st) : launch_even_compact_t<T, false>(a, g, p, st);
+    } else {
+        return force ? launch_step_compact_t<T, K, true>(a, b, g, p, st)
+                     : launch_step_compact_t<T, K, false>(a, b, g, p, st);
+    }
 }
 
 template <typename T>

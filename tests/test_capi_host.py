@@ -79,6 +79,19 @@ def test_too_many_cells_unsupported():
     assert capi.lbm_buffer_bytes(d)[0] == capi.LBM_ERR_UNSUPPORTED
 
 
+def test_compact_offset_limits():
+    # the compact kernels address one two-plane block with a 32-bit byte
+    # offset: 2 * roundup(N, 64) * sizeof(T) < 2^32
+    big = dict(layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_AA)
+    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F32, **big))[0] == capi.LBM_OK
+    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F64, **big))[0] == capi.LBM_ERR_UNSUPPORTED
+    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 255, capi.LBM_F64, **big))[0] == capi.LBM_OK
+    # the same box in a dense layout is fine
+    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F64))[0] == capi.LBM_OK
+    # the padded neighbour table: 4 (nx+2)(ny+2)(nz+2) < 2^32 (and N < 2^31)
+    assert capi.lbm_buffer_bytes(capi.make_desc(1022, 1022, 1022, capi.LBM_F32, **big))[0] == capi.LBM_ERR_UNSUPPORTED
+
+
 def test_buffer_rules():
     aa = capi.make_desc(8, 8, 8, scheme=capi.LBM_SCHEME_AA)
     ab = capi.make_desc(8, 8, 8, scheme=capi.LBM_SCHEME_AB)
