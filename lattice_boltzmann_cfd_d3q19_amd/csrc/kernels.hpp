@@ -53,18 +53,27 @@ enum IoOp : int { kReadF = 0, kReadMoments = 1, kWriteF = 2, kWriteEq = 3, kRead
 
 // ---------------------------------------------------------------- layout
 
+// Element offset of population q of `cell` in a buffer of the given layout.
+// q is a compile-time constant at every call, so the direction's part is
+// uniform (scalar) and the per-lane part is one 64-bit add.
+template <int L>
+__device__ __forceinline__ uint64_t slot_off(uint64_t n, int q, uint32_t cell)
+{
+    if constexpr (L == kStream) {
+        return (uint64_t)q * n + cell;
+    } else if constexpr (L == kBundle) {
+        return (uint64_t)kBundleFirst[q] * n + (uint64_t)cell * (uint32_t)kBundleSize[q] +
+               (uint32_t)(q - kBundleFirst[q]);
+    } else {
+        return (uint64_t)cell * (uint32_t)kQ + (uint32_t)q;
+    }
+}
+
 // Address of population q of `cell` in a buffer of the given layout.
 template <int L, typename T>
 __device__ __forceinline__ T* slot(T* base, uint64_t n, int q, uint32_t cell)
 {
-    if constexpr (L == kStream) {
-        return base + (uint64_t)q * n + cell;
-    } else if constexpr (L == kBundle) {
-        return base + (uint64_t)kBundleFirst[q] * n + (uint64_t)cell * (uint32_t)kBundleSize[q] +
-               (uint32_t)(q - kBundleFirst[q]);
-    } else {
-        return base + (uint64_t)cell * (uint32_t)kQ + (uint32_t)q;
-    }
+    return base + slot_off<L>(n, q, cell);
 }
 
 // ------------------------------------------------------- memory access
@@ -157,19 +166,26 @@ __device__ __forceinline__ bool beyond_wall(const Cell& c, int dx, int dy, int d
 
 // Bit q set iff the upstream cell x - c_q is solid or beyond a wall, i.e. the
 // population arriving along c_q is the bounced-back one.
+// The wrapped neighbour index is inside the box even where a wall cuts the
+// link, so its mask byte is read unconditionally (one uniform test for the
+// mask pointer, no per-lane branch around the 18 loads).
 template <bool BND>
 __device__ __forceinline__ uint32_t link_bits(const Geom& g, const Cell& c)
 {
     uint32_t bits = 0;
     if constexpr (BND) {
+        if (g.mask != nullptr) {
+            uint8_t m[kQ];
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-            if (q == 9) continue;
-            const int dx = -kCx[q], dy = -kCy[q], dz = -kCz[q];
-            bool solid = beyond_wall(c, dx, dy, dz);
-            if (!solid && g.mask != nullptr) solid = g.mask[nbr(c, dx, dy, dz)] != 0;
-            bits |= (uint32_t)solid << q;
+            for (int q = 0; q < kQ; ++q)
+                if (q != 9) m[q] = g.mask[nbr(c, -kCx[q], -kCy[q], -kCz[q])];
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+                if (q != 9) bits |= (uint32_t)(m[q] != 0) << q;
         }
+#pragma unroll
+        for (int q = 0; q < kQ; ++q)
+            if (q != 9) bits |= (uint32_t)beyond_wall(c, -kCx[q], -kCy[q], -kCz[q]) << q;
     }
     return bits;
 }
@@ -388,17 +404,22 @@ __device__ __forceinline__ void shifted_equilibrium(T rho, T ux, T uy, T uz, T (
 // (kAB: the source lattice holds h(t) with f(t) = stream(h(t)); kAAEven: the
 // lattice holds f(t) in natural slots; kAAOdd: it holds the post-collision
 // values of step t-1 in swapped slots).  This is the gather half of a step.
+// Both candidate offsets are formed and one is selected (v_cndmask): the
+// arms are a uniform plane offset plus a per-lane add, cheap enough that the
+// select is not turned into a divergent branch around the load.
 template <int S, int L, typename T>
 __device__ __forceinline__ T* state_slot(T* buf, uint64_t n, const Cell& c, uint32_t bits, int q)
 {
     const bool bb = (bits >> q) & 1u;
     const uint32_t up = nbr(c, -kCx[q], -kCy[q], -kCz[q]);
     if constexpr (S == kAB) {
-        return bb ? slot<L>(buf, n, opp(q), c.id) : slot<L>(buf, n, q, up);
+        const uint64_t own = slot_off<L>(n, opp(q), c.id), far = slot_off<L>(n, q, up);
+        return buf + (bb ? own : far);
     } else if constexpr (S == kAAEven) {
         return slot<L>(buf, n, q, c.id);
     } else {
-        return bb ? slot<L>(buf, n, q, c.id) : slot<L>(buf, n, opp(q), up);
+        const uint64_t own = slot_off<L>(n, q, c.id), far = slot_off<L>(n, opp(q), up);
+        return buf + (bb ? own : far);
     }
 }
 
@@ -444,9 +465,9 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
             // toward x + c_q, or straight back into (opp q, x) if that cell is
             // solid or beyond a wall (its upstream bit for opp q is set)
             const bool bb = (bits >> opp(q)) & 1u;
-            T* dst = bb ? slot<L>(a, n, opp(q), c.id)
-                        : slot<L>(a, n, q, nbr(c, kCx[q], kCy[q], kCz[q]));
-            st_pop(dst, f[q]);
+            const uint64_t own = slot_off<L>(n, opp(q), c.id);
+            const uint64_t far = slot_off<L>(n, q, nbr(c, kCx[q], kCy[q], kCz[q]));
+            st_pop(a + (bb ? own : far), f[q]);
         }
     }
 }
