@@ -39,12 +39,19 @@ struct Geom {
     const uint8_t* mask;           // uint8[n], nonzero = solid; may be null
 };
 
+// Relaxation and forcing constants, computed once on the host in double and
+// rounded to T.  The Guo term (1 - omega/2) w_q [3 (c_q - u) + 9 (c_q.u) c_q].F
+// of a pair (q, opp q), q < 9, splits into an even part
+// gev[q] (c_q.u) - gu[class] (u.F) and an odd part god[q] (+ for q, - for
+// opp q), with gev[q] = 9 (1 - omega/2) w_q (c_q.F), god[q] = 3 (1 - omega/2)
+// w_q (c_q.F) and gu = 3 (1 - omega/2) w for the rest / axis / diagonal class.
 template <typename T>
 struct Phys {
     T omega;  // 1 / tau (0 for tau = inf)
-    T guo;    // 1 - omega / 2
     T fx, fy, fz;
     T hfx, hfy, hfz;  // F / 2
+    T gev[9], god[9];
+    T gu[3];  // [0] rest, [1] axis (w = 1/18), [2] diagonal (w = 1/36)
 };
 
 // State transfers: canonical populations f out / in, moments out, equilibrium
@@ -224,6 +231,25 @@ __device__ __forceinline__ T wq(int q)
 // s*_q = s_q + omega (feq_q - w_q - s_q) + F_q.  Streaming moves s exactly as
 // it would move f (w_q = w_opposite(q)).
 
+// 1 / b for fp32: the hardware reciprocal (within 1 ulp) refined by one
+// Newton step, r + r (1 - b r), which leaves it within about half an ulp.
+__device__ __forceinline__ float recip_nr(float b)
+{
+    const float r = __builtin_amdgcn_rcpf(b);
+    return fmaf(fmaf(-b, r, 1.0f), r, r);
+}
+
+// a / b from r ~ 1 / b: q0 = a r is within an ulp or so, the residual
+// a - b q0 is exact in one fma, and q0 + r (a - b q0) rounds to the
+// correctly rounded quotient except when 1/b itself sits almost exactly
+// between two floats (Markstein's correction; b is the density, of order 1,
+// so no scaling is needed).
+__device__ __forceinline__ float quotient_rn(float a, float b, float r)
+{
+    const float q0 = a * r;
+    return fmaf(fmaf(-b, q0, a), r, q0);
+}
+
 // drho = sum_q s_q (q order), rho = 1 + drho, j = sum_q c_q s_q,
 // u = (j + F/2) / rho.
 template <typename T, bool FORCE>
@@ -250,12 +276,21 @@ __device__ __forceinline__ void moments(const T (&s)[kQ], const Phys<T>& p, T& d
         jy = jy + p.hfy;
         jz = jz + p.hfz;
     }
-    // three correctly rounded divisions: j * (1 / rho) rounds twice and, in
-    // fp32, biases the velocity enough to lift the 128^3 Taylor-Green energy
-    // by 1e-8 per step against the fp64 result; j / rho removes that drift
-    ux = jx / rho;
-    uy = jy / rho;
-    uz = jz / rho;
+    // u = j / rho.  j * (1 / rho) rounds twice and, in fp32, biases the
+    // velocity enough to lift the 128^3 Taylor-Green energy by 1e-8 per step
+    // against the fp64 result; the quotient must be (nearly) correctly
+    // rounded.  fp64 divides; fp32 takes one reciprocal per cell and corrects
+    // each quotient with its exact residual (quotient_rn below).
+    if constexpr (sizeof(T) == 4) {
+        const T r = recip_nr(rho);
+        ux = quotient_rn(jx, rho, r);
+        uy = quotient_rn(jy, rho, r);
+        uz = quotient_rn(jz, rho, r);
+    } else {
+        ux = jx / rho;
+        uy = jy / rho;
+        uz = jz / rho;
+    }
 }
 
 template <int q, typename T>
@@ -322,22 +357,17 @@ __device__ __forceinline__ T k15_of(T ux, T uy, T uz)
 
 template <int q, typename T, bool FORCE>
 __device__ __forceinline__ void relax_pair(T (&s)[kQ], const Phys<T>& p, T drho, T rho, T ux, T uy, T uz, T k15,
-                                           T uF, T odd)
+                                           T guF, T odd)
 {
     constexpr int o = opp(q);
     const T even = even_part<q>(drho, rho, ux, uy, uz, k15);
     T nq = fma(p.omega, (even + odd) - s[q], s[q]);
     T no = fma(p.omega, (even - odd) - s[o], s[o]);
     if constexpr (FORCE) {
-        // Guo term: (1 - omega/2) w [3 (c - u) + 9 (c.u) c] . F, split into the
-        // parts even and odd under c -> -c.
-        const T cu = cdot<q>(ux, uy, uz);
-        const T cF = cdot<q>(p.fx, p.fy, p.fz);
-        const T gw = p.guo * wq<T>(q);
-        const T geven = gw * (T(9) * cu * cF - T(3) * uF);
-        const T godd = gw * (T(3) * cF);
-        nq = nq + (geven + godd);
-        no = no + (geven - godd);
+        // Guo term of the pair, even part then odd part (constants in Phys)
+        const T geven = p.gev[q] * cdot<q>(ux, uy, uz) - guF;
+        nq = nq + (geven + p.god[q]);
+        no = no + (geven - p.god[q]);
     }
     s[q] = nq;
     s[o] = no;
@@ -350,23 +380,30 @@ __device__ __forceinline__ void collide(T (&s)[kQ], const Phys<T>& p)
     T drho, rho, ux, uy, uz;
     moments<T, FORCE>(s, p, drho, rho, ux, uy, uz);
     const T k15 = k15_of(ux, uy, uz);
-    T uF = T(0);
-    if constexpr (FORCE) uF = ux * p.fx + uy * p.fy + uz * p.fz;
+    T uF = T(0), guF0 = T(0), guF18 = T(0), guF36 = T(0);
+    if constexpr (FORCE) {
+        uF = ux * p.fx + uy * p.fy + uz * p.fz;
+        guF0 = p.gu[0] * uF;
+        guF18 = p.gu[1] * uF;
+        guF36 = p.gu[2] * uF;
+    }
     T od[9];
     odd_parts(rho, ux, uy, uz, od);
-    relax_pair<0, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[0]);
-    relax_pair<1, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[1]);
-    relax_pair<2, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[2]);
-    relax_pair<3, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[3]);
-    relax_pair<4, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[4]);
-    relax_pair<5, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[5]);
-    relax_pair<6, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[6]);
-    relax_pair<7, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[7]);
-    relax_pair<8, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, uF, od[8]);
+#define LBM_RELAX(q) relax_pair<q, T, FORCE>(s, p, drho, rho, ux, uy, uz, k15, is_diagonal(q) ? guF36 : guF18, od[q])
+    LBM_RELAX(0);
+    LBM_RELAX(1);
+    LBM_RELAX(2);
+    LBM_RELAX(3);
+    LBM_RELAX(4);
+    LBM_RELAX(5);
+    LBM_RELAX(6);
+    LBM_RELAX(7);
+    LBM_RELAX(8);
+#undef LBM_RELAX
     // rest population: shifted equilibrium w0 (drho - rho 3/2 u^2)
     const T e9 = wq<T>(9) * (drho - rho * k15);
     T n9 = fma(p.omega, e9 - s[9], s[9]);
-    if constexpr (FORCE) n9 = n9 + p.guo * wq<T>(9) * (T(-3) * uF);
+    if constexpr (FORCE) n9 = n9 - guF0;
     s[9] = n9;
 }
 

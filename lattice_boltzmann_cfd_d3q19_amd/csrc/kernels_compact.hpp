@@ -31,6 +31,7 @@ struct CompactGeom {
     uint32_t px;   // nx + 2
     uint32_t pxy;  // (nx + 2)(ny + 2)
     uint32_t s;    // population stride (fluid cells rounded up to 64); 2 s sizeof(T) < 2^32
+    uint32_t xk;   // workgroup chunk per XCD turn of the gather kernels (1 = hardware order)
 };
 
 // Compact indices of the 18 neighbours x + c_d (kInvalid = solid or wall),
@@ -160,21 +161,19 @@ __device__ __forceinline__ uint32_t link_off(uint32_t nbv, uint32_t nb_sub_bytes
     return nbv == kInvalid ? own_bytes : via_nb;
 }
 
-#ifndef LBM_COMPACT_XCD
-#define LBM_COMPACT_XCD 0
-#endif
-
 // Workgroup w runs on XCD w % 8 (the dispatcher deals workgroups out round
-// robin).  With LBM_COMPACT_XCD set, the gather kernels renumber them so that
-// XCD k takes the k-th contiguous slice of the fluid cells: the neighbour rows
-// a gather touches are then handled by one L2.  Measured on the 256^3 porous
-// box: 19% less HBM traffic for the in-place odd step, no change in time
-// (those kernels are bound by the address unit), so it is off by default.
-__device__ __forceinline__ uint32_t xcd_slice(uint32_t w, uint32_t nwg)
+// robin).  The gather kernels renumber them in chunks of K consecutive
+// workgroups: XCD x takes chunks x, x + 8, x + 16, ... so that a chunk's
+// neighbour rows (y +- 1 within the chunk, z +- 1 one plane = 8 chunks
+// later when K is an eighth of a plane's workgroups) are gathered through one
+// L2, while all XCDs still sweep the lattice together.  K = 1 is the
+// hardware order.  The grid is rounded up to 8 K workgroups; the extra ones
+// find no cells and exit.
+
+__device__ __forceinline__ uint32_t xcd_chunked(uint32_t hw, uint32_t k)
 {
-    const uint32_t q = nwg / 8u, r = nwg % 8u;
-    const uint32_t xcd = w % 8u, local = w / 8u;
-    return xcd < r ? xcd * (q + 1u) + local : r * (q + 1u) + (xcd - r) * q + local;
+    const uint32_t x = hw & 7u, l = hw >> 3;
+    return ((l / k) * 8u + x) * k + l % k;
 }
 
 // block of pair k inside a buffer: planes 2k, 2k + 1 (a uniform 64-bit base)
@@ -191,11 +190,7 @@ __global__ void __launch_bounds__(kBlockThreads) step_compact_kernel(T* __restri
                                                                      CompactGeom g, Phys<T> p)
 {
     static_assert(K == kAB || K == kAAOdd, "the even step has its own kernel");
-#if LBM_COMPACT_XCD
-    const uint32_t wg = xcd_slice(blockIdx.x, gridDim.x);
-#else
-    const uint32_t wg = blockIdx.x;
-#endif
+    const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
     const uint32_t i = wg * kBlockThreads + threadIdx.x;
     if (i >= g.nf) return;
     const uint32_t sb = g.s * (uint32_t)sizeof(T);  // bytes per plane; 2 sb < 2^32 (host check)
