@@ -17,6 +17,9 @@ Parity status per function (what pins it, from the tests):
                       Poiseuille closed form, shear-wave and Taylor-Green decay
   step_cells       -- equals ``run`` for one step on every cell
   moments, totals  -- direct sums, checked against numpy on the same f
+  momentum_exchange -- the step's momentum budget (P(t+1) - P(t) = N_fluid F
+                      minus the exchanged force, any state), zero force at
+                      rest, steady channel wall force = N_fluid F
 No function is "parity unpinned"; the specific random streams used to build
 inputs are unpinned by nature (determinism and statistics only).
 """
@@ -61,6 +64,7 @@ def _load():
     lib.orc_step_cells.restype = ctypes.c_int
     lib.orc_moments.argtypes = [P(_Box), u8p, dp, dp, dp]
     lib.orc_totals.argtypes = [P(_Box), u8p, dp, dp]
+    lib.orc_momentum_exchange.argtypes = [P(_Box), u8p, dp, dp]
     _lib = lib
     return lib
 
@@ -217,3 +221,17 @@ def totals(box, f, mask=None):
     b = box._c()
     lib.orc_totals(ctypes.byref(b), _mptr(m), _dptr(fin), _dptr(out))
     return {"mass": out[0], "momentum": out[1:4].copy(), "ke": out[4]}
+
+
+def momentum_exchange(box, f, mask=None):
+    """Force on the solids during the step that starts from f: dict(solid[3],
+    wall[3]), each the sum of 2 f*_q c_q over the bounce-back links that end
+    in a solid cell / leave the box through a non-periodic face."""
+    lib = _load()
+    m = _mask(box, mask)
+    fin = np.ascontiguousarray(f, np.float64).reshape(Q, box.n)
+    out = np.zeros(6, np.float64)
+    b = box._c()
+    lib.orc_momentum_exchange(ctypes.byref(b), _mptr(m), _dptr(fin), _dptr(out))
+    return {"solid": out[0:3].copy(), "wall": out[3:6].copy()}
+

@@ -294,3 +294,36 @@ void orc_totals(const orc_box *b, const uint8_t *mask, const double *f, double o
     for (int a = 0; a < 3; ++a) out[1 + a] = (double)p[a];
     out[4] = (double)ke;
 }
+
+/* Momentum exchange of the halfway bounce-back links during the step that
+ * starts from f (fieldcraft page, first section: the momentum exchange is
+ * taken over the wall links of a step).  A population f*_q that leaves fluid
+ * cell x toward a solid cell or a wall is reflected at the link midpoint and
+ * comes back as f*_q along -c_q, so the solid receives 2 f*_q c_q.  out[0..2]
+ * sums the links that end in a solid cell of the mask, out[3..5] the links
+ * that leave the box through a non-periodic face. */
+void orc_momentum_exchange(const orc_box *b, const uint8_t *mask, const double *f, double out[6])
+{
+    build_tables();
+    int64_t N = ncells(b);
+    long double solid[3] = {0.0L, 0.0L, 0.0L}, wall[3] = {0.0L, 0.0L, 0.0L};
+    for (int64_t z = 0; z < b->nz; ++z)
+        for (int64_t y = 0; y < b->ny; ++y)
+            for (int64_t xx = 0; xx < b->nx; ++xx) {
+                int64_t x = xx + b->nx * (y + b->ny * z);
+                if (is_solid(mask, x)) continue;
+                double in[ORC_Q], post[ORC_Q];
+                for (int q = 0; q < ORC_Q; ++q) in[q] = f[q * N + x];
+                orc_collide(b, in, post);
+                for (int q = 0; q < ORC_Q; ++q) {
+                    int64_t dst = neighbour(b, xx, y, z, C[q][0], C[q][1], C[q][2]);
+                    if (dst >= 0 && !is_solid(mask, dst)) continue;
+                    long double *acc = dst < 0 ? wall : solid;
+                    for (int a = 0; a < 3; ++a) acc[a] += 2.0L * (long double)post[q] * (long double)C[q][a];
+                }
+            }
+    for (int a = 0; a < 3; ++a) {
+        out[a] = (double)solid[a];
+        out[3 + a] = (double)wall[a];
+    }
+}

@@ -62,6 +62,11 @@ void orc_moments(const orc_box *b, const uint8_t *mask, const double *f, double 
 /* out = {mass, Px, Py, Pz, kinetic energy} summed over fluid cells in long double. */
 void orc_totals(const orc_box *b, const uint8_t *mask, const double *f, double out[5]);
 
+/* Momentum-exchange force of the step that starts from f: sum over the
+ * bounce-back links (fluid x, x + c_q solid or beyond a wall) of 2 f*_q c_q,
+ * f* = collision of f(x).  out = {solid x, y, z, wall x, y, z}. */
+void orc_momentum_exchange(const orc_box *b, const uint8_t *mask, const double *f, double out[6]);
+
 #ifdef __cplusplus
 }
 #endif

@@ -167,6 +167,55 @@ def test_mass_conserved_with_walls_and_mask():
     assert np.all(f1[:, solid] == 0.0)
 
 
+# ------------------------------------------- momentum exchange with the solids
+
+@pytest.mark.parametrize("periodic,F", [((1, 1, 1), (2e-4, -1e-4, 5e-5)), ((1, 0, 1), (0.0, 0.0, 3e-4)),
+                                        ((0, 0, 0), (1e-4, 2e-4, -1e-4))])
+def test_momentum_exchange_closes_the_step_budget(periodic, F):
+    # each step the collision adds F per fluid cell and every bounce-back link
+    # hands 2 f*_q c_q to the solid: P(t+1) - P(t) = N_fluid F - F_exchanged,
+    # for any state, exactly up to rounding
+    box = oracle.Box(7, 6, 5, periodic=periodic, tau=0.7, force=F)
+    mask = li.random_mask(7, 6, 5, fraction=0.2, seed=8)
+    nf = int(np.count_nonzero(mask == 0))
+    f = _random_state(box, seed=9, mask=mask)
+    for _ in range(4):
+        fx = oracle.momentum_exchange(box, f, mask)
+        p0 = oracle.totals(box, f, mask)
+        f = oracle.run(box, f, 1, mask)
+        p1 = oracle.totals(box, f, mask)
+        want = nf * np.array(F) - fx["solid"] - fx["wall"]
+        np.testing.assert_allclose(p1["momentum"] - p0["momentum"], want, rtol=0, atol=1e-14 * p0["mass"])
+        if all(periodic):
+            assert np.all(fx["wall"] == 0.0)
+        assert np.max(np.abs(fx["solid"])) > 1e-6  # the random state pushes on the solids
+
+
+def test_momentum_exchange_zero_at_rest():
+    # fluid at rest, no force: f* = w on every link; in a periodic box every row
+    # of a solid body has as many entry links as exit links, and the two walls
+    # of a channel mirror each other, so the exchanged force vanishes
+    for periodic in ((1, 1, 1), (1, 0, 1), (0, 0, 0)):
+        box = oracle.Box(8, 7, 6, periodic=periodic, tau=0.8)
+        mask = li.random_mask(8, 7, 6, fraction=0.3, seed=2) if all(periodic) else None
+        fx = oracle.momentum_exchange(box, oracle.init_equilibrium(box, mask), mask)
+        assert np.max(np.abs(fx["solid"])) < 1e-15 and np.max(np.abs(fx["wall"])) < 1e-15
+
+
+def test_steady_channel_wall_force_balances_body_force():
+    # steady plane Poiseuille flow: the walls carry the whole body force,
+    # F_wall = N_fluid g along the flow and nothing across it
+    H, g, tau = 16, 1e-5, 0.8
+    box = oracle.Box(1, H, 1, periodic=(1, 0, 1), tau=tau, force=(0.0, 0.0, g))
+    f = oracle.run(box, oracle.init_equilibrium(box), 6000)
+    fx = oracle.momentum_exchange(box, f)
+    assert abs(fx["wall"][2] - H * g) < 1e-6 * H * g
+    # across the channel the two walls take equal and opposite pressure forces
+    # (about 1/3 per wall cell), cancelling to rounding
+    assert abs(fx["wall"][0]) < 1e-18 and abs(fx["wall"][1]) < 1e-13
+    assert np.all(fx["solid"] == 0.0)
+
+
 # ------------------------------------------------ P5 / P6 streaming exactness
 
 def _brute_stream(box, f, mask):
