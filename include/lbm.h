@@ -173,6 +173,27 @@ lbm_status lbm_write_populations(lbm_sim *sim, const void *f);
 lbm_status lbm_save_state(lbm_sim *sim, void *s);
 lbm_status lbm_load_state(lbm_sim *sim, const void *s);
 
+/* Momentum exchange with the solids (fieldcraft page, first section: the
+ * momentum exchange is taken over the wall links of a step).  For the step
+ * that starts from the current state f(t), every population f*_q that leaves
+ * a fluid cell x toward a solid cell or through a wall is bounced back at the
+ * link midpoint, so the solid receives 2 f*_q c_q; f* is the post-collision
+ * state of x (collision and forcing exactly as in lbm_step).  Writes
+ *   force   device double[6]: the sum over links that end in a solid cell of
+ *           the mask (x, y, z), then over links that leave the box through a
+ *           non-periodic face (x, y, z).  8-byte aligned.
+ *   scratch device, 256-byte aligned, at least
+ *           lbm_momentum_exchange_scratch_bytes() bytes (per-workgroup
+ *           partial sums); reused by the caller freely once the call's work
+ *           on the stream has completed.
+ * The state and time are unchanged.  Sums are in double and in a fixed order,
+ * so the result is deterministic.  With F the body force and N_f the fluid
+ * cells, the fluid's momentum changes over that step by N_f F minus the two
+ * forces.  LBM_ERR_BAD_STATE before init; LBM_ERR_INVALID_ARGUMENT for NULL
+ * pointers or a short scratch; LBM_ERR_MISALIGNED for a misaligned buffer. */
+lbm_status lbm_momentum_exchange_scratch_bytes(const lbm_desc *desc, size_t *bytes);
+lbm_status lbm_momentum_exchange(lbm_sim *sim, void *force, void *scratch, size_t scratch_bytes);
+
 /* Release the handle (host memory only); NULL is a no-op. */
 lbm_status lbm_destroy(lbm_sim *sim);
 

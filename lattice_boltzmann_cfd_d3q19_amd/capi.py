@@ -26,7 +26,7 @@ LBM_SCHEME_AB, LBM_SCHEME_AA = 0, 1
 EXPORTED = ["lbm_buffer_bytes", "lbm_workspace_bytes", "lbm_create", "lbm_set_workspace", "lbm_set_geometry", "lbm_init_equilibrium", "lbm_step",
             "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_save_state",
             "lbm_load_state", "lbm_destroy", "lbm_time", "lbm_fluid_cells", "lbm_last_hip_error",
-            "lbm_status_string"]
+            "lbm_status_string", "lbm_momentum_exchange_scratch_bytes", "lbm_momentum_exchange"]
 
 
 class lbm_desc(ctypes.Structure):
@@ -84,6 +84,10 @@ _lib.lbm_save_state.argtypes = [_vp, _vp]
 _lib.lbm_save_state.restype = _st
 _lib.lbm_load_state.argtypes = [_vp, _vp]
 _lib.lbm_load_state.restype = _st
+_lib.lbm_momentum_exchange_scratch_bytes.argtypes = [_Desc_p, ctypes.POINTER(ctypes.c_size_t)]
+_lib.lbm_momentum_exchange_scratch_bytes.restype = _st
+_lib.lbm_momentum_exchange.argtypes = [_vp, _vp, _vp, ctypes.c_size_t]
+_lib.lbm_momentum_exchange.restype = _st
 _lib.lbm_destroy.argtypes = [_vp]
 _lib.lbm_destroy.restype = _st
 _lib.lbm_time.argtypes = [_vp]
@@ -178,6 +182,17 @@ def lbm_save_state(sim, s):
 
 def lbm_load_state(sim, s):
     return _lib.lbm_load_state(sim, _ptr(s))
+
+
+def lbm_momentum_exchange_scratch_bytes(desc):
+    """Return (status, bytes)."""
+    nb = ctypes.c_size_t(0)
+    st = _lib.lbm_momentum_exchange_scratch_bytes(ctypes.byref(desc), ctypes.byref(nb))
+    return st, nb.value
+
+
+def lbm_momentum_exchange(sim, force, scratch, nbytes):
+    return _lib.lbm_momentum_exchange(sim, _ptr(force), _ptr(scratch), int(nbytes))
 
 
 def lbm_destroy(sim):

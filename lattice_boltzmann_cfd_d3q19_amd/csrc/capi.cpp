@@ -345,6 +345,42 @@ lbm_status lbm_load_state(lbm_sim* sim, const void* s)
     return io(sim, lbm::kWriteS, nullptr, nullptr, s, nullptr);
 }
 
+lbm_status lbm_momentum_exchange_scratch_bytes(const lbm_desc* desc, size_t* bytes)
+{
+    const lbm_status v = validate_desc(desc);
+    if (v != LBM_OK) return v;
+    if (bytes == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    lbm::LaunchGeom g{};
+    g.nx = desc->nx;
+    g.ny = desc->ny;
+    g.nz = desc->nz;
+    *bytes = 6 * sizeof(double) * lbm::mex_partial_rows(g);
+    return LBM_OK;
+}
+
+lbm_status lbm_momentum_exchange(lbm_sim* sim, void* force, void* scratch, size_t scratch_bytes)
+{
+    if (sim == nullptr || force == nullptr || scratch == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    size_t need = 0;
+    lbm_momentum_exchange_scratch_bytes(&sim->d, &need);
+    if (scratch_bytes < need) return LBM_ERR_INVALID_ARGUMENT;
+    if ((uintptr_t)scratch % kAlign != 0 || (uintptr_t)force % sizeof(double) != 0) return LBM_ERR_MISALIGNED;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    const lbm::LaunchGeom g = geom_of(sim);
+    const lbm::LaunchPhys p = phys_of(sim);
+    const int st = state_kind(sim);
+    void* a = sim->d.scheme == LBM_SCHEME_AB ? sim->buf[sim->cur] : sim->buf[0];
+    const lbm::CompactTables* t = compact(sim->d) ? &sim->tables : nullptr;
+    hipError_t e;
+    if (sim->d.precision == LBM_F32)
+        e = lbm::launch_momentum_exchange<float>(sim->d.layout, st, (float*)a, g, t, p, (double*)scratch,
+                                                 (double*)force, sim->stream);
+    else
+        e = lbm::launch_momentum_exchange<double>(sim->d.layout, st, (double*)a, g, t, p, (double*)scratch,
+                                                  (double*)force, sim->stream);
+    return hip_status(sim, e);
+}
+
 lbm_status lbm_destroy(lbm_sim* sim)
 {
     delete sim;

@@ -1,0 +1,132 @@
+// kernels_force.hpp -- momentum exchange with the solids.
+//
+// During a step, every population f*_q that leaves a fluid cell x toward a
+// solid cell or through a wall is reflected at the link midpoint (halfway
+// bounce-back) and comes back along -c_q, so the solid takes 2 f*_q c_q
+// (fieldcraft page "GPU lattice Boltzmann: streaming layout and performance",
+// first section: the momentum exchange is taken over the wall links of the
+// step whose forces are read back).  These kernels evaluate it for the step
+// that starts from the stored state: gather the cell's 19 populations through
+// the state map, collide (the same function as the step kernels), and sum
+// 2 f*_q c_q over the bounce-back links, separately for links that end in a
+// solid cell of the mask and for links that leave the box through a
+// non-periodic face.  Sums are in double: per workgroup in a fixed order,
+// then over the workgroups in a fixed order, so the result is deterministic.
+#pragma once
+
+#include "kernels.hpp"
+#include "kernels_compact.hpp"
+
+namespace lbm {
+
+// v[0..5] summed over the workgroup (256 work-items, 2-D blocks flattened
+// x-fastest, which is how the hardware forms its waves); thread 0 writes the
+// six sums to out.
+__device__ __forceinline__ void block_sum6(double (&v)[6], double* __restrict__ out)
+{
+    __shared__ double part[kBlockThreads / 64][6];
+    const uint32_t tid = threadIdx.x + blockDim.x * threadIdx.y;
+#pragma unroll
+    for (int k = 0; k < 6; ++k)
+        for (int o = 32; o > 0; o >>= 1) v[k] += __shfl_down(v[k], o, 64);
+    if ((tid & 63u) == 0)
+#pragma unroll
+        for (int k = 0; k < 6; ++k) part[tid / 64][k] = v[k];
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+            double s = part[0][k];
+            for (uint32_t w = 1; w < (blockDim.x * blockDim.y + 63) / 64; ++w) s += part[w][k];
+            out[k] = s;
+        }
+    }
+}
+
+// Add 2 f*_q c_q of the outgoing link q (stored value s*_q = f*_q - w_q, w_q
+// rounded to T as in storage) to the solid (acc[0..2]) or wall (acc[3..5])
+// sums; f* is formed in double, so no rounding of s* + w to T.
+template <int q, typename T>
+__device__ __forceinline__ void add_link(double (&acc)[6], T spost, bool bounced, bool wall)
+{
+    const double v = bounced ? 2.0 * ((double)spost + (double)wq<T>(q)) : 0.0;
+    const double vs = wall ? 0.0 : v, vw = wall ? v : 0.0;
+    if constexpr (kCx[q] != 0) {
+        acc[0] += kCx[q] * vs;
+        acc[3] += kCx[q] * vw;
+    }
+    if constexpr (kCy[q] != 0) {
+        acc[1] += kCy[q] * vs;
+        acc[4] += kCy[q] * vw;
+    }
+    if constexpr (kCz[q] != 0) {
+        acc[2] += kCz[q] * vs;
+        acc[5] += kCz[q] * vw;
+    }
+}
+
+template <int q = 0, typename T, typename Pred>
+__device__ __forceinline__ void add_links(double (&acc)[6], const T (&s)[kQ], const Cell& c, Pred bounced)
+{
+    if constexpr (q < kQ) {
+        if constexpr (q != 9) add_link<q>(acc, s[q], bounced(q), beyond_wall(c, kCx[q], kCy[q], kCz[q]));
+        add_links<q + 1>(acc, s, c, bounced);
+    }
+}
+
+// Dense layouts: one work-item per cell (tile mapping of the step kernels),
+// one partial row of six doubles per workgroup.
+template <typename T, int L, int S>
+__global__ void __launch_bounds__(kBlockThreads) mex_kernel(T* __restrict__ a, Geom g, Phys<T> p,
+                                                            double* __restrict__ partial)
+{
+    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    Cell c;
+    if (locate(g, c) && !(g.mask != nullptr && g.mask[c.id] != 0)) {
+        const uint32_t bits = link_bits<true>(g, c);
+        T s[kQ];
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g.n, c, bits, q);
+        collide<T, true>(s, p);
+        // x + c_q is solid or beyond a wall iff the upstream bit of opp(q) is set
+        add_links(acc, s, c, [&](int q) { return ((bits >> opp(q)) & 1u) != 0; });
+    }
+    block_sum6(acc, partial + 6 * (size_t)blockIdx.x);
+}
+
+// Compact layout: same, the fluid cell found through the padded index table.
+template <typename T, int S>
+__global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restrict__ a, CompactGeom cg, Geom g,
+                                                                    Phys<T> p, double* __restrict__ partial)
+{
+    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    Cell c;
+    if (locate(g, c)) {
+        const uint32_t pp = (c.x + 1) + cg.px * (c.y + 1) + cg.pxy * (c.z + 1);
+        const uint32_t i = cg.idxp[pp];
+        if (i != kInvalid) {
+            uint32_t nb[kQ];
+            neighbours(cg, pp, nb);
+            T s[kQ];
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) s[q] = *compact_state_slot<S>(a, cg.s, i, nb, q);
+            collide<T, true>(s, p);
+            add_links(acc, s, c, [&](int q) { return nb[q] == kInvalid; });
+        }
+    }
+    block_sum6(acc, partial + 6 * (size_t)blockIdx.x);
+}
+
+// out[0..5] = sum of the n partial rows, in row order per work-item, then the
+// workgroup sum.
+static __global__ void __launch_bounds__(kBlockThreads) mex_sum_kernel(const double* __restrict__ partial, uint32_t n,
+                                                                double* __restrict__ out)
+{
+    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (uint32_t r = threadIdx.x; r < n; r += kBlockThreads)
+#pragma unroll
+        for (int k = 0; k < 6; ++k) acc[k] += partial[6 * (size_t)r + k];
+    block_sum6(acc, out);
+}
+
+}  // namespace lbm

@@ -56,4 +56,13 @@ template <typename T>
 hipError_t launch_io_compact(int state, int op, T* a, const LaunchGeom& g, const CompactTables& t,
                              const LaunchPhys& p, T* out0, T* out1, const T* in0, const T* in1, hipStream_t s);
 
+// Momentum exchange with the solids for the step that starts from the stored
+// state: force[0..2] on the mask's solid cells, force[3..5] on the walls
+// (device double[6]).  partial: device double[6 * mex_partial_rows(g)].
+size_t mex_partial_rows(const LaunchGeom& g);
+
+template <typename T>
+hipError_t launch_momentum_exchange(int layout, int state, T* a, const LaunchGeom& g, const CompactTables* t,
+                                    const LaunchPhys& p, double* partial, double* force, hipStream_t s);
+
 }  // namespace lbm

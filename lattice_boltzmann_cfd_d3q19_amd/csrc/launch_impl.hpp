@@ -5,6 +5,7 @@
 
 #include "kernels.hpp"
 #include "kernels_compact.hpp"
+#include "kernels_force.hpp"
 #include "launch.hpp"
 
 namespace lbm {
@@ -179,7 +180,7 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     // 0.430 -> 0.382 ms, 512^3 porous 3.59 -> 3.20 ms, 128^3 sphere 0.066 ->
     // 0.064 ms, periodic 256^3 unchanged; fixed chunks of 4 to 80
     // workgroups were no better on any of them.
-    const uint64_t wg_plane = ((uint64_t)t.nf / (uint64_t)lg.nz + kBlockThreads - 1) / kBlockThreads;
+    const uint64_t wg_plane = ((uint64_t)t.nf / (uint64_t)lg.nz + kGatherThreads - 1) / kGatherThreads;
     g.xk = (uint32_t)((wg_plane + 7) / 8);
     if (g.xk < 1) g.xk = 1;
     return g;
@@ -190,9 +191,9 @@ hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, hipStream
 {
     if (g.nf == 0) return hipSuccess;
     void* args[] = {&a, &b, &g, &p};
-    uint32_t nwg = (g.nf + kBlockThreads - 1) / kBlockThreads;
+    uint32_t nwg = (g.nf + kGatherThreads - 1) / kGatherThreads;
     if (g.xk > 1) nwg = (nwg + 8 * g.xk - 1) / (8 * g.xk) * (8 * g.xk);
-    const dim3 grid(nwg), block(kBlockThreads);
+    const dim3 grid(nwg), block(kGatherThreads);
     return hipLaunchKernel((const void*)&step_compact_kernel<T, K, FORCE>, grid, block, args, 0, st);
 }
 
@@ -202,7 +203,7 @@ hipError_t launch_even_compact_t(T* a, CompactGeom g, Phys<T> p, hipStream_t st)
     if (g.nf == 0) return hipSuccess;
     uint32_t s = g.s;
     void* args[] = {&a, &s, &p};
-    const dim3 grid((s + kBlockThreads - 1) / kBlockThreads), block(kBlockThreads);
+    const dim3 grid((s + kEvenThreads - 1) / kEvenThreads), block(kEvenThreads);
     return hipLaunchKernel((const void*)&even_compact_kernel<T, FORCE>, grid, block, args, 0, st);
 }
 
@@ -268,6 +269,68 @@ hipError_t launch_io_compact(int state, int op, T* a, const LaunchGeom& lg, cons
     case kAAOdd: return launch_io_compact_s<T, kAAOdd>(op, a, cg, s, p, o0, o1, i0, i1, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+// ------------------------------------------------------ momentum exchange
+
+template <typename T, int L, int S>
+hipError_t launch_mex_t(T* a, const Shape& sh, const Phys<T>& p, double* partial, hipStream_t st)
+{
+    Geom g = sh.g;
+    Phys<T> ph = p;
+    void* args[] = {&a, &g, &ph, &partial};
+    return hipLaunchKernel((const void*)&mex_kernel<T, L, S>, sh.grid, sh.block, args, 0, st);
+}
+
+template <typename T, int S>
+hipError_t launch_mex_compact_t(T* a, CompactGeom cg, const Shape& sh, const Phys<T>& p, double* partial,
+                                hipStream_t st)
+{
+    Geom g = sh.g;
+    Phys<T> ph = p;
+    void* args[] = {&a, &cg, &g, &ph, &partial};
+    return hipLaunchKernel((const void*)&mex_compact_kernel<T, S>, sh.grid, sh.block, args, 0, st);
+}
+
+template <typename T, int L>
+hipError_t launch_mex_l(int state, T* a, const Shape& sh, const Phys<T>& p, double* partial, hipStream_t st)
+{
+    switch (state) {
+    case kAB: return launch_mex_t<T, L, kAB>(a, sh, p, partial, st);
+    case kAAEven: return launch_mex_t<T, L, kAAEven>(a, sh, p, partial, st);
+    case kAAOdd: return launch_mex_t<T, L, kAAOdd>(a, sh, p, partial, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_momentum_exchange(int layout, int state, T* a, const LaunchGeom& lg, const CompactTables* t,
+                                    const LaunchPhys& lp, double* partial, double* force, hipStream_t st)
+{
+    const Shape sh = make_shape(lg);
+    const Phys<T> p = make_phys<T>(lp);
+    hipError_t e;
+    if (t != nullptr) {
+        const CompactGeom cg = compact_geom(lg, *t);
+        switch (state) {
+        case kAB: e = launch_mex_compact_t<T, kAB>(a, cg, sh, p, partial, st); break;
+        case kAAEven: e = launch_mex_compact_t<T, kAAEven>(a, cg, sh, p, partial, st); break;
+        case kAAOdd: e = launch_mex_compact_t<T, kAAOdd>(a, cg, sh, p, partial, st); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (layout) {
+        case kStream: e = launch_mex_l<T, kStream>(state, a, sh, p, partial, st); break;
+        case kBundle: e = launch_mex_l<T, kBundle>(state, a, sh, p, partial, st); break;
+        case kCollision: e = launch_mex_l<T, kCollision>(state, a, sh, p, partial, st); break;
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (e != hipSuccess) return e;
+    const double* part = partial;
+    uint32_t rows = sh.grid.x;
+    void* args[] = {&part, &rows, &force};
+    return hipLaunchKernel((const void*)&mex_sum_kernel, dim3(1), dim3(kBlockThreads), args, 0, st);
 }
 
 }  // namespace lbm

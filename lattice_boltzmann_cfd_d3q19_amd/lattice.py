@@ -108,6 +108,18 @@ class Lattice:
         capi.check(capi.lbm_write_populations(self.handle, ff.data_ptr()), "lbm_write_populations", self.handle)
         self._keep = (ff,)
 
+    def momentum_exchange(self):
+        """Force on the solids during the step that starts from the current
+        state: (solid, wall), each a float64 tensor of 3 on the device."""
+        if getattr(self, "_mex_scratch", None) is None:
+            st, nb = capi.lbm_momentum_exchange_scratch_bytes(self.desc)
+            capi.check(st, "lbm_momentum_exchange_scratch_bytes")
+            self._mex_scratch = torch.empty(nb, dtype=torch.uint8, device=self.device)
+        out = torch.empty(6, dtype=torch.float64, device=self.device)
+        capi.check(capi.lbm_momentum_exchange(self.handle, out.data_ptr(), self._mex_scratch.data_ptr(),
+                                              self._mex_scratch.numel()), "lbm_momentum_exchange", self.handle)
+        return out[0:3], out[3:6]
+
     def save_state(self):
         """Exact checkpoint: stored values f - w, canonical order [19][N]."""
         s = torch.empty((Q, self.n), dtype=self.dtype, device=self.device)

@@ -128,6 +128,25 @@ def test_state_machine_before_any_launch():
         assert capi.lbm_destroy(h) == capi.LBM_OK
 
 
+def test_momentum_exchange_arguments_before_any_launch():
+    d = capi.make_desc(40, 8, 8)
+    st, nb = capi.lbm_momentum_exchange_scratch_bytes(d)
+    # one row of six doubles per workgroup: tiles of 64 x 4 cells -> 1 x 2 x 8
+    assert st == capi.LBM_OK and nb == 6 * 8 * (1 * 2 * 8)
+    st, h = capi.lbm_create(d, FAKE)
+    assert st == capi.LBM_OK
+    try:
+        assert capi.lbm_momentum_exchange(h, None, FAKE, nb) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert capi.lbm_momentum_exchange(h, FAKE, None, nb) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert capi.lbm_momentum_exchange(h, FAKE, FAKE, nb - 1) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert capi.lbm_momentum_exchange(h, FAKE, FAKE + 8, nb) == capi.LBM_ERR_MISALIGNED
+        assert capi.lbm_momentum_exchange(h, FAKE + 4, FAKE, nb) == capi.LBM_ERR_MISALIGNED
+        assert capi.lbm_momentum_exchange(h, FAKE, FAKE, nb) == capi.LBM_ERR_BAD_STATE
+    finally:
+        capi.lbm_destroy(h)
+    assert capi.lbm_momentum_exchange(None, FAKE, FAKE, nb) == capi.LBM_ERR_INVALID_ARGUMENT
+
+
 def test_null_handle_and_status_strings():
     assert capi.lbm_destroy(None) == capi.LBM_OK
     assert capi.lbm_time(None) == -1
