@@ -14,10 +14,12 @@
 // Work decomposition: the box is cut into tiles of BX x BY cells (BX along
 // x, the fastest index, so each wave64 covers consecutive cells of one row
 // or of a few short rows); one workgroup per tile, tiles numbered x-, then
-// y-, then z-fastest.  The hardware's round-robin placement of consecutive
-// workgroups over the 8 XCDs is kept: in the SoA layouts every cache line is
-// touched by one workgroup only, and giving each XCD a contiguous slab of
-// tiles instead measured 8% slower on the 256^3 porous box.
+// y-, then z-fastest.  The SoA layouts keep the hardware's round-robin
+// placement of consecutive workgroups over the 8 XCDs (every cache line is
+// touched by one workgroup only; a contiguous slab of tiles per XCD measured
+// 8% slower and chunked orders up to 8% slower on the 256^3 porous box).  The
+// AoS layout, whose neighbour records share lines across rows, uses chunked
+// orders (xcd_chunked).
 //
 // The collision arithmetic is one inlined function used by every layout and
 // scheme, compiled with floating-point contraction off, so the result of a
@@ -35,6 +37,7 @@ struct Geom {
     uint32_t nx, ny, nz, nxy;
     uint32_t per_x, per_y, per_z;  // 1 = periodic, 0 = bounce-back wall beyond both faces
     uint32_t ntx, nty, ntiles;     // tiles per x-row of tiles, per y-column, total
+    uint32_t xk;                   // workgroup chunk per XCD turn (1 = hardware order)
     uint64_t n;                    // cells
     const uint8_t* mask;           // uint8[n], nonzero = solid; may be null
 };
@@ -126,10 +129,21 @@ struct Cell {
     bool wall[3][2];               // beyond the low / high face on a non-periodic axis
 };
 
+// Workgroup w runs on XCD w % 8 (the dispatcher deals workgroups out round
+// robin).  Renumbered in chunks of k consecutive workgroups, XCD x takes
+// chunks x, x + 8, x + 16, ...: neighbouring rows of tiles then share an L2.
+// k = 1 is the hardware order; the grid is rounded up to 8 k workgroups.
+__device__ __forceinline__ uint32_t xcd_chunked(uint32_t hw, uint32_t k)
+{
+    const uint32_t x = hw & 7u, l = hw >> 3;
+    return ((l / k) * 8u + x) * k + l % k;
+}
+
 // Decode this work-item's cell; false if it lies outside the box.
 __device__ __forceinline__ bool locate(const Geom& g, Cell& c)
 {
-    const uint32_t tile = blockIdx.x;
+    const uint32_t tile = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
+    if (tile >= g.ntiles) return false;
     const uint32_t tx = tile % g.ntx;
     const uint32_t rest = tile / g.ntx;
     const uint32_t ty = rest % g.nty;

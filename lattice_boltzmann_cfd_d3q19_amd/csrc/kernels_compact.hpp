@@ -182,11 +182,6 @@ __device__ __forceinline__ uint32_t link_off(uint32_t nbv, uint32_t nb_sub_bytes
 // hardware order.  The grid is rounded up to 8 K workgroups; the extra ones
 // find no cells and exit.
 
-__device__ __forceinline__ uint32_t xcd_chunked(uint32_t hw, uint32_t k)
-{
-    const uint32_t x = hw & 7u, l = hw >> 3;
-    return ((l / k) * 8u + x) * k + l % k;
-}
 
 // block of pair k inside a buffer: planes 2k, 2k + 1 (a uniform 64-bit base)
 __device__ __forceinline__ char* pair_block(char* base, int k, uint32_t plane_bytes)

@@ -17,7 +17,7 @@ struct Shape {
 
 // Tile shape: BX = smallest power of two >= nx, clamped to [32, 256], so a
 // wave64 covers one row segment (or two rows of 32); BY fills 256 threads.
-inline Shape make_shape(const LaunchGeom& lg)
+inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
 {
     Shape s{};
     uint32_t bx = 32;
@@ -36,8 +36,16 @@ inline Shape make_shape(const LaunchGeom& lg)
     g.ntiles = g.ntx * g.nty * g.nz;
     g.n = (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz;
     g.mask = lg.mask;
+    g.xk = 1;
+    if (xcd_chunks) {
+        // an eighth of a z-plane's tiles per chunk: the tiles of rows y +- 1
+        // and of the planes z +- 1 then run on the same XCD
+        g.xk = (g.ntx * g.nty + 7) / 8;
+        if (g.xk < 1) g.xk = 1;
+    }
     s.block = dim3(bx, by, 1);
-    s.grid = dim3(g.ntiles, 1, 1);
+    const uint32_t chunk = 8 * g.xk;
+    s.grid = dim3(g.xk > 1 ? (g.ntiles + chunk - 1) / chunk * chunk : g.ntiles, 1, 1);
     return s;
 }
 
@@ -101,7 +109,10 @@ template <typename T>
 hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp,
                        hipStream_t st)
 {
-    const Shape s = make_shape(lg);
+    // XCD-chunked tile order for the AoS layout only.  Measured, 256^3 porous
+    // box, hardware order -> chunked: collision AA odd 2.06 -> 1.22 ms, AB
+    // 0.92 -> 0.78 ms; stream AA +8% / +2% and AB +7%, bundle within 2%.
+    const Shape s = make_shape(lg, layout == kCollision);
     const Phys<T> p = make_phys<T>(lp);
     const bool bnd = lg.mask != nullptr || !lg.periodic[0] || !lg.periodic[1] || !lg.periodic[2];
     switch (layout) {
