@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(kBlockThreads) compact_fill_rows(const uint8_t
     }
 }
 
-// Halo of idxp: periodic image or kInvalid (beyond a wall).
+// Halo of idxp: periodic image, or kWall beyond a non-periodic face.
 __global__ void __launch_bounds__(kBlockThreads) compact_fill_halo(uint32_t nx, uint32_t ny, uint32_t nz,
                                                                    uint32_t per_x, uint32_t per_y, uint32_t per_z,
                                                                    uint32_t px, uint32_t pxy, uint64_t npad,
@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(kBlockThreads) compact_fill_halo(uint32_t nx, 
     const bool ox = gx < 0 || gx >= (int32_t)nx, oy = gy < 0 || gy >= (int32_t)ny, oz = gz < 0 || gz >= (int32_t)nz;
     if (!ox && !oy && !oz) return;  // interior: filled per row
     if ((ox && !per_x) || (oy && !per_y) || (oz && !per_z)) {
-        idxp[pp] = kInvalid;
+        idxp[pp] = kWall;
         return;
     }
     const uint32_t ix = (uint32_t)((gx + (int32_t)nx) % (int32_t)nx);

@@ -1,8 +1,9 @@
 // kernels_compact.hpp -- the fluid-compacted SoA layout ("compact").
 //
 // Only fluid cells are stored: population q of the i-th fluid cell (fluid
-// cells ranked in cell order) lives at q * S + i, S = the fluid count rounded
-// up to 64.  In a porous medium a dense layout moves whole cache lines that
+// cells ranked in cell order) lives at P(q) * S + i, S = the fluid count
+// rounded up to 64, P(q) the storage plane of q (opposite directions side by
+// side, below).  In a porous medium a dense layout moves whole cache lines that
 // are mostly solid (in the 256^3, 62%-porous benchmark medium 98.6% of
 // 128-byte lines hold some fluid, so a dense step moves ~1.6x the fluid
 // bytes); here every population line is fully used.
@@ -11,7 +12,7 @@
 //   idxp[p]   for every cell of the box padded by one halo layer on each side,
 //             p = (x+1) + px ((y+1) + py (z+1)), px = nx+2, py = ny+2: the
 //             compact index of the cell, kInvalid for solid cells; halo cells
-//             hold the index of their periodic image, or kInvalid beyond a
+//             hold the index of their periodic image, or kWall beyond a
 //             non-periodic face (halfway bounce-back walls).
 //   cellp[i]  padded id p of the i-th fluid cell.
 // A neighbour along c_d is then idxp[cellp[i] + off_d] with
@@ -22,7 +23,13 @@
 
 namespace lbm {
 
+// Index-table markers: a solid cell, and a halo cell beyond a non-periodic
+// face (a wall).  Both are "no fluid neighbour" (>= kWall) to the step
+// kernels; the momentum exchange tells them apart.
 constexpr uint32_t kInvalid = 0xFFFFFFFFu;
+constexpr uint32_t kWall = 0xFFFFFFFEu;
+
+__device__ __forceinline__ bool no_fluid(uint32_t nbv) { return nbv >= kWall; }
 
 // Workgroup sizes of the compact step kernels.  Measured on the porous
 // boxes: 512-thread gathers 0.5% (256^3) and 1.2% (512^3) faster than 256,
@@ -46,7 +53,7 @@ struct CompactGeom {
     uint32_t xk;   // workgroup chunk per XCD turn of the gather kernels (1 = hardware order)
 };
 
-// Compact indices of the 18 neighbours x + c_d (kInvalid = solid or wall),
+// Compact indices of the 18 neighbours x + c_d (kInvalid: solid, kWall: wall),
 // used by the state transfers: one table read per direction.
 __device__ __forceinline__ void neighbours(const CompactGeom& g, uint32_t p, uint32_t (&nb)[kQ])
 {
@@ -120,11 +127,11 @@ __device__ __forceinline__ uint64_t compact_state_off(uint64_t s, uint32_t i, co
 {
     const uint32_t up = nb[opp(q)];
     if constexpr (S == kAB) {
-        return up == kInvalid ? (uint64_t)plane_of(opp(q)) * s + i : (uint64_t)plane_of(q) * s + up;
+        return no_fluid(up) ? (uint64_t)plane_of(opp(q)) * s + i : (uint64_t)plane_of(q) * s + up;
     } else if constexpr (S == kAAEven) {
         return (uint64_t)plane_of(q) * s + i;
     } else {
-        return up == kInvalid ? (uint64_t)plane_of(q) * s + i : (uint64_t)plane_of(opp(q)) * s + up;
+        return no_fluid(up) ? (uint64_t)plane_of(q) * s + i : (uint64_t)plane_of(opp(q)) * s + up;
     }
 }
 
@@ -170,7 +177,7 @@ template <typename T>
 __device__ __forceinline__ uint32_t link_off(uint32_t nbv, uint32_t nb_sub_bytes, uint32_t own_bytes)
 {
     const uint32_t via_nb = nbv * (uint32_t)sizeof(T) + nb_sub_bytes;
-    return nbv == kInvalid ? own_bytes : via_nb;
+    return no_fluid(nbv) ? own_bytes : via_nb;
 }
 
 // Workgroup w runs on XCD w % 8 (the dispatcher deals workgroups out round

@@ -94,25 +94,46 @@ __global__ void __launch_bounds__(kBlockThreads) mex_kernel(T* __restrict__ a, G
     block_sum6(acc, partial + 6 * (size_t)blockIdx.x);
 }
 
-// Compact layout: same, the fluid cell found through the padded index table.
+template <int q = 0, typename T>
+__device__ __forceinline__ void add_links_nb(double (&acc)[6], const T (&s)[kQ], const uint32_t (&nb)[kQ])
+{
+    if constexpr (q < kQ) {
+        if constexpr (q != 9) add_link<q>(acc, s[q], no_fluid(nb[q]), nb[q] == kWall);
+        add_links_nb<q + 1>(acc, s, nb);
+    }
+}
+
+// Compact layout: one work-item per fluid cell, the gathers of the step
+// kernels (row-wise neighbour reads, the same slot maps), one partial row per
+// workgroup.  The index table marks wall links (kWall) apart from solid ones.
 template <typename T, int S>
-__global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restrict__ a, CompactGeom cg, Geom g,
-                                                                    Phys<T> p, double* __restrict__ partial)
+__global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restrict__ a, CompactGeom g, Phys<T> p,
+                                                                    double* __restrict__ partial)
 {
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    Cell c;
-    if (locate(g, c)) {
-        const uint32_t pp = (c.x + 1) + cg.px * (c.y + 1) + cg.pxy * (c.z + 1);
-        const uint32_t i = cg.idxp[pp];
-        if (i != kInvalid) {
-            uint32_t nb[kQ];
-            neighbours(cg, pp, nb);
-            T s[kQ];
+    const uint32_t i = blockIdx.x * kBlockThreads + threadIdx.x;
+    if (i < g.nf) {
+        const uint32_t sb = g.s * (uint32_t)sizeof(T);
+        const uint32_t own0 = i * (uint32_t)sizeof(T);
+        const uint32_t own1 = own0 + sb;
+        char* const A = (char*)a;
+        uint32_t nb[kQ];
+        neighbours_rows(g, g.cellp[i], nb);
+        T f[kQ];
 #pragma unroll
-            for (int q = 0; q < kQ; ++q) s[q] = *compact_state_slot<S>(a, cg.s, i, nb, q);
-            collide<T, true>(s, p);
-            add_links(acc, s, c, [&](int q) { return nb[q] == kInvalid; });
+        for (int q = 0; q < kQ; ++q) {
+            uint32_t off;
+            if constexpr (S == kAAEven) {
+                off = sub_of(q) ? own1 : own0;
+            } else if constexpr (S == kAB) {
+                off = q == 9 ? own0 : link_off<T>(nb[opp(q)], sub_of(q) ? sb : 0u, sub_of(opp(q)) ? own1 : own0);
+            } else {
+                off = q == 9 ? own0 : link_off<T>(nb[opp(q)], sub_of(opp(q)) ? sb : 0u, sub_of(q) ? own1 : own0);
+            }
+            f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), off);
         }
+        collide<T, true>(f, p);
+        add_links_nb(acc, f, nb);
     }
     block_sum6(acc, partial + 6 * (size_t)blockIdx.x);
 }

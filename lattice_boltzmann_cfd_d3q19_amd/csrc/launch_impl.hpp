@@ -294,13 +294,12 @@ hipError_t launch_mex_t(T* a, const Shape& sh, const Phys<T>& p, double* partial
 }
 
 template <typename T, int S>
-hipError_t launch_mex_compact_t(T* a, CompactGeom cg, const Shape& sh, const Phys<T>& p, double* partial,
-                                hipStream_t st)
+hipError_t launch_mex_compact_t(T* a, CompactGeom cg, const Phys<T>& p, double* partial, hipStream_t st)
 {
-    Geom g = sh.g;
     Phys<T> ph = p;
-    void* args[] = {&a, &cg, &g, &ph, &partial};
-    return hipLaunchKernel((const void*)&mex_compact_kernel<T, S>, sh.grid, sh.block, args, 0, st);
+    void* args[] = {&a, &cg, &ph, &partial};
+    const dim3 grid((cg.nf + kBlockThreads - 1) / kBlockThreads), block(kBlockThreads);
+    return hipLaunchKernel((const void*)&mex_compact_kernel<T, S>, grid, block, args, 0, st);
 }
 
 template <typename T, int L>
@@ -318,16 +317,22 @@ template <typename T>
 hipError_t launch_momentum_exchange(int layout, int state, T* a, const LaunchGeom& lg, const CompactTables* t,
                                     const LaunchPhys& lp, double* partial, double* force, hipStream_t st)
 {
+    // partial rows: one per workgroup; fewer than mex_partial_rows() in the
+    // compact case (fluid cells / 256 <= cells / 256 <= tiles)
     const Shape sh = make_shape(lg);
     const Phys<T> p = make_phys<T>(lp);
-    hipError_t e;
+    hipError_t e = hipSuccess;
+    uint32_t rows = sh.grid.x;
     if (t != nullptr) {
         const CompactGeom cg = compact_geom(lg, *t);
-        switch (state) {
-        case kAB: e = launch_mex_compact_t<T, kAB>(a, cg, sh, p, partial, st); break;
-        case kAAEven: e = launch_mex_compact_t<T, kAAEven>(a, cg, sh, p, partial, st); break;
-        case kAAOdd: e = launch_mex_compact_t<T, kAAOdd>(a, cg, sh, p, partial, st); break;
-        default: return hipErrorInvalidValue;
+        rows = (cg.nf + kBlockThreads - 1) / kBlockThreads;
+        if (rows > 0) {
+            switch (state) {
+            case kAB: e = launch_mex_compact_t<T, kAB>(a, cg, p, partial, st); break;
+            case kAAEven: e = launch_mex_compact_t<T, kAAEven>(a, cg, p, partial, st); break;
+            case kAAOdd: e = launch_mex_compact_t<T, kAAOdd>(a, cg, p, partial, st); break;
+            default: return hipErrorInvalidValue;
+            }
         }
     } else {
         switch (layout) {
@@ -339,7 +344,6 @@ hipError_t launch_momentum_exchange(int layout, int state, T* a, const LaunchGeo
     }
     if (e != hipSuccess) return e;
     const double* part = partial;
-    uint32_t rows = sh.grid.x;
     void* args[] = {&part, &rows, &force};
     return hipLaunchKernel((const void*)&mex_sum_kernel, dim3(1), dim3(kBlockThreads), args, 0, st);
 }

@@ -61,10 +61,16 @@ def test_force_matches_oracle_all_layouts_schemes(name, precision):
                 if all(per):
                     assert np.all(wall == 0.0)
                 results.setdefault(lat.t, {})[(layout, scheme)] = np.concatenate([solid, wall])
+    # the dense layouts share the cell-to-workgroup mapping and so the order of
+    # the sums: bit-identical; the compact layout sums per fluid cell, in
+    # another order: equal to rounding
     for t, r in results.items():
         ref = r[("stream", "ab")]
         for k, v in r.items():
-            assert np.array_equal(v, ref), f"t={t}: {k} differs from stream/ab"
+            if k[0] == "compact":
+                assert np.max(np.abs(v - ref)) <= 1e-15 * n, f"t={t}: {k} differs from stream/ab"
+            else:
+                assert np.array_equal(v, ref), f"t={t}: {k} differs from stream/ab"
 
 
 @pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "ab"), ("bundle", "aa")])

@@ -270,7 +270,7 @@ def test_full_size_sampled_steps(name, layout, scheme):
 def test_compact_tables_bit_exact(periodic):
     """The device-built tables of the compact layout equal a numpy construction:
     fluid cells ranked in cell order; halo cells hold their periodic image or
-    the invalid marker beyond a wall."""
+    the wall marker beyond a non-periodic face."""
     need_gpu()
     import torch
     shape = (37, 21, 13)
@@ -293,7 +293,8 @@ def test_compact_tables_bit_exact(periodic):
             ok &= ~out
         coords.append(np.mod(g, n))
     cell = coords[0] + nx * (coords[1] + ny * coords[2])
-    want_idxp = np.where(ok, rank[cell], 0xFFFFFFFF).astype(np.uint32).reshape(-1)
+    # beyond a wall: the wall marker 0xFFFFFFFE (solid cells: 0xFFFFFFFF)
+    want_idxp = np.where(ok, rank[cell], 0xFFFFFFFE).astype(np.uint32).reshape(-1)
     ws = lat.workspace.cpu().numpy().view(np.uint32)
     # header (256 B), then the row table, then idxp, then cellp (256-B aligned)
     rows_words = ((4 * ny * nz + 255) // 256 * 256) // 4
