@@ -38,7 +38,8 @@ _lib = None
 class _Box(ctypes.Structure):
     _fields_ = [("nx", ctypes.c_int64), ("ny", ctypes.c_int64), ("nz", ctypes.c_int64),
                 ("periodic", ctypes.c_int32 * 3), ("tau", ctypes.c_double),
-                ("force", ctypes.c_double * 3)]
+                ("force", ctypes.c_double * 3), ("open", ctypes.c_int32 * 6),
+                ("face_rho", ctypes.c_double * 6), ("face_u", (ctypes.c_double * 3) * 6)]
 
 
 def _load():
@@ -65,6 +66,7 @@ def _load():
     lib.orc_moments.argtypes = [P(_Box), u8p, dp, dp, dp]
     lib.orc_totals.argtypes = [P(_Box), u8p, dp, dp]
     lib.orc_momentum_exchange.argtypes = [P(_Box), u8p, dp, dp]
+    lib.orc_apply_open_faces.argtypes = [P(_Box), u8p, dp]
     _lib = lib
     return lib
 
@@ -79,14 +81,23 @@ def _mptr(mask):
     return mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
 
 
-class Box:
-    """Box description: dims, periodic axes, relaxation time, body force."""
+FACES = ("-x", "+x", "-y", "+y", "-z", "+z")
 
-    def __init__(self, nx, ny, nz, periodic=(1, 1, 1), tau=1.0, force=(0.0, 0.0, 0.0)):
+
+class Box:
+    """Box description: dims, periodic axes, relaxation time, body force, and
+    open faces: ``open_faces`` maps a face name ("-x", "+x", ...) on a
+    non-periodic axis to its reservoir (rho, (ux, uy, uz)); populations
+    entering through that face are the reservoir's equilibrium."""
+
+    def __init__(self, nx, ny, nz, periodic=(1, 1, 1), tau=1.0, force=(0.0, 0.0, 0.0), open_faces=None):
         self.nx, self.ny, self.nz = int(nx), int(ny), int(nz)
         self.periodic = tuple(int(p) for p in periodic)
         self.tau = float(tau)
         self.force = tuple(float(v) for v in force)
+        self.open_faces = dict(open_faces or {})
+        for k in self.open_faces:
+            assert k in FACES and not self.periodic[FACES.index(k) // 2], k
 
     @property
     def n(self):
@@ -102,6 +113,11 @@ class Box:
         b.periodic[:] = list(self.periodic)
         b.tau = self.tau
         b.force[:] = list(self.force)
+        for k, (rho, u) in self.open_faces.items():
+            i = FACES.index(k)
+            b.open[i] = 1
+            b.face_rho[i] = float(rho)
+            b.face_u[i][:] = [float(v) for v in u]
         return b
 
 
@@ -234,4 +250,15 @@ def momentum_exchange(box, f, mask=None):
     b = box._c()
     lib.orc_momentum_exchange(ctypes.byref(b), _mptr(m), _dptr(fin), _dptr(out))
     return {"solid": out[0:3].copy(), "wall": out[3:6].copy()}
+
+
+def apply_open_faces(box, f, mask=None):
+    """Copy of f with every population entering through an open face set to
+    the face reservoir's equilibrium."""
+    lib = _load()
+    m = _mask(box, mask)
+    out = np.array(f, np.float64, copy=True).reshape(Q, box.n)
+    b = box._c()
+    lib.orc_apply_open_faces(ctypes.byref(b), _mptr(m), _dptr(out))
+    return out
 

@@ -35,7 +35,11 @@
  *    F_q = (1 - omega/2) w_q [3 (c_q - u) + 9 (c_q.u) c_q] . F, with F a
  *    constant force density.
  *  - tau = +inf means omega = 0: collision is the identity (streaming only).
- *  - Cells outside a non-periodic face count as solid.
+ *  - Cells outside a non-periodic face count as solid, unless that face is
+ *    open: then the populations entering through it are the equilibrium of
+ *    the face's (rho, u) (PortLBM page, section 3.1: the inlet takes the
+ *    equilibrium distribution of Dirichlet values; used here at every open
+ *    face), and those leaving through it are dropped.
  */
 #include "lbm_oracle.h"
 
@@ -138,18 +142,65 @@ static int is_solid(const uint8_t *mask, int64_t cell)
     return mask != NULL && mask[cell] != 0;
 }
 
-/* Cell index of (x + dx, y + dy, z + dz), wrapped on periodic axes; -1 if it
- * lies beyond a non-periodic face. */
-static int64_t neighbour(const orc_box *b, int64_t x, int64_t y, int64_t z, int dx, int dy, int dz)
+/* What lies at (x + dx, y + dy, z + dz): a fluid cell (its index in *cell),
+ * a solid cell or a wall (bounce-back), or the reservoir of an open face
+ * (its number in *face).  Periodic axes wrap.  Beyond two faces at once (an
+ * edge of the box), a wall wins over an open face, and of two open faces the
+ * one on the first axis in x, y, z order is used. */
+enum { LINK_FLUID = 0, LINK_SOLID = 1, LINK_WALL = 2, LINK_OPEN = 3 };
+
+static int classify(const orc_box *b, const uint8_t *mask, int64_t x, int64_t y, int64_t z, int dx, int dy,
+                    int dz, int64_t *cell, int *face)
 {
     int64_t p[3] = {x + dx, y + dy, z + dz};
     int64_t n[3] = {b->nx, b->ny, b->nz};
+    int wall = 0, open_face = -1;
     for (int a = 0; a < 3; ++a) {
         if (p[a] >= 0 && p[a] < n[a]) continue;
-        if (!b->periodic[a]) return -1;
-        p[a] = (p[a] + n[a]) % n[a];
+        if (b->periodic[a]) {
+            p[a] = (p[a] + n[a]) % n[a];
+            continue;
+        }
+        int k = 2 * a + (p[a] < 0 ? 0 : 1);
+        if (b->open[k]) {
+            if (open_face < 0) open_face = k;
+        } else {
+            wall = 1;
+        }
     }
-    return p[0] + b->nx * (p[1] + b->ny * p[2]);
+    if (wall) return LINK_WALL;
+    if (open_face >= 0) {
+        *face = open_face;
+        return LINK_OPEN;
+    }
+    *cell = p[0] + b->nx * (p[1] + b->ny * p[2]);
+    return is_solid(mask, *cell) ? LINK_SOLID : LINK_FLUID;
+}
+
+static void face_equilibrium(const orc_box *b, int face, double feq[ORC_Q])
+{
+    orc_equilibrium(b->face_rho[face], b->face_u[face], feq);
+}
+
+void orc_apply_open_faces(const orc_box *b, const uint8_t *mask, double *f)
+{
+    build_tables();
+    int64_t N = ncells(b);
+    for (int64_t z = 0; z < b->nz; ++z)
+        for (int64_t y = 0; y < b->ny; ++y)
+            for (int64_t xx = 0; xx < b->nx; ++xx) {
+                int64_t x = xx + b->nx * (y + b->ny * z);
+                if (is_solid(mask, x)) continue;
+                for (int q = 0; q < ORC_Q; ++q) {
+                    int64_t src;
+                    int face;
+                    if (classify(b, mask, xx, y, z, -C[q][0], -C[q][1], -C[q][2], &src, &face) != LINK_OPEN)
+                        continue;
+                    double feq[ORC_Q];
+                    face_equilibrium(b, face, feq);
+                    f[q * N + x] = feq[q];
+                }
+            }
 }
 
 int orc_init_equilibrium(const orc_box *b, const uint8_t *mask, const double *rho0,
@@ -170,6 +221,7 @@ int orc_init_equilibrium(const orc_box *b, const uint8_t *mask, const double *rh
         orc_equilibrium(rho, u, feq);
         for (int q = 0; q < ORC_Q; ++q) f[q * N + x] = feq[q];
     }
+    orc_apply_open_faces(b, mask, f);
     return 0;
 }
 
@@ -190,8 +242,9 @@ static void collide_all(const orc_box *b, const uint8_t *mask, const double *f, 
 }
 
 /* Streaming pass (pull): the value arriving at x along c_q left x - c_q, unless
- * that cell is solid or outside, in which case the population that left x
- * along -c_q is reflected back at the link midpoint. */
+ * that cell is solid or beyond a wall, in which case the population that left
+ * x along -c_q is reflected back at the link midpoint, or lies beyond an open
+ * face, in which case it is the face reservoir's equilibrium population. */
 static void stream_all(const orc_box *b, const uint8_t *mask, const double *post, double *fnew)
 {
     int64_t N = ncells(b);
@@ -204,11 +257,18 @@ static void stream_all(const orc_box *b, const uint8_t *mask, const double *post
                         fnew[q * N + x] = 0.0;
                         continue;
                     }
-                    int64_t src = neighbour(b, xx, y, z, -C[q][0], -C[q][1], -C[q][2]);
-                    if (src < 0 || is_solid(mask, src))
-                        fnew[q * N + x] = post[OPP[q] * N + x];
-                    else
+                    int64_t src = -1;
+                    int face = -1;
+                    int kind = classify(b, mask, xx, y, z, -C[q][0], -C[q][1], -C[q][2], &src, &face);
+                    if (kind == LINK_FLUID) {
                         fnew[q * N + x] = post[q * N + src];
+                    } else if (kind == LINK_OPEN) {
+                        double feq[ORC_Q];
+                        face_equilibrium(b, face, feq);
+                        fnew[q * N + x] = feq[q];
+                    } else {
+                        fnew[q * N + x] = post[OPP[q] * N + x];
+                    }
                 }
             }
 }
@@ -243,8 +303,16 @@ int orc_step_cells(const orc_box *b, const uint8_t *mask, const double *f, int64
         }
         int64_t xx = x % b->nx, y = (x / b->nx) % b->ny, z = x / (b->nx * b->ny);
         for (int q = 0; q < ORC_Q; ++q) {
-            int64_t src = neighbour(b, xx, y, z, -C[q][0], -C[q][1], -C[q][2]);
-            int use_bb = (src < 0 || is_solid(mask, src));
+            int64_t src = -1;
+            int face = -1;
+            int kind = classify(b, mask, xx, y, z, -C[q][0], -C[q][1], -C[q][2], &src, &face);
+            if (kind == LINK_OPEN) {
+                double feq[ORC_Q];
+                face_equilibrium(b, face, feq);
+                o[q] = feq[q];
+                continue;
+            }
+            int use_bb = kind != LINK_FLUID;
             int64_t from = use_bb ? x : src;
             double in[ORC_Q], post[ORC_Q];
             for (int p = 0; p < ORC_Q; ++p) in[p] = f[p * N + from];
@@ -301,7 +369,8 @@ void orc_totals(const orc_box *b, const uint8_t *mask, const double *f, double o
  * cell x toward a solid cell or a wall is reflected at the link midpoint and
  * comes back as f*_q along -c_q, so the solid receives 2 f*_q c_q.  out[0..2]
  * sums the links that end in a solid cell of the mask, out[3..5] the links
- * that leave the box through a non-periodic face. */
+ * that leave the box through a wall (a non-periodic face that is not open;
+ * links through open faces carry flux, not force on a solid). */
 void orc_momentum_exchange(const orc_box *b, const uint8_t *mask, const double *f, double out[6])
 {
     build_tables();
@@ -316,9 +385,11 @@ void orc_momentum_exchange(const orc_box *b, const uint8_t *mask, const double *
                 for (int q = 0; q < ORC_Q; ++q) in[q] = f[q * N + x];
                 orc_collide(b, in, post);
                 for (int q = 0; q < ORC_Q; ++q) {
-                    int64_t dst = neighbour(b, xx, y, z, C[q][0], C[q][1], C[q][2]);
-                    if (dst >= 0 && !is_solid(mask, dst)) continue;
-                    long double *acc = dst < 0 ? wall : solid;
+                    int64_t dst = -1;
+                    int face = -1;
+                    int kind = classify(b, mask, xx, y, z, C[q][0], C[q][1], C[q][2], &dst, &face);
+                    if (kind == LINK_FLUID || kind == LINK_OPEN) continue;
+                    long double *acc = kind == LINK_WALL ? wall : solid;
                     for (int a = 0; a < 3; ++a) acc[a] += 2.0L * (long double)post[q] * (long double)C[q][a];
                 }
             }

@@ -27,6 +27,14 @@ typedef struct {
     int32_t periodic[3]; /* 1: periodic axis; 0: halfway bounce-back wall beyond both faces */
     double tau;          /* BGK relaxation time; +inf gives omega = 0 (no collision) */
     double force[3];     /* constant body-force density, Guo forcing; zeros = off */
+    /* Open faces, in the order -x, +x, -y, +y, -z, +z (only on non-periodic
+     * axes): open[k] = 1 replaces the wall beyond face k by a reservoir at
+     * equilibrium, so every population entering the box through face k is
+     * feq(face_rho[k], face_u[k]) (the equilibrium Dirichlet inlet of the
+     * PortLBM page, section 3.1, used at every open face). */
+    int32_t open[6];
+    double face_rho[6];
+    double face_u[6][3];
 } orc_box;
 
 /* Velocity set, weights and opposite-direction table. */
@@ -61,6 +69,10 @@ void orc_moments(const orc_box *b, const uint8_t *mask, const double *f, double 
 
 /* out = {mass, Px, Py, Pz, kinetic energy} summed over fluid cells in long double. */
 void orc_totals(const orc_box *b, const uint8_t *mask, const double *f, double out[5]);
+
+/* Set every population entering the box through an open face to the face's
+ * equilibrium (the state invariant of open faces; init applies it). */
+void orc_apply_open_faces(const orc_box *b, const uint8_t *mask, double *f);
 
 /* Momentum-exchange force of the step that starts from f: sum over the
  * bounce-back links (fluid x, x + c_q solid or beyond a wall) of 2 f*_q c_q,

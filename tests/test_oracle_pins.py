@@ -216,6 +216,74 @@ def test_steady_channel_wall_force_balances_body_force():
     assert np.all(fx["solid"] == 0.0)
 
 
+# ----------------------------------------------------------- open faces
+
+def test_open_faces_keep_uniform_flow():
+    # a uniform stream whose reservoirs on both open faces hold the same
+    # equilibrium is a fixed point of the update: what leaves equals what the
+    # reservoir sends in, on every link
+    for periodic, faces, u in (((0, 1, 1), ("-x", "+x"), (0.03, -0.01, 0.02)),
+                               ((1, 0, 1), ("-y", "+y"), (0.01, 0.025, 0.0)),
+                               ((0, 0, 1), ("-x", "+x", "-y", "+y"), (0.02, 0.01, -0.015))):
+        box = oracle.Box(7, 6, 5, periodic=periodic, tau=0.8, open_faces={k: (1.02, u) for k in faces})
+        n = box.n
+        f0 = oracle.init_equilibrium(box, None, np.full(n, 1.02), np.tile(np.array(u)[:, None], (1, n)))
+        f1 = oracle.run(box, f0, 40)
+        assert np.max(np.abs(f1 - f0)) < 1e-15, periodic
+
+
+def test_open_faces_close_mass_and_momentum_budget():
+    # open x faces, periodic y and z: per step the box gains what the
+    # reservoirs send in along the entering links and loses the post-collision
+    # populations on the leaving links (collision conserves mass and adds F
+    # per fluid cell; bounce-back at solids hands 2 f* c to them)
+    F = (1e-4, 2e-5, 0.0)
+    faces = {"-x": (1.01, (0.04, 0.0, 0.01)), "+x": (0.99, (0.02, -0.01, 0.0))}
+    box = oracle.Box(9, 6, 5, periodic=(0, 1, 1), tau=0.75, force=F, open_faces=faces)
+    mask = li.random_mask(9, 6, 5, fraction=0.15, seed=12)
+    nf = int(np.count_nonzero(mask == 0))
+    c, _, _ = oracle.lattice()
+    rho, u = li.random_fields(9, 6, 5, seed=13)
+    f = oracle.init_equilibrium(box, mask, rho, u)
+    solid = mask.reshape(5, 6, 9).astype(bool)
+    feq = {k: oracle.equilibrium(r, v) for k, (r, v) in faces.items()}
+    for _ in range(3):
+        m0 = oracle.totals(box, f, mask)
+        gain_m, gain_p = 0.0, np.zeros(3)
+        fz = f.reshape(19, 5, 6, 9)
+        for z in range(5):
+            for y in range(6):
+                for x, face, side in ((0, "-x", 1), (8, "+x", -1)):
+                    if solid[z, y, x]:
+                        continue
+                    post = oracle.collide(box, fz[:, z, y, x])
+                    for q in range(19):
+                        if c[q][0] == side:      # enters through this face
+                            gain_m += feq[face][q]
+                            gain_p += feq[face][q] * c[q]
+                        elif c[q][0] == -side:   # leaves through it
+                            gain_m -= post[q]
+                            gain_p -= post[q] * c[q]
+        fx = oracle.momentum_exchange(box, f, mask)
+        f = oracle.run(box, f, 1, mask)
+        m1 = oracle.totals(box, f, mask)
+        assert abs(m1["mass"] - m0["mass"] - gain_m) < 1e-13 * m0["mass"]
+        want_p = gain_p + nf * np.array(F) - fx["solid"] - fx["wall"]
+        np.testing.assert_allclose(m1["momentum"] - m0["momentum"], want_p, rtol=0, atol=1e-13 * m0["mass"])
+        assert np.all(fx["wall"] == 0.0)
+
+
+def test_apply_open_faces_is_what_init_does():
+    faces = {"-z": (1.0, (0.0, 0.01, 0.03)), "+y": (1.03, (0.0, 0.0, 0.0))}
+    box = oracle.Box(6, 7, 8, periodic=(1, 0, 0), tau=0.9, open_faces=faces)
+    rho, u = li.random_fields(6, 7, 8, seed=3)
+    f = oracle.init_equilibrium(box, None, rho, u)
+    plain = oracle.init_equilibrium(oracle.Box(6, 7, 8, periodic=(1, 0, 0), tau=0.9), None, rho, u)
+    np.testing.assert_array_equal(oracle.apply_open_faces(box, plain), f)
+    np.testing.assert_array_equal(oracle.apply_open_faces(box, f), f)
+    assert np.any(f != plain)
+
+
 # ------------------------------------------------ P5 / P6 streaming exactness
 
 def _brute_stream(box, f, mask):
