@@ -33,6 +33,7 @@ METRIC = "MLUPS (million lattice updates/s) and % of HBM roofline, D3Q19 fp32, 1
 
 
 def workload(name):
+    import numpy as np
     import lbm_inputs as li
     if name == "porous256":
         mask, ns = li.porous_mask(256)
@@ -52,6 +53,16 @@ def workload(name):
     if name == "channel_f64":
         return dict(shape=(64, 64, 256), periodic=(1, 0, 1), tau=0.9, force=(0.0, 0.0, 1e-6), mask=None,
                     rho=None, u=None, precision="f64", extra={})
+    if name == "karman":
+        # open channel along x: reservoirs at equilibrium (rho 1, u 0.05 along x)
+        # on both x faces, walls in y, periodic z; a cylinder of radius 20 a
+        # quarter-cell off the centre line, Re = u D / nu = 100 (tau 0.56)
+        nx, ny, nz = 768, 192, 96
+        u_in = (0.05, 0.0, 0.0)
+        return dict(shape=(nx, ny, nz), periodic=(0, 0, 1), tau=0.56, force=(0.0, 0.0, 0.0),
+                    mask=li.cylinder_mask(nx, ny, nz, 2 * 160, 2 * 96 + 1, 20), rho=None,
+                    u=np.tile(np.array(u_in, np.float32)[:, None], (1, nx * ny * nz)), precision="f32",
+                    open_faces={"-x": (1.0, u_in), "+x": (1.0, u_in)}, extra={})
     if name == "periodic256_mask0":
         import numpy as np
         return dict(shape=(256, 256, 256), periodic=(1, 1, 1), tau=0.65, force=(1e-6, 0.0, 0.0),
@@ -93,7 +104,8 @@ def cpu_baseline(wl, steps=3):
     """Time the single-threaded fp64 oracle on a few steps of the same box."""
     import numpy as np
     import oracle
-    box = oracle.Box(*wl["shape"], periodic=wl["periodic"], tau=wl["tau"], force=wl["force"])
+    box = oracle.Box(*wl["shape"], periodic=wl["periodic"], tau=wl["tau"], force=wl["force"],
+                     open_faces=wl.get("open_faces"))
     f = oracle.init_equilibrium(box, wl["mask"], wl["rho"], wl["u"])
     t0 = time.perf_counter()
     f = oracle.run(box, f, steps, wl["mask"])
@@ -149,6 +161,8 @@ def main():
     lat = Lattice(*shape, precision=prec, layout=args.layout, scheme=args.scheme, tau=wl["tau"],
                   force=wl["force"])
     lat.set_geometry(None if mask is None else torch.from_numpy(mask), wl["periodic"])
+    if wl.get("open_faces"):
+        lat.set_open_faces(wl["open_faces"])
     lat.init(None if wl["rho"] is None else torch.from_numpy(wl["rho"]),
              None if wl["u"] is None else torch.from_numpy(wl["u"]))
     stream = lat.stream

@@ -135,6 +135,26 @@ lbm_status lbm_set_workspace(lbm_sim *sim, void *ws, size_t bytes);
  * Invalidates the state: lbm_init_equilibrium must be called again.  Host only. */
 lbm_status lbm_set_geometry(lbm_sim *sim, const uint8_t *mask, const int32_t periodic[3]);
 
+/* Open faces (PortLBM page, section 3.1: the inlet takes the equilibrium
+ * distribution of Dirichlet values; here every open face does).  Faces are
+ * numbered -x, +x, -y, +y, -z, +z.  open[k] = 1 replaces the wall beyond face
+ * k, whose axis must be non-periodic, by a reservoir at equilibrium: every
+ * population entering the box through face k is feq(rho[k], u[3k..3k+2]) (the
+ * second-order equilibrium of the collision), and populations leaving through
+ * it are dropped.  Where a link crosses two faces (an edge of the box), a wall
+ * wins over an open face, and of two open faces the one on the first axis in
+ * x, y, z order is used.  The entering populations of the state are always the
+ * reservoir's: lbm_init_equilibrium and lbm_write_populations store them
+ * whatever the inputs hold there.  Bounce-back links to solid cells and walls
+ * are unchanged; links through open faces carry no momentum-exchange force.
+ *   open   host int32[6], 0 or 1.
+ *   rho    host double[6] (> 0 where open), u host double[18]; read only
+ *          where open[k] = 1 (may be NULL when no face is open).
+ * lbm_set_geometry resets all faces to closed.  Invalidates the state.
+ * LBM_ERR_INVALID_ARGUMENT for an open face on a periodic axis or a
+ * non-finite or non-positive reservoir.  Host only. */
+lbm_status lbm_set_open_faces(lbm_sim *sim, const int32_t open[6], const double rho[6], const double u[18]);
+
 /* f(0) = equilibrium(rho, u) on fluid cells, 0 on solid cells; t := 0.
  *   rho   device T[N] or NULL (rho = 1).
  *   u     device T[3][N] (component-major) or NULL (u = 0).

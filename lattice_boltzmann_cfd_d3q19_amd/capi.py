@@ -26,7 +26,8 @@ LBM_SCHEME_AB, LBM_SCHEME_AA = 0, 1
 EXPORTED = ["lbm_buffer_bytes", "lbm_workspace_bytes", "lbm_create", "lbm_set_workspace", "lbm_set_geometry", "lbm_init_equilibrium", "lbm_step",
             "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_save_state",
             "lbm_load_state", "lbm_destroy", "lbm_time", "lbm_fluid_cells", "lbm_last_hip_error",
-            "lbm_status_string", "lbm_momentum_exchange_scratch_bytes", "lbm_momentum_exchange"]
+            "lbm_status_string", "lbm_momentum_exchange_scratch_bytes", "lbm_momentum_exchange",
+            "lbm_set_open_faces"]
 
 
 class lbm_desc(ctypes.Structure):
@@ -70,6 +71,9 @@ _lib.lbm_create.argtypes = [_Desc_p, _vp, _vp, _vp, ctypes.POINTER(_vp)]
 _lib.lbm_create.restype = _st
 _lib.lbm_set_geometry.argtypes = [_vp, _vp, ctypes.POINTER(_i32)]
 _lib.lbm_set_geometry.restype = _st
+_lib.lbm_set_open_faces.argtypes = [_vp, ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double)]
+_lib.lbm_set_open_faces.restype = _st
 _lib.lbm_init_equilibrium.argtypes = [_vp, _vp, _vp]
 _lib.lbm_init_equilibrium.restype = _st
 _lib.lbm_step.argtypes = [_vp, _i64]
@@ -154,6 +158,23 @@ def lbm_create(desc, buf0, buf1=None, stream=None):
 def lbm_set_geometry(sim, mask, periodic):
     per = None if periodic is None else (_i32 * 3)(*[int(p) for p in periodic])
     return _lib.lbm_set_geometry(sim, _ptr(mask), per)
+
+
+FACES = ("-x", "+x", "-y", "+y", "-z", "+z")
+
+
+def lbm_set_open_faces(sim, faces):
+    """faces: {face name: (rho, (ux, uy, uz))}; faces not named are closed."""
+    op = (_i32 * 6)()
+    rho = (ctypes.c_double * 6)(*([1.0] * 6))
+    u = (ctypes.c_double * 18)()
+    for k, (r, v) in faces.items():
+        i = FACES.index(k)
+        op[i] = 1
+        rho[i] = float(r)
+        for a in range(3):
+            u[3 * i + a] = float(v[a])
+    return _lib.lbm_set_open_faces(sim, op, rho, u)
 
 
 def lbm_init_equilibrium(sim, rho=None, u=None):

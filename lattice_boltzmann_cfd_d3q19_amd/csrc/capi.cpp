@@ -38,6 +38,9 @@ struct lbm_sim {
     int cur;  // AB: index of the buffer holding h(t)
     double omega;
     hipError_t last_hip;  // status of the last failed launch (hipSuccess if none)
+    uint32_t open;        // open faces (bit k: -x, +x, -y, +y, -z, +z)
+    double face_rho[6];
+    double face_u[6][3];
 };
 
 namespace {
@@ -94,6 +97,7 @@ lbm::LaunchGeom geom_of(const lbm_sim* s)
     g.ny = s->d.ny;
     g.nz = s->d.nz;
     for (int a = 0; a < 3; ++a) g.periodic[a] = s->periodic[a];
+    g.open = s->open;
     g.mask = s->mask;
     return g;
 }
@@ -106,6 +110,10 @@ lbm::LaunchPhys phys_of(const lbm_sim* s)
     for (int a = 0; a < 3; ++a) {
         p.force[a] = s->d.force[a];
         if (s->d.force[a] != 0.0) p.has_force = true;
+    }
+    for (int k = 0; k < 6; ++k) {
+        p.face_rho[k] = s->face_rho[k];
+        for (int a = 0; a < 3; ++a) p.face_u[k][a] = s->face_u[k][a];
     }
     return p;
 }
@@ -253,6 +261,32 @@ lbm_status lbm_set_geometry(lbm_sim* sim, const uint8_t* mask, const int32_t per
         if (periodic[a] != 0 && periodic[a] != 1) return LBM_ERR_INVALID_ARGUMENT;
     sim->mask = mask;
     for (int a = 0; a < 3; ++a) sim->periodic[a] = periodic[a];
+    sim->open = 0;
+    sim->initialized = false;
+    sim->t = 0;
+    sim->cur = 0;
+    return LBM_OK;
+}
+
+lbm_status lbm_set_open_faces(lbm_sim* sim, const int32_t open[6], const double rho[6], const double u[18])
+{
+    if (sim == nullptr || open == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    uint32_t bits = 0;
+    for (int k = 0; k < 6; ++k) {
+        if (open[k] != 0 && open[k] != 1) return LBM_ERR_INVALID_ARGUMENT;
+        if (!open[k]) continue;
+        if (sim->periodic[k / 2] || rho == nullptr || u == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+        if (!std::isfinite(rho[k]) || !(rho[k] > 0.0)) return LBM_ERR_INVALID_ARGUMENT;
+        for (int a = 0; a < 3; ++a)
+            if (!std::isfinite(u[3 * k + a])) return LBM_ERR_INVALID_ARGUMENT;
+        bits |= 1u << k;
+    }
+    sim->open = bits;
+    for (int k = 0; k < 6; ++k) {
+        const bool o = (bits >> k) & 1u;
+        sim->face_rho[k] = o ? rho[k] : 1.0;
+        for (int a = 0; a < 3; ++a) sim->face_u[k][a] = o ? u[3 * k + a] : 0.0;
+    }
     sim->initialized = false;
     sim->t = 0;
     sim->cur = 0;

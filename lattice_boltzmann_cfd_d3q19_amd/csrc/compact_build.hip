@@ -96,11 +96,11 @@ __global__ void __launch_bounds__(kBlockThreads) compact_fill_rows(const uint8_t
     }
 }
 
-// Halo of idxp: periodic image, or kWall beyond a non-periodic face.
+// Halo of idxp: periodic image, kWall beyond a wall face, kOpen + k beyond open face k.
 __global__ void __launch_bounds__(kBlockThreads) compact_fill_halo(uint32_t nx, uint32_t ny, uint32_t nz,
                                                                    uint32_t per_x, uint32_t per_y, uint32_t per_z,
-                                                                   uint32_t px, uint32_t pxy, uint64_t npad,
-                                                                   uint32_t* __restrict__ idxp)
+                                                                   uint32_t open, uint32_t px, uint32_t pxy,
+                                                                   uint64_t npad, uint32_t* __restrict__ idxp)
 {
     const uint64_t p = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
     if (p >= npad) return;
@@ -110,8 +110,23 @@ __global__ void __launch_bounds__(kBlockThreads) compact_fill_halo(uint32_t nx, 
     const int32_t gz = (int32_t)(pp / pxy) - 1;
     const bool ox = gx < 0 || gx >= (int32_t)nx, oy = gy < 0 || gy >= (int32_t)ny, oz = gz < 0 || gz >= (int32_t)nz;
     if (!ox && !oy && !oz) return;  // interior: filled per row
-    if ((ox && !per_x) || (oy && !per_y) || (oz && !per_z)) {
-        idxp[pp] = kWall;
+    // beyond a non-periodic face: a wall wins over an open face; of two open
+    // faces, the one on the first axis in x, y, z order
+    const bool out[3] = {ox && !per_x, oy && !per_y, oz && !per_z};
+    const int32_t gc[3] = {gx, gy, gz};
+    bool wall = false;
+    int face = -1;
+    for (int a = 0; a < 3; ++a) {
+        if (!out[a]) continue;
+        const int k = 2 * a + (gc[a] < 0 ? 0 : 1);
+        if ((open >> k) & 1u) {
+            if (face < 0) face = k;
+        } else {
+            wall = true;
+        }
+    }
+    if (wall || face >= 0) {
+        idxp[pp] = wall ? kWall : kOpen + (uint32_t)face;
         return;
     }
     const uint32_t ix = (uint32_t)((gx + (int32_t)nx) % (int32_t)nx);
@@ -148,7 +163,8 @@ hipError_t launch_compact_build(const LaunchGeom& lg, const CompactTables& t, hi
                        (const uint32_t*)t.rows, t.idxp, t.cellp);
     hipLaunchKernelGGL(compact_fill_halo, dim3((uint32_t)((npad + kBlockThreads - 1) / kBlockThreads)),
                        dim3(kBlockThreads), 0, st, nx, ny, nz, (uint32_t)(lg.periodic[0] != 0),
-                       (uint32_t)(lg.periodic[1] != 0), (uint32_t)(lg.periodic[2] != 0), px, pxy, npad, t.idxp);
+                       (uint32_t)(lg.periodic[1] != 0), (uint32_t)(lg.periodic[2] != 0), lg.open, px, pxy, npad,
+                       t.idxp);
     return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ struct Geom {
     uint32_t per_x, per_y, per_z;  // 1 = periodic, 0 = bounce-back wall beyond both faces
     uint32_t ntx, nty, ntiles;     // tiles per x-row of tiles, per y-column, total
     uint32_t xk;                   // workgroup chunk per XCD turn (1 = hardware order)
+    uint32_t open;                 // bit k: face k (-x, +x, -y, +y, -z, +z) is open
     uint64_t n;                    // cells
     const uint8_t* mask;           // uint8[n], nonzero = solid; may be null
 };
@@ -55,6 +56,9 @@ struct Phys {
     T hfx, hfy, hfz;  // F / 2
     T gev[9], god[9];
     T gu[3];  // [0] rest, [1] axis (w = 1/18), [2] diagonal (w = 1/36)
+    // Open faces: the shifted equilibrium feq_q(rho_k, u_k) - w_q of face k's
+    // reservoir, the value of every population entering through face k.
+    T seq[6][kQ];
 };
 
 // State transfers: canonical populations f out / in, moments out, equilibrium
@@ -126,7 +130,8 @@ __device__ __forceinline__ void st_pop(T* p, T v)
 struct Cell {
     uint32_t x, y, z, id;
     uint32_t ox[3], oy[3], oz[3];  // wrapped neighbour coordinates as index offsets
-    bool wall[3][2];               // beyond the low / high face on a non-periodic axis
+    bool wall[3][2];               // at the low / high face of a non-periodic axis, beyond it a wall
+    bool open[3][2];               // ... beyond it an open face
 };
 
 // Workgroup w runs on XCD w % 8 (the dispatcher deals workgroups out round
@@ -164,12 +169,17 @@ __device__ __forceinline__ bool locate(const Geom& g, Cell& c)
     c.oz[0] = zm * g.nxy;
     c.oz[1] = c.z * g.nxy;
     c.oz[2] = zp * g.nxy;
-    c.wall[0][0] = !g.per_x && c.x == 0;
-    c.wall[0][1] = !g.per_x && c.x + 1 == g.nx;
-    c.wall[1][0] = !g.per_y && c.y == 0;
-    c.wall[1][1] = !g.per_y && c.y + 1 == g.ny;
-    c.wall[2][0] = !g.per_z && c.z == 0;
-    c.wall[2][1] = !g.per_z && c.z + 1 == g.nz;
+    const bool at[3][2] = {{!g.per_x && c.x == 0, !g.per_x && c.x + 1 == g.nx},
+                           {!g.per_y && c.y == 0, !g.per_y && c.y + 1 == g.ny},
+                           {!g.per_z && c.z == 0, !g.per_z && c.z + 1 == g.nz}};
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int sd = 0; sd < 2; ++sd) {
+            const bool open = (g.open >> (2 * a + sd)) & 1u;
+            c.wall[a][sd] = at[a][sd] && !open;
+            c.open[a][sd] = at[a][sd] && open;
+        }
     return true;
 }
 
@@ -185,9 +195,17 @@ __device__ __forceinline__ bool beyond_wall(const Cell& c, int dx, int dy, int d
            (dy > 0 && c.wall[1][1]) || (dz < 0 && c.wall[2][0]) || (dz > 0 && c.wall[2][1]);
 }
 
+__device__ __forceinline__ bool beyond_open(const Cell& c, int dx, int dy, int dz)
+{
+    return (dx < 0 && c.open[0][0]) || (dx > 0 && c.open[0][1]) || (dy < 0 && c.open[1][0]) ||
+           (dy > 0 && c.open[1][1]) || (dz < 0 && c.open[2][0]) || (dz > 0 && c.open[2][1]);
+}
+
 // Bit q set iff the upstream cell x - c_q is solid or beyond a wall, i.e. the
-// population arriving along c_q is the bounced-back one.
-// The wrapped neighbour index is inside the box even where a wall cuts the
+// population arriving along c_q is the bounced-back one.  A link that leaves
+// through an open face (and no wall) is not bounced back, whatever the
+// wrapped cell on the far side holds.
+// The wrapped neighbour index is inside the box even where a face cuts the
 // link, so its mask byte is read unconditionally (one uniform test for the
 // mask pointer, no per-lane branch around the 18 loads).
 template <bool BND>
@@ -202,13 +220,80 @@ __device__ __forceinline__ uint32_t link_bits(const Geom& g, const Cell& c)
                 if (q != 9) m[q] = g.mask[nbr(c, -kCx[q], -kCy[q], -kCz[q])];
 #pragma unroll
             for (int q = 0; q < kQ; ++q)
-                if (q != 9) bits |= (uint32_t)(m[q] != 0) << q;
+                if (q != 9)
+                    bits |= (uint32_t)(m[q] != 0 && !beyond_open(c, -kCx[q], -kCy[q], -kCz[q])) << q;
         }
 #pragma unroll
         for (int q = 0; q < kQ; ++q)
             if (q != 9) bits |= (uint32_t)beyond_wall(c, -kCx[q], -kCy[q], -kCz[q]) << q;
     }
     return bits;
+}
+
+// Bit q set iff the population arriving along c_q enters through an open face
+// (x - c_q beyond an open face and beyond no wall).
+__device__ __forceinline__ uint32_t open_bits(const Geom& g, const Cell& c)
+{
+    uint32_t bits = 0;
+    if (g.open != 0) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q)
+            if (q != 9)
+                bits |= (uint32_t)(beyond_open(c, -kCx[q], -kCy[q], -kCz[q]) &&
+                                   !beyond_wall(c, -kCx[q], -kCy[q], -kCz[q]))
+                        << q;
+    }
+    return bits;
+}
+
+// The faces through which population q can enter a cell: x - c_q lies beyond
+// the low face of axis a when c_q[a] > 0, beyond the high face when c_q[a] <
+// 0.  f0 is on the first axis with c_q[a] != 0 (x, y, z order), f1 on the
+// second (-1 if c_q has one nonzero component).  Where both are open, f0 is
+// used.
+template <int q>
+struct Entering {
+    static constexpr int a0 = kCx[q] != 0 ? 0 : kCy[q] != 0 ? 1 : 2;
+    static constexpr int a1 = (a0 < 1 && kCy[q] != 0) ? 1 : (a0 < 2 && kCz[q] != 0) ? 2 : -1;
+    static constexpr int c0 = a0 == 0 ? kCx[q] : a0 == 1 ? kCy[q] : kCz[q];
+    static constexpr int c1 = a1 == 1 ? kCy[q] : a1 == 2 ? kCz[q] : 0;
+    static constexpr int side0 = c0 > 0 ? 0 : 1;
+    static constexpr int f0 = 2 * a0 + side0;
+    static constexpr int f1 = a1 < 0 ? -1 : 2 * a1 + (c1 > 0 ? 0 : 1);
+};
+
+// The reservoir value of population q entering c (stored, shifted form).
+template <int q, typename T>
+__device__ __forceinline__ T entering_value(const Phys<T>& p, const Cell& c)
+{
+    using E = Entering<q>;
+    if constexpr (E::f1 < 0) {
+        return p.seq[E::f0][q];
+    } else {
+        return c.open[E::a0][E::side0] ? p.seq[E::f0][q] : p.seq[E::f1][q];
+    }
+}
+
+// Odd in-place step: where x + c_q lies beyond an open face, f*_q leaves the
+// box and the slot it would have taken, the own slot (opp q, x), receives the
+// reservoir's population entering along -c_q: f[q] := that value.
+template <int q = 0, typename T>
+__device__ __forceinline__ void open_outflow(T (&f)[kQ], uint32_t obits, const Phys<T>& p, const Cell& c)
+{
+    if constexpr (q < kQ) {
+        if constexpr (q != 9) f[q] = ((obits >> opp(q)) & 1u) ? entering_value<opp(q)>(p, c) : f[q];
+        open_outflow<q + 1>(f, obits, p, c);
+    }
+}
+
+// f[q] := the reservoir value where population q enters through an open face.
+template <int q = 0, typename T>
+__device__ __forceinline__ void apply_open(T (&f)[kQ], uint32_t obits, const Phys<T>& p, const Cell& c)
+{
+    if constexpr (q < kQ) {
+        if constexpr (q != 9) f[q] = ((obits >> q) & 1u) ? entering_value<q>(p, c) : f[q];
+        apply_open<q + 1>(f, obits, p, c);
+    }
 }
 
 // ------------------------------------------------------------- collision
@@ -479,8 +564,10 @@ __device__ __forceinline__ T* state_slot(T* buf, uint64_t n, const Cell& c, uint
 constexpr int kBlockThreads = 256;
 
 // One fused time step.  K: kAB (a = source, b = destination), kAAEven or
-// kAAOdd (a = the single lattice).  BND: a mask or a wall exists.
-template <typename T, int L, int K, bool BND, bool FORCE>
+// kAAOdd (a = the single lattice).  BND: 0 = fully periodic, no mask;
+// 1 = a mask or a wall exists; 2 = also open faces (a separate instance, so
+// the reservoir selects cost the other kernels no registers).
+template <typename T, int L, int K, int BND, bool FORCE>
 __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, T* __restrict__ b,
                                                              Geom g, Phys<T> p)
 {
@@ -489,7 +576,8 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
     if constexpr (BND) {
         if (g.mask != nullptr && g.mask[c.id] != 0) return;  // solid cells are never updated
     }
-    const uint32_t bits = link_bits<BND>(g, c);
+    const uint32_t bits = link_bits<BND != 0>(g, c);
+    const uint32_t obits = BND == 2 ? open_bits(g, c) : 0u;  // populations entering through open faces
     const uint64_t n = g.n;
 
     T f[kQ];
@@ -503,8 +591,12 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
             f[q] = ld_pop(state_slot<kAAOdd, L>(a, n, c, bits, q));
         }
     }
+    // the even step's natural slots already hold the reservoir values (the odd
+    // step and the initialisation put them there); the gathers take them here
+    if constexpr (BND == 2 && K != kAAEven) apply_open(f, obits, p, c);
 
     collide<T, FORCE>(f, p);
+    if constexpr (BND == 2 && K == kAAOdd) open_outflow(f, obits, p, c);
 
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
@@ -514,11 +606,14 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
             st_pop(slot<L>(a, n, opp(q), c.id), f[q]);
         } else {
             // toward x + c_q, or straight back into (opp q, x) if that cell is
-            // solid or beyond a wall (its upstream bit for opp q is set)
-            const bool bb = (bits >> opp(q)) & 1u;
+            // solid or beyond a wall (its upstream bit for opp q is set); if
+            // x + c_q lies beyond an open face, f*_q leaves the box and (opp q,
+            // x) receives the reservoir's population entering along -c_q
+            // (the reservoir values were put into f by open_outflow above)
+            const bool own_slot = ((bits | obits) >> opp(q)) & 1u;
             const uint64_t own = slot_off<L>(n, opp(q), c.id);
             const uint64_t far = slot_off<L>(n, q, nbr(c, kCx[q], kCy[q], kCz[q]));
-            st_pop(a + (bb ? own : far), f[q]);
+            st_pop(a + (own_slot ? own : far), f[q]);
         }
     }
 }
@@ -555,10 +650,12 @@ __global__ void __launch_bounds__(kBlockThreads) io_kernel(T* __restrict__ a, T*
         return;
     }
     const uint32_t bits = link_bits<true>(g, c);
+    const uint32_t obits = open_bits(g, c);
     T f[kQ];
     if constexpr (OP == kReadF || OP == kReadMoments || OP == kReadS) {
 #pragma unroll
         for (int q = 0; q < kQ; ++q) f[q] = *state_slot<S, L>(a, n, c, bits, q);
+        if constexpr (S != kAAEven) apply_open(f, obits, p, c);
         if constexpr (OP == kReadF) {
 #pragma unroll
             for (int q = 0; q < kQ; ++q) out0[(uint64_t)q * n + c.id] = f[q] + wq<T>(q);
@@ -590,8 +687,15 @@ __global__ void __launch_bounds__(kBlockThreads) io_kernel(T* __restrict__ a, T*
             }
             shifted_equilibrium(rho, ux, uy, uz, f);
         }
+        // populations entering through an open face are the reservoir's: the
+        // even state stores them in their natural slots, the others have no
+        // slot for them (their map would point across the box)
+        if constexpr (S == kAAEven) apply_open(f, obits, p, c);
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) *state_slot<S, L>(a, n, c, bits, q) = f[q];
+        for (int q = 0; q < kQ; ++q) {
+            if (S != kAAEven && ((obits >> q) & 1u)) continue;
+            *state_slot<S, L>(a, n, c, bits, q) = f[q];
+        }
     }
 }
 

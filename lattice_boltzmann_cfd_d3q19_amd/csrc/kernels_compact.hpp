@@ -12,8 +12,8 @@
 //   idxp[p]   for every cell of the box padded by one halo layer on each side,
 //             p = (x+1) + px ((y+1) + py (z+1)), px = nx+2, py = ny+2: the
 //             compact index of the cell, kInvalid for solid cells; halo cells
-//             hold the index of their periodic image, or kWall beyond a
-//             non-periodic face (halfway bounce-back walls).
+//             hold the index of their periodic image, kWall beyond a wall
+//             face (halfway bounce-back) or kOpen + k beyond open face k.
 //   cellp[i]  padded id p of the i-th fluid cell.
 // A neighbour along c_d is then idxp[cellp[i] + off_d] with
 // off_d = c_x + px (c_y + py c_z): no coordinates, no wrap logic.
@@ -28,8 +28,35 @@ namespace lbm {
 // kernels; the momentum exchange tells them apart.
 constexpr uint32_t kInvalid = 0xFFFFFFFFu;
 constexpr uint32_t kWall = 0xFFFFFFFEu;
+// halo beyond open face k (-x, +x, -y, +y, -z, +z): kOpen + k
+constexpr uint32_t kOpen = 0xFFFFFFF0u;
 
-__device__ __forceinline__ bool no_fluid(uint32_t nbv) { return nbv >= kWall; }
+__device__ __forceinline__ bool no_fluid(uint32_t nbv) { return nbv >= kOpen; }
+__device__ __forceinline__ bool bounced(uint32_t nbv) { return nbv >= kWall; }
+__device__ __forceinline__ bool is_open(uint32_t nbv) { return nbv >= kOpen && nbv < kWall; }
+
+// Reservoir value of population q entering through the open face that the
+// table entry nbv (of the upstream cell x - c_q) names.
+template <int q, typename T>
+__device__ __forceinline__ T entering_value_nb(const Phys<T>& p, uint32_t nbv)
+{
+    using E = Entering<q>;
+    if constexpr (E::f1 < 0) {
+        return p.seq[E::f0][q];
+    } else {
+        return nbv == kOpen + (uint32_t)E::f0 ? p.seq[E::f0][q] : p.seq[E::f1][q];
+    }
+}
+
+// f[q] := the reservoir value where the upstream entry nb[opp q] is open.
+template <int q = 0, typename T>
+__device__ __forceinline__ void apply_open_nb(T (&f)[kQ], const uint32_t (&nb)[kQ], const Phys<T>& p)
+{
+    if constexpr (q < kQ) {
+        if constexpr (q != 9) f[q] = is_open(nb[opp(q)]) ? entering_value_nb<q>(p, nb[opp(q)]) : f[q];
+        apply_open_nb<q + 1>(f, nb, p);
+    }
+}
 
 // Workgroup sizes of the compact step kernels.  Measured on the porous
 // boxes: 512-thread gathers 0.5% (256^3) and 1.2% (512^3) faster than 256,
@@ -51,6 +78,7 @@ struct CompactGeom {
     uint32_t pxy;  // (nx + 2)(ny + 2)
     uint32_t s;    // population stride (fluid cells rounded up to 64); 2 s sizeof(T) < 2^32
     uint32_t xk;   // workgroup chunk per XCD turn of the gather kernels (1 = hardware order)
+    uint32_t open; // bit k: face k is open (some table entries are kOpen + k)
 };
 
 // Compact indices of the 18 neighbours x + c_d (kInvalid: solid, kWall: wall),
@@ -167,6 +195,18 @@ __device__ __forceinline__ void st_at(char* blk, uint32_t off, T v)
     }
 }
 
+// Odd step: for each direction d whose neighbour entry is an open face, the
+// value written to d's slot (the own slot (opp d, x)) is the reservoir's
+// population entering along -c_d instead of f*_d.
+template <int d = 0, typename T>
+__device__ __forceinline__ void open_outflow(T (&f)[kQ], const uint32_t (&nb)[kQ], const Phys<T>& p)
+{
+    if constexpr (d < kQ) {
+        if constexpr (d != 9) f[d] = is_open(nb[d]) ? entering_value_nb<opp(d)>(p, nb[d]) : f[d];
+        open_outflow<d + 1>(f, nb, p);
+    }
+}
+
 // Byte offset, inside the block of pair(d), of the slot that direction d
 // of fluid cell i owns in the in-place odd step and in the pull's gather:
 // sub-plane `sv` at the neighbour's index `nbv` if that neighbour is fluid,
@@ -198,8 +238,10 @@ __device__ __forceinline__ char* pair_block(char* base, int k, uint32_t plane_by
 
 // Gather step over the fluid cells, one work-item per fluid cell: the
 // two-lattice fused pull (K = kAB, a = source, b = destination) or the odd
-// step of the in-place pattern (K = kAAOdd, a = the lattice).
-template <typename T, int K, bool FORCE>
+// step of the in-place pattern (K = kAAOdd, a = the lattice).  OPEN: some
+// faces are open (a separate instance: the reservoir selects would cost the
+// other cases registers).
+template <typename T, int K, bool FORCE, bool OPEN>
 __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restrict__ a, T* __restrict__ b,
                                                                      CompactGeom g, Phys<T> p)
 {
@@ -216,13 +258,15 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
     neighbours_rows(g, g.cellp[i], nb);
     T f[kQ];
     if constexpr (K == kAB) {
-        // f_q = src[q][x - c_q], or src[opp q][x] if x - c_q is solid
+        // f_q = src[q][x - c_q], or src[opp q][x] if x - c_q is solid, or the
+        // reservoir's value if x - c_q lies beyond an open face
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
             const uint32_t off = q == 9 ? own0
                                         : link_off<T>(nb[opp(q)], sub_of(q) ? sb : 0u, sub_of(opp(q)) ? own1 : own0);
             f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), off);
         }
+        if constexpr (OPEN) apply_open_nb(f, nb, p);
         collide<T, FORCE>(f, p);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(B, pair_of(q), sb), sub_of(q) ? own1 : own0, f[q]);
@@ -235,7 +279,11 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
             off[d] = d == 9 ? own0 : link_off<T>(nb[d], sub_of(d) ? sb : 0u, sub_of(opp(d)) ? own1 : own0);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), off[opp(q)]);
+        if constexpr (OPEN) apply_open_nb(f, nb, p);
         collide<T, FORCE>(f, p);
+        // beyond an open face, f*_d leaves the box and the own slot (opp d, x)
+        // takes the reservoir's population entering along -c_d
+        if constexpr (OPEN) open_outflow(f, nb, p);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<false>(pair_block(A, pair_of(q), sb), off[q], f[q]);
     }
@@ -296,6 +344,8 @@ __global__ void __launch_bounds__(kBlockThreads) io_compact_kernel(T* __restrict
     if constexpr (OP == kReadF || OP == kReadMoments || OP == kReadS) {
 #pragma unroll
         for (int q = 0; q < kQ; ++q) f[q] = *compact_state_slot<S>(a, s, i, nb, q);
+        if constexpr (S != kAAEven)
+            if (cg.open) apply_open_nb(f, nb, p);
         if constexpr (OP == kReadF) {
 #pragma unroll
             for (int q = 0; q < kQ; ++q) out0[(uint64_t)q * n + c.id] = f[q] + wq<T>(q);
@@ -327,8 +377,15 @@ __global__ void __launch_bounds__(kBlockThreads) io_compact_kernel(T* __restrict
             }
             shifted_equilibrium(rho, ux, uy, uz, f);
         }
+        // populations entering through an open face are the reservoir's: the
+        // even state keeps them in their natural slots, the others have none
+        if constexpr (S == kAAEven)
+            if (cg.open) apply_open_nb(f, nb, p);
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) *compact_state_slot<S>(a, s, i, nb, q) = f[q];
+        for (int q = 0; q < kQ; ++q) {
+            if (S != kAAEven && is_open(nb[opp(q)])) continue;
+            *compact_state_slot<S>(a, s, i, nb, q) = f[q];
+        }
     }
 }
 

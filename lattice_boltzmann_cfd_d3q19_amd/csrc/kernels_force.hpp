@@ -87,6 +87,7 @@ __global__ void __launch_bounds__(kBlockThreads) mex_kernel(T* __restrict__ a, G
         T s[kQ];
 #pragma unroll
         for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g.n, c, bits, q);
+        if constexpr (S != kAAEven) apply_open(s, open_bits(g, c), p, c);
         collide<T, true>(s, p);
         // x + c_q is solid or beyond a wall iff the upstream bit of opp(q) is set
         add_links(acc, s, c, [&](int q) { return ((bits >> opp(q)) & 1u) != 0; });
@@ -98,14 +99,15 @@ template <int q = 0, typename T>
 __device__ __forceinline__ void add_links_nb(double (&acc)[6], const T (&s)[kQ], const uint32_t (&nb)[kQ])
 {
     if constexpr (q < kQ) {
-        if constexpr (q != 9) add_link<q>(acc, s[q], no_fluid(nb[q]), nb[q] == kWall);
+        if constexpr (q != 9) add_link<q>(acc, s[q], bounced(nb[q]), nb[q] == kWall);
         add_links_nb<q + 1>(acc, s, nb);
     }
 }
 
 // Compact layout: one work-item per fluid cell, the gathers of the step
 // kernels (row-wise neighbour reads, the same slot maps), one partial row per
-// workgroup.  The index table marks wall links (kWall) apart from solid ones.
+// workgroup.  The index table marks wall links (kWall) apart from solid ones
+// (kInvalid) and from open faces (kOpen + k, which carry no force).
 template <typename T, int S>
 __global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restrict__ a, CompactGeom g, Phys<T> p,
                                                                     double* __restrict__ partial)
@@ -132,6 +134,8 @@ __global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restric
             }
             f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), off);
         }
+        if constexpr (S != kAAEven)
+            if (g.open) apply_open_nb(f, nb, p);
         collide<T, true>(f, p);
         add_links_nb(acc, f, nb);
     }

@@ -9,6 +9,7 @@ namespace lbm {
 struct LaunchGeom {
     int64_t nx, ny, nz;
     int32_t periodic[3];
+    uint32_t open;  // bit k: face k (-x, +x, -y, +y, -z, +z) is open (its axis is not periodic)
     const uint8_t* mask;
 };
 
@@ -16,6 +17,8 @@ struct LaunchPhys {
     double omega;
     double force[3];
     bool has_force;
+    double face_rho[6];     // reservoir of each open face
+    double face_u[6][3];
 };
 
 // One fused step of kind `kind` (kAB: a = source, b = destination; kAAEven /

@@ -31,6 +31,7 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
     g.per_x = lg.periodic[0] != 0;
     g.per_y = lg.periodic[1] != 0;
     g.per_z = lg.periodic[2] != 0;
+    g.open = lg.open;
     g.ntx = (g.nx + bx - 1) / bx;
     g.nty = (g.ny + by - 1) / by;
     g.ntiles = g.ntx * g.nty * g.nz;
@@ -70,10 +71,23 @@ inline Phys<T> make_phys(const LaunchPhys& lp)
     p.gu[0] = (T)(3.0 * guo / 3.0);
     p.gu[1] = (T)(3.0 * guo / 18.0);
     p.gu[2] = (T)(3.0 * guo / 36.0);
+    // open-face reservoirs: feq(rho_k, u_k) in double, minus the weight as
+    // stored (rounded to T), then rounded once to T
+    for (int k = 0; k < 6; ++k) {
+        const double rho = lp.face_rho[k], *u = lp.face_u[k];
+        const double usq = u[0] * u[0] + u[1] * u[1] + u[2] * u[2];
+        for (int q = 0; q < kQ; ++q) {
+            const double w = kW36[q] / 36.0;
+            const double cu = kCx[q] * u[0] + kCy[q] * u[1] + kCz[q] * u[2];
+            const double feq = w * rho * (1.0 + 3.0 * cu + 4.5 * cu * cu - 1.5 * usq);
+            const T wt = kW36[q] == 12 ? T(1) / T(3) : kW36[q] == 2 ? T(1) / T(18) : T(1) / T(36);
+            p.seq[k][q] = (T)(feq - (double)wt);
+        }
+    }
     return p;
 }
 
-template <typename T, int L, int K, bool BND, bool FORCE>
+template <typename T, int L, int K, int BND, bool FORCE>
 hipError_t launch_step_t(T* a, T* b, const Shape& s, const Phys<T>& p, hipStream_t st)
 {
     Geom g = s.g;
@@ -84,17 +98,20 @@ hipError_t launch_step_t(T* a, T* b, const Shape& s, const Phys<T>& p, hipStream
 }
 
 template <typename T, int L, int K>
-hipError_t launch_step_k(T* a, T* b, const Shape& s, const Phys<T>& p, bool bnd, bool force, hipStream_t st)
+hipError_t launch_step_k(T* a, T* b, const Shape& s, const Phys<T>& p, int bnd, bool force, hipStream_t st)
 {
-    if (bnd)
-        return force ? launch_step_t<T, L, K, true, true>(a, b, s, p, st)
-                     : launch_step_t<T, L, K, true, false>(a, b, s, p, st);
-    return force ? launch_step_t<T, L, K, false, true>(a, b, s, p, st)
-                 : launch_step_t<T, L, K, false, false>(a, b, s, p, st);
+    if (bnd == 2)
+        return force ? launch_step_t<T, L, K, 2, true>(a, b, s, p, st)
+                     : launch_step_t<T, L, K, 2, false>(a, b, s, p, st);
+    if (bnd == 1)
+        return force ? launch_step_t<T, L, K, 1, true>(a, b, s, p, st)
+                     : launch_step_t<T, L, K, 1, false>(a, b, s, p, st);
+    return force ? launch_step_t<T, L, K, 0, true>(a, b, s, p, st)
+                 : launch_step_t<T, L, K, 0, false>(a, b, s, p, st);
 }
 
 template <typename T, int L>
-hipError_t launch_step_l(int kind, T* a, T* b, const Shape& s, const Phys<T>& p, bool bnd, bool force,
+hipError_t launch_step_l(int kind, T* a, T* b, const Shape& s, const Phys<T>& p, int bnd, bool force,
                          hipStream_t st)
 {
     switch (kind) {
@@ -114,7 +131,7 @@ hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, c
     // 0.92 -> 0.78 ms; stream AA +8% / +2% and AB +7%, bundle within 2%.
     const Shape s = make_shape(lg, layout == kCollision);
     const Phys<T> p = make_phys<T>(lp);
-    const bool bnd = lg.mask != nullptr || !lg.periodic[0] || !lg.periodic[1] || !lg.periodic[2];
+    const int bnd = lg.open != 0 ? 2 : (lg.mask != nullptr || !lg.periodic[0] || !lg.periodic[1] || !lg.periodic[2]);
     switch (layout) {
     case kStream: return launch_step_l<T, kStream>(kind, a, b, s, p, bnd, lp.has_force, st);
     case kBundle: return launch_step_l<T, kBundle>(kind, a, b, s, p, bnd, lp.has_force, st);
@@ -185,6 +202,7 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     g.px = (uint32_t)lg.nx + 2;
     g.pxy = (uint32_t)((lg.nx + 2) * (lg.ny + 2));
     g.s = (uint32_t)t.stride;
+    g.open = lg.open;
     // XCD chunk of the gather kernels: an eighth of the workgroups of an
     // average z-plane, so the rows at z +- 1 fall on the same XCD as the
     // rows they are gathered by.  Measured (odd in-place step): 256^3 porous
@@ -205,7 +223,9 @@ hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, hipStream
     uint32_t nwg = (g.nf + kGatherThreads - 1) / kGatherThreads;
     if (g.xk > 1) nwg = (nwg + 8 * g.xk - 1) / (8 * g.xk) * (8 * g.xk);
     const dim3 grid(nwg), block(kGatherThreads);
-    return hipLaunchKernel((const void*)&step_compact_kernel<T, K, FORCE>, grid, block, args, 0, st);
+    const void* k = g.open ? (const void*)&step_compact_kernel<T, K, FORCE, true>
+                           : (const void*)&step_compact_kernel<T, K, FORCE, false>;
+    return hipLaunchKernel(k, grid, block, args, 0, st);
 }
 
 template <typename T, bool FORCE>

@@ -69,6 +69,12 @@ class Lattice:
         capi.check(capi.lbm_set_geometry(self.handle, None if mask is None else mask.data_ptr(), periodic),
                    "lbm_set_geometry")
 
+    def set_open_faces(self, faces):
+        """faces: {"-x" | "+x" | "-y" | "+y" | "-z" | "+z": (rho, (ux, uy, uz))} on
+        non-periodic axes; populations entering through them are the
+        reservoir's equilibrium.  Call after set_geometry, before init."""
+        capi.check(capi.lbm_set_open_faces(self.handle, faces), "lbm_set_open_faces")
+
     def _dev(self, a, shape):
         t = torch.as_tensor(a).to(device=self.device, dtype=self.dtype).contiguous()
         return t.reshape(shape)

@@ -14,11 +14,12 @@ Workloads (box sizes and physics of the five benchmark configurations):
   random_fields    -- 32^3 periodic box, rho = 1 + 0.01 U(-1,1), u_a = 0.05 U(-1,1)
   taylor_green     -- 128^3 Taylor-Green vortex, u0 = 0.04
   sphere_mask      -- 128^3 box, sphere of radius 16 at the box centre
+  cylinder_mask    -- a cylinder along z (the obstacle of the open-channel workload)
   porous_mask      -- 256^3 (and 512^3) overlapping spheres, r ~ U(6, 12)
 """
 from .mt64 import MT19937_64, uniform01
 from .fields import random_fields, taylor_green, shear_wave
-from .geometry import sphere_mask, porous_mask, porous_sphere_count, random_mask
+from .geometry import cylinder_mask, sphere_mask, porous_mask, porous_sphere_count, random_mask
 
 __all__ = ["MT19937_64", "uniform01", "random_fields", "taylor_green", "shear_wave",
-           "sphere_mask", "porous_mask", "porous_sphere_count", "random_mask"]
+           "sphere_mask", "porous_mask", "porous_sphere_count", "random_mask", "cylinder_mask"]

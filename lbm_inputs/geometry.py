@@ -21,6 +21,17 @@ def sphere_mask(nx, ny=None, nz=None, radius=16):
     return (d2 <= r2).astype(np.uint8).reshape(-1)
 
 
+def cylinder_mask(nx, ny, nz, cx2, cy2, radius):
+    """A cylinder along z through the whole box, axis at (cx2 / 2, cy2 / 2) in
+    cell units (half-cell resolution, integers).  A cell is solid iff
+    (2i - cx2)^2 + (2j - cy2)^2 <= (2r)^2."""
+    i = (2 * np.arange(nx, dtype=np.int64) - int(cx2)) ** 2
+    j = (2 * np.arange(ny, dtype=np.int64) - int(cy2)) ** 2
+    d2 = j[:, None] + i[None, :]
+    plane = (d2 <= (2 * int(radius)) ** 2).astype(np.uint8)
+    return np.broadcast_to(plane, (nz, ny, nx)).copy().reshape(-1)
+
+
 def porous_sphere_count(nx, ny=None, nz=None, per_128cube=300):
     """Sphere count that keeps the porosity of `per_128cube` spheres in a 128^3
     box at any box volume: n = 300 * N / 128^3 (2400 at 256^3, 19200 at 512^3)."""

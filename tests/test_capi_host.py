@@ -147,6 +147,23 @@ def test_momentum_exchange_arguments_before_any_launch():
     assert capi.lbm_momentum_exchange(None, FAKE, FAKE, nb) == capi.LBM_ERR_INVALID_ARGUMENT
 
 
+def test_open_faces_arguments():
+    st, h = capi.lbm_create(capi.make_desc(8, 8, 8), FAKE)
+    assert st == capi.LBM_OK
+    try:
+        assert capi.lbm_set_geometry(h, None, (0, 1, 1)) == capi.LBM_OK
+        assert capi.lbm_set_open_faces(h, {"-x": (1.0, (0.01, 0, 0))}) == capi.LBM_OK
+        # faces on the periodic y axis cannot be open
+        assert capi.lbm_set_open_faces(h, {"+y": (1.0, (0, 0, 0))}) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert capi.lbm_set_open_faces(h, {"+x": (0.0, (0, 0, 0))}) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert capi.lbm_set_open_faces(h, {"+x": (1.0, (float("nan"), 0, 0))}) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert capi.lbm_set_open_faces(h, {}) == capi.LBM_OK
+        assert capi.lbm_step(h, 1) == capi.LBM_ERR_BAD_STATE
+    finally:
+        capi.lbm_destroy(h)
+    assert capi.lbm_set_open_faces(None, {}) == capi.LBM_ERR_INVALID_ARGUMENT
+
+
 def test_null_handle_and_status_strings():
     assert capi.lbm_destroy(None) == capi.LBM_OK
     assert capi.lbm_time(None) == -1

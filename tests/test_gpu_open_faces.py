@@ -1,0 +1,90 @@
+"""Open faces (reservoirs at equilibrium) on the GPU against the oracle:
+canonical populations after 100 / 101 steps from the same seeded inputs, every
+layout and scheme, fp32 and fp64, and the uniform-stream fixed point."""
+import numpy as np
+import pytest
+
+import lbm_inputs as li
+import oracle
+from gpu_util import LAYOUTS, SCHEMES, TOL, cast, host_f, make, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _open_case(name):
+    if name == "inlet_outlet":
+        # channel along x: reservoirs on both x faces, walls in y, periodic z,
+        # a sphere in the stream
+        shape, per, tau, F = (30, 18, 14), (0, 0, 1), 0.7, (0.0, 0.0, 0.0)
+        faces = {"-x": (1.0, (0.04, 0.0, 0.0)), "+x": (0.998, (0.04, 0.0, 0.0))}
+        mask = li.sphere_mask(30, 18, 14, radius=4)
+    elif name == "open_edges":
+        # no periodic axis; open -x, +x, -y and +z, walls on +y and -z: edges
+        # where an open face meets a wall or another open face
+        shape, per, tau, F = (17, 15, 13), (0, 0, 0), 0.65, (2e-5, -1e-5, 1e-5)
+        faces = {"-x": (1.01, (0.03, 0.01, 0.0)), "+x": (0.99, (0.02, 0.0, -0.01)),
+                 "-y": (1.0, (0.0, 0.02, 0.01)), "+z": (1.02, (0.01, -0.01, -0.02))}
+        mask = li.random_mask(17, 15, 13, fraction=0.1, seed=9)
+    else:
+        raise KeyError(name)
+    return shape, per, tau, F, faces, mask
+
+
+def _make_open(shape, precision, layout, scheme, tau, F, faces, mask, per, rho, u):
+    from lattice_boltzmann_cfd_d3q19_amd import Lattice
+    import torch
+    lat = Lattice(*shape, precision=precision, layout=layout, scheme=scheme, tau=tau, force=F)
+    lat.set_geometry(None if mask is None else torch.from_numpy(np.ascontiguousarray(mask)), per)
+    lat.set_open_faces(faces)
+    lat.init(torch.from_numpy(np.ascontiguousarray(rho)), torch.from_numpy(np.ascontiguousarray(u)))
+    return lat
+
+
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+@pytest.mark.parametrize("name,nsteps", [("inlet_outlet", 100), ("open_edges", 101)])
+def test_open_faces_all_layouts_schemes(name, nsteps, precision):
+    need_gpu()
+    shape, per, tau, F, faces, mask = _open_case(name)
+    rho, u = li.random_fields(*shape, seed=31)
+    u = 0.5 * u
+    rho, u = cast(rho, precision), cast(u, precision)
+    box = oracle.Box(*shape, periodic=per, tau=tau, force=F, open_faces=faces)
+    f0 = oracle.init_equilibrium(box, mask, rho, u)
+    want = oracle.run(box, f0, nsteps, mask)
+    results = {}
+    for layout in LAYOUTS:
+        for scheme in SCHEMES:
+            say("open", name, precision, layout, scheme, nsteps)
+            lat = _make_open(shape, precision, layout, scheme, tau, F, faces, mask, per, rho, u)
+            g0 = host_f(lat)
+            rel = 4e-7 if precision == "f32" else 1e-15
+            assert np.max(np.abs(g0 - f0)) <= rel * np.max(np.abs(f0)), "initial state"
+            lat.step(nsteps)
+            got = host_f(lat)
+            err = np.max(np.abs(got - want))
+            say("  max-abs", err)
+            assert err <= TOL[precision], (layout, scheme, err)
+            results[(layout, scheme)] = got
+    ref = results[("stream", "ab")]
+    for k, v in results.items():
+        assert np.array_equal(v, ref), f"{k} differs from stream/ab"
+
+
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+def test_uniform_stream_is_a_fixed_point(precision):
+    need_gpu()
+    shape, per = (20, 12, 9), (0, 1, 0)
+    uu = (0.03, -0.01, 0.02)
+    faces = {k: (1.0, uu) for k in ("-x", "+x", "-z", "+z")}
+    n = int(np.prod(shape))
+    rho = cast(np.ones(n), precision)
+    u = cast(np.tile(np.array(uu)[:, None], (1, n)), precision)
+    for layout in ("compact", "stream", "collision"):
+        for scheme in SCHEMES:
+            say("uniform", precision, layout, scheme)
+            lat = _make_open(shape, precision, layout, scheme, 0.8, (0.0, 0.0, 0.0), faces, None, per, rho, u)
+            f0 = host_f(lat)
+            lat.step(40)
+            f1 = host_f(lat)
+            tol = 2e-7 if precision == "f32" else 1e-15
+            assert np.max(np.abs(f1 - f0)) <= tol, (layout, scheme, np.max(np.abs(f1 - f0)))
