@@ -107,7 +107,7 @@ lbm_status lbm_buffer_bytes(const lbm_desc *desc, size_t *bytes_per_buffer, int3
 
 /* Device workspace the layout needs for geometry tables: 0 for the dense
  * layouts; for LBM_LAYOUT_COMPACT about 4 bytes per cell of the box padded by
- * one halo layer plus 4 bytes per cell (index tables).  Host only. */
+ * one halo layer plus 8 bytes per cell (index tables).  Host only. */
 lbm_status lbm_workspace_bytes(const lbm_desc *desc, size_t *bytes);
 
 /* Create a handle over caller-owned population memory.
@@ -167,6 +167,20 @@ lbm_status lbm_init_equilibrium(lbm_sim *sim, const void *rho, const void *u);
 
 /* Advance n >= 0 time steps (one fused kernel launch each); t += n. */
 lbm_status lbm_step(lbm_sim *sim, int64_t n);
+
+/* Advance n >= 1 time steps like lbm_step; the last step also writes the
+ * density and velocity its collision uses, i.e. the moments of f(t + n - 1),
+ * t the time before the call (the fused macroscopic output of the PortLBM
+ * page, section 5.2: its combined kernel writes four macroscopic values per
+ * update besides the populations; here 4 sizeof(T) bytes more per cell on
+ * the last step instead of a separate pass over the state).
+ *   rho   device T[N], u device T[3][N] (component-major, u includes F/2);
+ *         0 on solid cells.  The values equal what lbm_moments returns
+ *         before the last step, bit for bit.
+ * The compact layout first zeroes rho and u on the solid cells, then its step
+ * writes the fluid cells.  LBM_ERR_INVALID_ARGUMENT for n < 1 or NULL
+ * outputs. */
+lbm_status lbm_step_moments(lbm_sim *sim, int64_t n, void *rho, void *u);
 
 /* Density and velocity of the canonical state f(t):
  * rho = sum_q f_q, u = (sum_q c_q f_q + F/2) / rho; 0 on solid cells.

@@ -27,7 +27,7 @@ EXPORTED = ["lbm_buffer_bytes", "lbm_workspace_bytes", "lbm_create", "lbm_set_wo
             "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_save_state",
             "lbm_load_state", "lbm_destroy", "lbm_time", "lbm_fluid_cells", "lbm_last_hip_error",
             "lbm_status_string", "lbm_momentum_exchange_scratch_bytes", "lbm_momentum_exchange",
-            "lbm_set_open_faces"]
+            "lbm_set_open_faces", "lbm_step_moments"]
 
 
 class lbm_desc(ctypes.Structure):
@@ -77,6 +77,8 @@ _lib.lbm_set_open_faces.restype = _st
 _lib.lbm_init_equilibrium.argtypes = [_vp, _vp, _vp]
 _lib.lbm_init_equilibrium.restype = _st
 _lib.lbm_step.argtypes = [_vp, _i64]
+_lib.lbm_step_moments.argtypes = [_vp, _i64, _vp, _vp]
+_lib.lbm_step_moments.restype = _st
 _lib.lbm_step.restype = _st
 _lib.lbm_moments.argtypes = [_vp, _vp, _vp]
 _lib.lbm_moments.restype = _st
@@ -183,6 +185,10 @@ def lbm_init_equilibrium(sim, rho=None, u=None):
 
 def lbm_step(sim, n):
     return _lib.lbm_step(sim, int(n))
+
+
+def lbm_step_moments(sim, n, rho, u):
+    return _lib.lbm_step_moments(sim, int(n), _ptr(rho), _ptr(u))
 
 
 def lbm_moments(sim, rho, u):

@@ -169,6 +169,7 @@ lbm_status build_compact(lbm_sim* s)
     t.rows = (uint32_t*)(base + lay.rows);
     t.idxp = (uint32_t*)(base + lay.idxp);
     t.cellp = (uint32_t*)(base + lay.cellp);
+    t.cellid = (uint32_t*)(base + lay.cellid);
     t.nf = 0;
     t.stride = 0;
     hipError_t e = lbm::launch_compact_build(geom_of(s), t, s->stream);
@@ -309,10 +310,14 @@ lbm_status lbm_init_equilibrium(lbm_sim* sim, const void* rho, const void* u)
     return r;
 }
 
-lbm_status lbm_step(lbm_sim* sim, int64_t n)
+}  // extern "C"
+
+namespace {
+
+// n steps; the last one also writes the density and velocity its collision
+// used into rho / u when they are given.
+lbm_status run_steps(lbm_sim* sim, int64_t n, void* rho, void* u)
 {
-    if (sim == nullptr || n < 0) return LBM_ERR_INVALID_ARGUMENT;
-    if (!sim->initialized) return LBM_ERR_BAD_STATE;
     const lbm::LaunchGeom g = geom_of(sim);
     const lbm::LaunchPhys p = phys_of(sim);
     for (int64_t i = 0; i < n; ++i) {
@@ -326,22 +331,46 @@ lbm_status lbm_step(lbm_sim* sim, int64_t n)
             kind = (sim->t % 2 == 0) ? lbm::kAAEven : lbm::kAAOdd;
             a = sim->buf[0];
         }
+        void* ro = i + 1 == n ? rho : nullptr;
+        void* uo = i + 1 == n ? u : nullptr;
         hipError_t e;
         if (compact(sim->d)) {
             if (sim->d.precision == LBM_F32)
-                e = lbm::launch_step_compact<float>(kind, (float*)a, (float*)b, g, sim->tables, p, sim->stream);
+                e = lbm::launch_step_compact<float>(kind, (float*)a, (float*)b, g, sim->tables, p, (float*)ro,
+                                                    (float*)uo, sim->stream);
             else
-                e = lbm::launch_step_compact<double>(kind, (double*)a, (double*)b, g, sim->tables, p, sim->stream);
+                e = lbm::launch_step_compact<double>(kind, (double*)a, (double*)b, g, sim->tables, p, (double*)ro,
+                                                     (double*)uo, sim->stream);
         } else if (sim->d.precision == LBM_F32) {
-            e = lbm::launch_step<float>(sim->d.layout, kind, (float*)a, (float*)b, g, p, sim->stream);
+            e = lbm::launch_step<float>(sim->d.layout, kind, (float*)a, (float*)b, g, p, (float*)ro, (float*)uo,
+                                        sim->stream);
         } else {
-            e = lbm::launch_step<double>(sim->d.layout, kind, (double*)a, (double*)b, g, p, sim->stream);
+            e = lbm::launch_step<double>(sim->d.layout, kind, (double*)a, (double*)b, g, p, (double*)ro,
+                                         (double*)uo, sim->stream);
         }
         if (e != hipSuccess) return hip_status(sim, e);
         if (sim->d.scheme == LBM_SCHEME_AB) sim->cur = 1 - sim->cur;
         sim->t += 1;
     }
     return LBM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lbm_status lbm_step(lbm_sim* sim, int64_t n)
+{
+    if (sim == nullptr || n < 0) return LBM_ERR_INVALID_ARGUMENT;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    return run_steps(sim, n, nullptr, nullptr);
+}
+
+lbm_status lbm_step_moments(lbm_sim* sim, int64_t n, void* rho, void* u)
+{
+    if (sim == nullptr || n < 1 || rho == nullptr || u == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    return run_steps(sim, n, rho, u);
 }
 
 lbm_status lbm_moments(lbm_sim* sim, void* rho, void* u)

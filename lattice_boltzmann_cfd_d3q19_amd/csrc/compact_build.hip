@@ -61,7 +61,8 @@ __global__ void __launch_bounds__(kBlockThreads) compact_fill_rows(const uint8_t
                                                                    uint32_t ny, uint32_t px, uint32_t pxy,
                                                                    const uint32_t* __restrict__ row_start,
                                                                    uint32_t* __restrict__ idxp,
-                                                                   uint32_t* __restrict__ cellp)
+                                                                   uint32_t* __restrict__ cellp,
+                                                                   uint32_t* __restrict__ cellid)
 {
     __shared__ uint32_t wave_tot[kBlockThreads / 64];
     const uint32_t r = blockIdx.x;
@@ -87,6 +88,7 @@ __global__ void __launch_bounds__(kBlockThreads) compact_fill_rows(const uint8_t
                 const uint32_t i = base + before + below;
                 idxp[p] = i;
                 cellp[i] = p;
+                cellid[i] = r * nx + x;
             } else {
                 idxp[p] = kInvalid;
             }
@@ -147,7 +149,8 @@ CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz)
     b.rows = 256;
     b.idxp = b.rows + up(4 * nrows);
     b.cellp = b.idxp + up(4 * npad);
-    b.total = b.cellp + up(4 * n64);
+    b.cellid = b.cellp + up(4 * n64);
+    b.total = b.cellid + up(4 * n64);
     return b;
 }
 
@@ -160,7 +163,7 @@ hipError_t launch_compact_build(const LaunchGeom& lg, const CompactTables& t, hi
     hipLaunchKernelGGL(compact_count_rows, dim3(nrows), dim3(kBlockThreads), 0, st, lg.mask, nx, t.rows);
     hipLaunchKernelGGL(compact_scan_rows, dim3(1), dim3(1024), 0, st, t.rows, nrows, t.header);
     hipLaunchKernelGGL(compact_fill_rows, dim3(nrows), dim3(kBlockThreads), 0, st, lg.mask, nx, ny, px, pxy,
-                       (const uint32_t*)t.rows, t.idxp, t.cellp);
+                       (const uint32_t*)t.rows, t.idxp, t.cellp, t.cellid);
     hipLaunchKernelGGL(compact_fill_halo, dim3((uint32_t)((npad + kBlockThreads - 1) / kBlockThreads)),
                        dim3(kBlockThreads), 0, st, nx, ny, nz, (uint32_t)(lg.periodic[0] != 0),
                        (uint32_t)(lg.periodic[1] != 0), (uint32_t)(lg.periodic[2] != 0), lg.open, px, pxy, npad,

@@ -472,11 +472,12 @@ __device__ __forceinline__ void relax_pair(T (&s)[kQ], const Phys<T>& p, T drho,
     s[o] = no;
 }
 
-// BGK collision of one cell, in place on the shifted populations.
+// BGK collision of one cell, in place on the shifted populations; also hands
+// back the density and velocity it relaxed toward (u includes F/2).
 template <typename T, bool FORCE>
-__device__ __forceinline__ void collide(T (&s)[kQ], const Phys<T>& p)
+__device__ __forceinline__ void collide(T (&s)[kQ], const Phys<T>& p, T& rho, T& ux, T& uy, T& uz)
 {
-    T drho, rho, ux, uy, uz;
+    T drho;
     moments<T, FORCE>(s, p, drho, rho, ux, uy, uz);
     const T k15 = k15_of(ux, uy, uz);
     T uF = T(0), guF0 = T(0), guF18 = T(0), guF36 = T(0);
@@ -504,6 +505,31 @@ __device__ __forceinline__ void collide(T (&s)[kQ], const Phys<T>& p)
     T n9 = fma(p.omega, e9 - s[9], s[9]);
     if constexpr (FORCE) n9 = n9 - guF0;
     s[9] = n9;
+}
+
+template <typename T, bool FORCE>
+__device__ __forceinline__ void collide(T (&s)[kQ], const Phys<T>& p)
+{
+    T rho, ux, uy, uz;
+    collide<T, FORCE>(s, p, rho, ux, uy, uz);
+}
+
+// Destination of the macroscopic fields a step can write as it goes (the
+// density and velocity its collision used): rho[N], u[3][N] in cell order.
+template <typename T>
+struct MomOut {
+    T* rho;
+    T* u;
+    uint64_t n;
+};
+
+template <typename T>
+__device__ __forceinline__ void write_moments(const MomOut<T>& o, uint64_t id, T rho, T ux, T uy, T uz)
+{
+    o.rho[id] = rho;
+    o.u[id] = ux;
+    o.u[o.n + id] = uy;
+    o.u[2 * o.n + id] = uz;
 }
 
 // Shifted equilibrium populations of (rho, u): s_q = feq_q(rho, u) - w_q, built
@@ -566,15 +592,19 @@ constexpr int kBlockThreads = 256;
 // One fused time step.  K: kAB (a = source, b = destination), kAAEven or
 // kAAOdd (a = the single lattice).  BND: 0 = fully periodic, no mask;
 // 1 = a mask or a wall exists; 2 = also open faces (a separate instance, so
-// the reservoir selects cost the other kernels no registers).
-template <typename T, int L, int K, int BND, bool FORCE>
+// the reservoir selects cost the other kernels no registers).  OUT: also
+// write the density and velocity the collision used (0 on solid cells).
+template <typename T, int L, int K, int BND, bool FORCE, bool OUT>
 __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, T* __restrict__ b,
-                                                             Geom g, Phys<T> p)
+                                                             Geom g, Phys<T> p, MomOut<T> mo)
 {
     Cell c;
     if (!locate(g, c)) return;
     if constexpr (BND) {
-        if (g.mask != nullptr && g.mask[c.id] != 0) return;  // solid cells are never updated
+        if (g.mask != nullptr && g.mask[c.id] != 0) {  // solid cells are never updated
+            if constexpr (OUT) write_moments(mo, c.id, T(0), T(0), T(0), T(0));
+            return;
+        }
     }
     const uint32_t bits = link_bits<BND != 0>(g, c);
     const uint32_t obits = BND == 2 ? open_bits(g, c) : 0u;  // populations entering through open faces
@@ -595,7 +625,9 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
     // step and the initialisation put them there); the gathers take them here
     if constexpr (BND == 2 && K != kAAEven) apply_open(f, obits, p, c);
 
-    collide<T, FORCE>(f, p);
+    T rho, ux, uy, uz;
+    collide<T, FORCE>(f, p, rho, ux, uy, uz);
+    if constexpr (OUT) write_moments(mo, c.id, rho, ux, uy, uz);
     if constexpr (BND == 2 && K == kAAOdd) open_outflow(f, obits, p, c);
 
 #pragma unroll

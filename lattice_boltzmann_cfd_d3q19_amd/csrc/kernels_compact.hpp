@@ -15,6 +15,8 @@
 //             hold the index of their periodic image, kWall beyond a wall
 //             face (halfway bounce-back) or kOpen + k beyond open face k.
 //   cellp[i]  padded id p of the i-th fluid cell.
+//   cellid[i] cell index x + nx (y + ny z) of the i-th fluid cell (for the
+//             macroscopic fields a step writes as it goes).
 // A neighbour along c_d is then idxp[cellp[i] + off_d] with
 // off_d = c_x + px (c_y + py c_z): no coordinates, no wrap logic.
 #pragma once
@@ -73,6 +75,7 @@ constexpr int kEvenThreads = LBM_EVEN_THREADS;
 struct CompactGeom {
     const uint32_t* idxp;
     const uint32_t* cellp;
+    const uint32_t* cellid;  // cell index x + nx (y + ny z) of the i-th fluid cell
     uint32_t nf;   // fluid cells
     uint32_t px;   // nx + 2
     uint32_t pxy;  // (nx + 2)(ny + 2)
@@ -241,9 +244,9 @@ __device__ __forceinline__ char* pair_block(char* base, int k, uint32_t plane_by
 // step of the in-place pattern (K = kAAOdd, a = the lattice).  OPEN: some
 // faces are open (a separate instance: the reservoir selects would cost the
 // other cases registers).
-template <typename T, int K, bool FORCE, bool OPEN>
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT>
 __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restrict__ a, T* __restrict__ b,
-                                                                     CompactGeom g, Phys<T> p)
+                                                                     CompactGeom g, Phys<T> p, MomOut<T> mo)
 {
     static_assert(K == kAB || K == kAAOdd, "the even step has its own kernel");
     const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
@@ -267,7 +270,9 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
             f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), off);
         }
         if constexpr (OPEN) apply_open_nb(f, nb, p);
-        collide<T, FORCE>(f, p);
+        T rho, ux, uy, uz;
+        collide<T, FORCE>(f, p, rho, ux, uy, uz);
+        if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(B, pair_of(q), sb), sub_of(q) ? own1 : own0, f[q]);
     } else {
@@ -280,7 +285,9 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
 #pragma unroll
         for (int q = 0; q < kQ; ++q) f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), off[opp(q)]);
         if constexpr (OPEN) apply_open_nb(f, nb, p);
-        collide<T, FORCE>(f, p);
+        T rho, ux, uy, uz;
+        collide<T, FORCE>(f, p, rho, ux, uy, uz);
+        if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
         // beyond an open face, f*_d leaves the box and the own slot (opp d, x)
         // takes the reservoir's population entering along -c_d
         if constexpr (OPEN) open_outflow(f, nb, p);
@@ -294,8 +301,10 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
 // others but never read as state.  Wider accesses (2 or 4 cells per
 // work-item, 8- or 16-byte vectors) measured no faster: this step moves
 // every line once and runs at the HBM rate of the in-place pattern.
-template <typename T, bool FORCE>
-__global__ void __launch_bounds__(kEvenThreads) even_compact_kernel(T* __restrict__ a, uint32_t s, Phys<T> p)
+template <typename T, bool FORCE, bool OUT>
+__global__ void __launch_bounds__(kEvenThreads) even_compact_kernel(T* __restrict__ a, uint32_t s, Phys<T> p,
+                                                                    MomOut<T> mo, const uint32_t* __restrict__ cellid,
+                                                                    uint32_t nf)
 {
     const uint32_t i = blockIdx.x * kEvenThreads + threadIdx.x;
     if (i >= s) return;
@@ -307,9 +316,21 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_kernel(T* __restric
 #pragma unroll
     for (int q = 0; q < kQ; ++q)
         f[q] = __builtin_nontemporal_load((const T*)(pair_block(A, pair_of(q), sb) + (sub_of(q) ? own1 : own0)));
-    collide<T, FORCE>(f, p);
+    T rho, ux, uy, uz;
+    collide<T, FORCE>(f, p, rho, ux, uy, uz);
+    if constexpr (OUT)
+        if (i < nf) write_moments(mo, cellid[i], rho, ux, uy, uz);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(A, pair_of(q), sb), sub_of(opp(q)) ? own1 : own0, f[q]);
+}
+
+// rho and u := 0 on the solid cells (the fields of a compact step; the step
+// itself writes the fluid cells).
+template <typename T>
+__global__ void __launch_bounds__(kBlockThreads) zero_moments_kernel(MomOut<T> mo, const uint8_t* __restrict__ mask)
+{
+    const uint64_t id = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+    if (id < mo.n && mask[id] != 0) write_moments(mo, id, T(0), T(0), T(0), T(0));
 }
 
 // State transfers between canonical dense arrays ([19][N], [N], [3][N]) and

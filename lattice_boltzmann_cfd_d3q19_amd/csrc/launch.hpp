@@ -23,9 +23,11 @@ struct LaunchPhys {
 
 // One fused step of kind `kind` (kAB: a = source, b = destination; kAAEven /
 // kAAOdd: a = the lattice, b unused) over the whole box.
+// rho_out / u_out: device T[N] / T[3][N] for the density and velocity the
+// step's collision uses (0 on solid cells), or null.
 template <typename T>
-hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& g, const LaunchPhys& p,
-                       hipStream_t s);
+hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& g, const LaunchPhys& p, T* rho_out,
+                       T* u_out, hipStream_t s);
 
 // Canonical-state transfer `op` (an IoOp) for a stored state of kind `state`.
 template <typename T>
@@ -38,13 +40,14 @@ struct CompactTables {
     uint32_t* rows;    // per x-row fluid counts, then their exclusive scan
     uint32_t* idxp;    // halo-padded cell -> compact index (kInvalid: solid / wall)
     uint32_t* cellp;   // compact index -> padded cell
+    uint32_t* cellid;  // compact index -> cell index
     uint32_t nf;       // fluid cells (known on the host after the build)
     uint64_t stride;   // population stride, nf rounded up to 64
 };
 
 // Byte offsets of the tables inside a workspace, and its size.
 struct CompactLayoutBytes {
-    size_t header, rows, idxp, cellp, total;
+    size_t header, rows, idxp, cellp, cellid, total;
 };
 CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz);
 
@@ -53,7 +56,7 @@ hipError_t launch_compact_build(const LaunchGeom& g, const CompactTables& t, hip
 
 template <typename T>
 hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& g, const CompactTables& t,
-                               const LaunchPhys& p, hipStream_t s);
+                               const LaunchPhys& p, T* rho_out, T* u_out, hipStream_t s);
 
 template <typename T>
 hipError_t launch_io_compact(int state, int op, T* a, const LaunchGeom& g, const CompactTables& t,

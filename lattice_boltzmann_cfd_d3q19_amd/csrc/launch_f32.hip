@@ -2,12 +2,12 @@
 #include "launch_impl.hpp"
 
 namespace lbm {
-template hipError_t launch_step<float>(int, int, float*, float*, const LaunchGeom&, const LaunchPhys&,
+template hipError_t launch_step<float>(int, int, float*, float*, const LaunchGeom&, const LaunchPhys&, float*, float*,
                                        hipStream_t);
 template hipError_t launch_io<float>(int, int, int, float*, float*, const LaunchGeom&, const LaunchPhys&,
                                      float*, float*, const float*, const float*, hipStream_t);
 template hipError_t launch_step_compact<float>(int, float*, float*, const LaunchGeom&, const CompactTables&,
-                                               const LaunchPhys&, hipStream_t);
+                                               const LaunchPhys&, float*, float*, hipStream_t);
 template hipError_t launch_io_compact<float>(int, int, float*, const LaunchGeom&, const CompactTables&,
                                              const LaunchPhys&, float*, float*, const float*, const float*, hipStream_t);
 template hipError_t launch_momentum_exchange<float>(int, int, float*, const LaunchGeom&, const CompactTables*,

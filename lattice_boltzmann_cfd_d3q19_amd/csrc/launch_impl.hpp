@@ -88,54 +88,59 @@ inline Phys<T> make_phys(const LaunchPhys& lp)
 }
 
 template <typename T, int L, int K, int BND, bool FORCE>
-hipError_t launch_step_t(T* a, T* b, const Shape& s, const Phys<T>& p, hipStream_t st)
+hipError_t launch_step_t(T* a, T* b, const Shape& s, const Phys<T>& p, const MomOut<T>& mo, hipStream_t st)
 {
     Geom g = s.g;
     Phys<T> ph = p;
-    void* args[] = {&a, &b, &g, &ph};
+    MomOut<T> m = mo;
+    void* args[] = {&a, &b, &g, &ph, &m};
     // hipLaunchKernel reports the status of this launch only (no stale errors)
-    return hipLaunchKernel((const void*)&step_kernel<T, L, K, BND, FORCE>, s.grid, s.block, args, 0, st);
+    const void* k = mo.rho != nullptr ? (const void*)&step_kernel<T, L, K, BND, FORCE, true>
+                                      : (const void*)&step_kernel<T, L, K, BND, FORCE, false>;
+    return hipLaunchKernel(k, s.grid, s.block, args, 0, st);
 }
 
 template <typename T, int L, int K>
-hipError_t launch_step_k(T* a, T* b, const Shape& s, const Phys<T>& p, int bnd, bool force, hipStream_t st)
+hipError_t launch_step_k(T* a, T* b, const Shape& s, const Phys<T>& p, const MomOut<T>& mo, int bnd, bool force,
+                         hipStream_t st)
 {
     if (bnd == 2)
-        return force ? launch_step_t<T, L, K, 2, true>(a, b, s, p, st)
-                     : launch_step_t<T, L, K, 2, false>(a, b, s, p, st);
+        return force ? launch_step_t<T, L, K, 2, true>(a, b, s, p, mo, st)
+                     : launch_step_t<T, L, K, 2, false>(a, b, s, p, mo, st);
     if (bnd == 1)
-        return force ? launch_step_t<T, L, K, 1, true>(a, b, s, p, st)
-                     : launch_step_t<T, L, K, 1, false>(a, b, s, p, st);
-    return force ? launch_step_t<T, L, K, 0, true>(a, b, s, p, st)
-                 : launch_step_t<T, L, K, 0, false>(a, b, s, p, st);
+        return force ? launch_step_t<T, L, K, 1, true>(a, b, s, p, mo, st)
+                     : launch_step_t<T, L, K, 1, false>(a, b, s, p, mo, st);
+    return force ? launch_step_t<T, L, K, 0, true>(a, b, s, p, mo, st)
+                 : launch_step_t<T, L, K, 0, false>(a, b, s, p, mo, st);
 }
 
 template <typename T, int L>
-hipError_t launch_step_l(int kind, T* a, T* b, const Shape& s, const Phys<T>& p, int bnd, bool force,
-                         hipStream_t st)
+hipError_t launch_step_l(int kind, T* a, T* b, const Shape& s, const Phys<T>& p, const MomOut<T>& mo, int bnd,
+                         bool force, hipStream_t st)
 {
     switch (kind) {
-    case kAB: return launch_step_k<T, L, kAB>(a, b, s, p, bnd, force, st);
-    case kAAEven: return launch_step_k<T, L, kAAEven>(a, b, s, p, bnd, force, st);
-    case kAAOdd: return launch_step_k<T, L, kAAOdd>(a, b, s, p, bnd, force, st);
+    case kAB: return launch_step_k<T, L, kAB>(a, b, s, p, mo, bnd, force, st);
+    case kAAEven: return launch_step_k<T, L, kAAEven>(a, b, s, p, mo, bnd, force, st);
+    case kAAOdd: return launch_step_k<T, L, kAAOdd>(a, b, s, p, mo, bnd, force, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp,
-                       hipStream_t st)
+hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp, T* rho_out,
+                       T* u_out, hipStream_t st)
 {
     // XCD-chunked tile order for the AoS layout only.  Measured, 256^3 porous
     // box, hardware order -> chunked: collision AA odd 2.06 -> 1.22 ms, AB
     // 0.92 -> 0.78 ms; stream AA +8% / +2% and AB +7%, bundle within 2%.
     const Shape s = make_shape(lg, layout == kCollision);
     const Phys<T> p = make_phys<T>(lp);
+    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz};
     const int bnd = lg.open != 0 ? 2 : (lg.mask != nullptr || !lg.periodic[0] || !lg.periodic[1] || !lg.periodic[2]);
     switch (layout) {
-    case kStream: return launch_step_l<T, kStream>(kind, a, b, s, p, bnd, lp.has_force, st);
-    case kBundle: return launch_step_l<T, kBundle>(kind, a, b, s, p, bnd, lp.has_force, st);
-    case kCollision: return launch_step_l<T, kCollision>(kind, a, b, s, p, bnd, lp.has_force, st);
+    case kStream: return launch_step_l<T, kStream>(kind, a, b, s, p, mo, bnd, lp.has_force, st);
+    case kBundle: return launch_step_l<T, kBundle>(kind, a, b, s, p, mo, bnd, lp.has_force, st);
+    case kCollision: return launch_step_l<T, kCollision>(kind, a, b, s, p, mo, bnd, lp.has_force, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -198,6 +203,7 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     CompactGeom g{};
     g.idxp = t.idxp;
     g.cellp = t.cellp;
+    g.cellid = t.cellid;
     g.nf = t.nf;
     g.px = (uint32_t)lg.nx + 2;
     g.pxy = (uint32_t)((lg.nx + 2) * (lg.ny + 2));
@@ -216,49 +222,66 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
 }
 
 template <typename T, int K, bool FORCE>
-hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, hipStream_t st)
+hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, MomOut<T> mo, hipStream_t st)
 {
     if (g.nf == 0) return hipSuccess;
-    void* args[] = {&a, &b, &g, &p};
+    void* args[] = {&a, &b, &g, &p, &mo};
     uint32_t nwg = (g.nf + kGatherThreads - 1) / kGatherThreads;
     if (g.xk > 1) nwg = (nwg + 8 * g.xk - 1) / (8 * g.xk) * (8 * g.xk);
     const dim3 grid(nwg), block(kGatherThreads);
-    const void* k = g.open ? (const void*)&step_compact_kernel<T, K, FORCE, true>
-                           : (const void*)&step_compact_kernel<T, K, FORCE, false>;
+    const bool out = mo.rho != nullptr;
+    const void* k = g.open ? (out ? (const void*)&step_compact_kernel<T, K, FORCE, true, true>
+                                  : (const void*)&step_compact_kernel<T, K, FORCE, true, false>)
+                           : (out ? (const void*)&step_compact_kernel<T, K, FORCE, false, true>
+                                  : (const void*)&step_compact_kernel<T, K, FORCE, false, false>);
     return hipLaunchKernel(k, grid, block, args, 0, st);
 }
 
 template <typename T, bool FORCE>
-hipError_t launch_even_compact_t(T* a, CompactGeom g, Phys<T> p, hipStream_t st)
+hipError_t launch_even_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, hipStream_t st)
 {
     if (g.nf == 0) return hipSuccess;
-    uint32_t s = g.s;
-    void* args[] = {&a, &s, &p};
+    uint32_t s = g.s, nf = g.nf;
+    const uint32_t* cellid = g.cellid;
+    void* args[] = {&a, &s, &p, &mo, &cellid, &nf};
     const dim3 grid((s + kEvenThreads - 1) / kEvenThreads), block(kEvenThreads);
-    return hipLaunchKernel((const void*)&even_compact_kernel<T, FORCE>, grid, block, args, 0, st);
+    const void* k = mo.rho != nullptr ? (const void*)&even_compact_kernel<T, FORCE, true>
+                                      : (const void*)&even_compact_kernel<T, FORCE, false>;
+    return hipLaunchKernel(k, grid, block, args, 0, st);
 }
 
 template <typename T, int K>
-hipError_t launch_step_compact_k(T* a, T* b, CompactGeom g, Phys<T> p, bool force, hipStream_t st)
+hipError_t launch_step_compact_k(T* a, T* b, CompactGeom g, Phys<T> p, MomOut<T> mo, bool force, hipStream_t st)
 {
     if constexpr (K == kAAEven) {
-        return force ? launch_even_compact_t<T, true>(a, g, p, st) : launch_even_compact_t<T, false>(a, g, p, st);
+        return force ? launch_even_compact_t<T, true>(a, g, p, mo, st) : launch_even_compact_t<T, false>(a, g, p, mo, st);
     } else {
-        return force ? launch_step_compact_t<T, K, true>(a, b, g, p, st)
-                     : launch_step_compact_t<T, K, false>(a, b, g, p, st);
+        return force ? launch_step_compact_t<T, K, true>(a, b, g, p, mo, st)
+                     : launch_step_compact_t<T, K, false>(a, b, g, p, mo, st);
     }
 }
 
 template <typename T>
 hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& lg, const CompactTables& t,
-                               const LaunchPhys& lp, hipStream_t st)
+                               const LaunchPhys& lp, T* rho_out, T* u_out, hipStream_t st)
 {
     const CompactGeom g = compact_geom(lg, t);
     const Phys<T> p = make_phys<T>(lp);
+    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz};
+    if (rho_out != nullptr && lg.mask != nullptr) {
+        // solid cells get zeros here; the step writes the fluid cells
+        const uint64_t blocks = (mo.n + kBlockThreads - 1) / kBlockThreads;
+        MomOut<T> m = mo;
+        const uint8_t* mask = lg.mask;
+        void* args[] = {&m, &mask};
+        const hipError_t e = hipLaunchKernel((const void*)&zero_moments_kernel<T>, dim3((uint32_t)blocks),
+                                             dim3(kBlockThreads), args, 0, st);
+        if (e != hipSuccess) return e;
+    }
     switch (kind) {
-    case kAB: return launch_step_compact_k<T, kAB>(a, b, g, p, lp.has_force, st);
-    case kAAEven: return launch_step_compact_k<T, kAAEven>(a, b, g, p, lp.has_force, st);
-    case kAAOdd: return launch_step_compact_k<T, kAAOdd>(a, b, g, p, lp.has_force, st);
+    case kAB: return launch_step_compact_k<T, kAB>(a, b, g, p, mo, lp.has_force, st);
+    case kAAEven: return launch_step_compact_k<T, kAAEven>(a, b, g, p, mo, lp.has_force, st);
+    case kAAOdd: return launch_step_compact_k<T, kAAOdd>(a, b, g, p, mo, lp.has_force, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -89,6 +89,15 @@ class Lattice:
     def step(self, n=1):
         capi.check(capi.lbm_step(self.handle, n), "lbm_step", self.handle)
 
+    def step_moments(self, n=1):
+        """n steps; returns the density and velocity the last step's collision
+        used (the moments of the state at t + n - 1), written by that step."""
+        rho = torch.empty(self.n, dtype=self.dtype, device=self.device)
+        u = torch.empty((3, self.n), dtype=self.dtype, device=self.device)
+        capi.check(capi.lbm_step_moments(self.handle, n, rho.data_ptr(), u.data_ptr()), "lbm_step_moments",
+                   self.handle)
+        return rho, u
+
     @property
     def t(self):
         return capi.lbm_time(self.handle)
