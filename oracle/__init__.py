@@ -20,6 +20,11 @@ Parity status per function (what pins it, from the tests):
   momentum_exchange -- the step's momentum budget (P(t+1) - P(t) = N_fluid F
                       minus the exchanged force, any state), zero force at
                       rest, steady channel wall force = N_fluid F
+  apply_open_faces -- uniform streams are fixed points of every rule; the
+                      moments each Zou-He rule prescribes hold exactly on any
+                      state; Neumann copies the inward cell's equilibrium;
+                      per-step mass budget through the faces; pressure-driven
+                      channel flow
 No function is "parity unpinned"; the specific random streams used to build
 inputs are unpinned by nature (determinism and statistics only).
 """
@@ -39,7 +44,8 @@ class _Box(ctypes.Structure):
     _fields_ = [("nx", ctypes.c_int64), ("ny", ctypes.c_int64), ("nz", ctypes.c_int64),
                 ("periodic", ctypes.c_int32 * 3), ("tau", ctypes.c_double),
                 ("force", ctypes.c_double * 3), ("open", ctypes.c_int32 * 6),
-                ("face_rho", ctypes.c_double * 6), ("face_u", (ctypes.c_double * 3) * 6)]
+                ("face_rho", ctypes.c_double * 6), ("face_u", (ctypes.c_double * 3) * 6),
+                ("face_kind", ctypes.c_int32 * 6)]
 
 
 def _load():
@@ -82,22 +88,36 @@ def _mptr(mask):
 
 
 FACES = ("-x", "+x", "-y", "+y", "-z", "+z")
+# open-face rules, in the C oracle's numbering
+FACE_RULES = ("equilibrium", "neumann", "zou_he_pressure", "zou_he_velocity")
 
 
 class Box:
     """Box description: dims, periodic axes, relaxation time, body force, and
     open faces: ``open_faces`` maps a face name ("-x", "+x", ...) on a
-    non-periodic axis to its reservoir (rho, (ux, uy, uz)); populations
-    entering through that face are the reservoir's equilibrium."""
+    non-periodic axis to (rho, (ux, uy, uz)) or (rho, (ux, uy, uz), rule),
+    rule one of FACE_RULES (default "equilibrium": a reservoir whose
+    equilibrium enters the box).  The other rules need every open face on one
+    axis and at least 3 cells along it."""
 
     def __init__(self, nx, ny, nz, periodic=(1, 1, 1), tau=1.0, force=(0.0, 0.0, 0.0), open_faces=None):
         self.nx, self.ny, self.nz = int(nx), int(ny), int(nz)
         self.periodic = tuple(int(p) for p in periodic)
         self.tau = float(tau)
         self.force = tuple(float(v) for v in force)
-        self.open_faces = dict(open_faces or {})
-        for k in self.open_faces:
+        self.open_faces = {}
+        for k, v in dict(open_faces or {}).items():
             assert k in FACES and not self.periodic[FACES.index(k) // 2], k
+            rule = v[2] if len(v) > 2 else "equilibrium"
+            assert rule in FACE_RULES, rule
+            self.open_faces[k] = (float(v[0]), tuple(float(c) for c in v[1]), rule)
+        axes = {FACES.index(k) // 2 for k in self.open_faces}
+        for k, (_, _, rule) in self.open_faces.items():
+            if rule != "equilibrium":
+                a = FACES.index(k) // 2
+                if len(axes) > 1 or (self.nx, self.ny, self.nz)[a] < 3:
+                    raise ValueError("face rules other than equilibrium need all open faces on one axis, "
+                                     "at least 3 cells long")
 
     @property
     def n(self):
@@ -113,11 +133,12 @@ class Box:
         b.periodic[:] = list(self.periodic)
         b.tau = self.tau
         b.force[:] = list(self.force)
-        for k, (rho, u) in self.open_faces.items():
+        for k, (rho, u, rule) in self.open_faces.items():
             i = FACES.index(k)
             b.open[i] = 1
-            b.face_rho[i] = float(rho)
-            b.face_u[i][:] = [float(v) for v in u]
+            b.face_rho[i] = rho
+            b.face_u[i][:] = list(u)
+            b.face_kind[i] = FACE_RULES.index(rule)
         return b
 
 
@@ -253,8 +274,8 @@ def momentum_exchange(box, f, mask=None):
 
 
 def apply_open_faces(box, f, mask=None):
-    """Copy of f with every population entering through an open face set to
-    the face reservoir's equilibrium."""
+    """Copy of f with every population entering through an open face set by
+    the face's rule."""
     lib = _load()
     m = _mask(box, mask)
     out = np.array(f, np.float64, copy=True).reshape(Q, box.n)

@@ -36,10 +36,18 @@
  *    constant force density.
  *  - tau = +inf means omega = 0: collision is the identity (streaming only).
  *  - Cells outside a non-periodic face count as solid, unless that face is
- *    open: then the populations entering through it are the equilibrium of
- *    the face's (rho, u) (PortLBM page, section 3.1: the inlet takes the
- *    equilibrium distribution of Dirichlet values; used here at every open
- *    face), and those leaving through it are dropped.
+ *    open: then the populations leaving through it are dropped and those
+ *    entering through it are set by the face's rule after streaming
+ *    (PortLBM page, section 3.1, boundary paragraph: an inlet takes the
+ *    equilibrium distribution of Dirichlet or Neumann values, the outlet an
+ *    adapted Zou-He condition).  Readings: Dirichlet = a reservoir at
+ *    feq(face rho, face u); Neumann = feq of the density and velocity of the
+ *    cell one layer inward (zero normal gradient, same state); Zou-He = the
+ *    non-equilibrium bounce-back of Zou and He (Phys. Fluids 9, 1591, 1997)
+ *    on the entering populations, with the transverse momentum correction
+ *    that the 3-D lattice needs (Hecht and Harting, J. Stat. Mech. 2010,
+ *    P01018), for a prescribed density (pressure) or velocity; the momentum
+ *    in it is the bare sum of c f, i.e. rho u - F/2 under Guo forcing.
  */
 #include "lbm_oracle.h"
 
@@ -182,6 +190,128 @@ static void face_equilibrium(const orc_box *b, int face, double feq[ORC_Q])
     orc_equilibrium(b->face_rho[face], b->face_u[face], feq);
 }
 
+static int is_reservoir(const orc_box *b, int face)
+{
+    return b->face_kind[face] == ORC_FACE_EQUILIBRIUM;
+}
+
+/* The rule of face k (not a reservoir) at one cell on that face.  fx: the
+ * cell's 19 populations after streaming; the entries with ent[q] set (the
+ * populations entering through face k) are replaced.  f1: the 19 populations
+ * of the cell one layer inward along the face normal (NULL if solid), read by
+ * the Neumann rule only. */
+static void face_rule(const orc_box *b, int k, double fx[ORC_Q], const int ent[ORC_Q], const double *f1)
+{
+    const int a = k / 2;
+    const int sigma = (k % 2 == 0) ? 1 : -1; /* inward normal is sigma e_a */
+    if (b->face_kind[k] == ORC_FACE_NEUMANN) {
+        double rho, u[3], feq[ORC_Q];
+        if (f1 != NULL) {
+            orc_cell_moments(b, f1, &rho, u);
+        } else {
+            rho = b->face_rho[k];
+            for (int t = 0; t < 3; ++t) u[t] = b->face_u[k][t];
+        }
+        orc_equilibrium(rho, u, feq);
+        for (int q = 0; q < ORC_Q; ++q)
+            if (ent[q]) fx[q] = feq[q];
+        return;
+    }
+    /* Zou-He: mass of the populations parallel to the face (c_a = 0) and of
+     * those leaving through it (c_a = -sigma); tangential momentum of the
+     * parallel ones */
+    double par = 0.0, out = 0.0, tpar[3] = {0.0, 0.0, 0.0};
+    for (int q = 0; q < ORC_Q; ++q) {
+        if (C[q][a] == 0) {
+            par += fx[q];
+            for (int t = 0; t < 3; ++t) tpar[t] += C[q][t] * fx[q];
+        } else if (C[q][a] == -sigma) {
+            out += fx[q];
+        }
+    }
+    /* bare momentum j = sum c f = rho u - F/2.  Mass: rho = par + in + out and
+     * sigma j_a = in - out, so sigma j_a = rho - par - 2 out. */
+    double rho, j[3];
+    if (b->face_kind[k] == ORC_FACE_ZOU_HE_PRESSURE) {
+        rho = b->face_rho[k];
+        for (int t = 0; t < 3; ++t) j[t] = rho * b->face_u[k][t] - 0.5 * b->force[t];
+        j[a] = sigma * (rho - par - 2.0 * out);
+    } else {
+        rho = (par + 2.0 * out - 0.5 * sigma * b->force[a]) / (1.0 - sigma * b->face_u[k][a]);
+        for (int t = 0; t < 3; ++t) j[t] = rho * b->face_u[k][t] - 0.5 * b->force[t];
+    }
+    /* transverse correction: the parallel populations carry tangential
+     * momentum tpar; the entering ones must bring j_t - tpar - (leaving ones'
+     * share), which the bounce-back of the opposites gives up to 2 N_t */
+    double nt[3] = {0.0, 0.0, 0.0};
+    for (int t = 0; t < 3; ++t)
+        if (t != a) nt[t] = 0.5 * tpar[t] - j[t] / 3.0;
+    for (int q = 0; q < ORC_Q; ++q) {
+        if (!ent[q]) continue;
+        double cj = 0.0, corr = 0.0;
+        for (int t = 0; t < 3; ++t) {
+            cj += C[q][t] * j[t];
+            corr += C[q][t] * nt[t];
+        }
+        /* feq_q - feq_opp(q) = 6 w_q c_q . j (the odd part of the equilibrium) */
+        fx[q] = fx[OPP[q]] + 6.0 * W[q] * cj - corr;
+    }
+}
+
+/* Which populations of cell (xx, y, z) enter through face k; 0 if none. */
+static int entering_through(const orc_box *b, const uint8_t *mask, int64_t xx, int64_t y, int64_t z, int k,
+                            int ent[ORC_Q])
+{
+    int any = 0;
+    for (int q = 0; q < ORC_Q; ++q) {
+        int64_t src;
+        int face = -1;
+        ent[q] = classify(b, mask, xx, y, z, -C[q][0], -C[q][1], -C[q][2], &src, &face) == LINK_OPEN && face == k;
+        any |= ent[q];
+    }
+    return any;
+}
+
+/* Apply the rule of face k to every fluid cell on it, in place in f. */
+static void face_cells_apply(const orc_box *b, const uint8_t *mask, double *f, int k)
+{
+    int64_t N = ncells(b);
+    const int a = k / 2;
+    const int sigma = (k % 2 == 0) ? 1 : -1;
+    int64_t n[3] = {b->nx, b->ny, b->nz};
+    for (int64_t z = 0; z < b->nz; ++z)
+        for (int64_t y = 0; y < b->ny; ++y)
+            for (int64_t xx = 0; xx < b->nx; ++xx) {
+                int64_t p[3] = {xx, y, z};
+                if (p[a] != (sigma > 0 ? 0 : n[a] - 1)) continue;
+                int64_t x = xx + b->nx * (y + b->ny * z);
+                if (is_solid(mask, x)) continue;
+                int ent[ORC_Q];
+                if (!entering_through(b, mask, xx, y, z, k, ent)) continue;
+                p[a] += sigma;
+                int64_t x1 = p[0] + b->nx * (p[1] + b->ny * p[2]);
+                double fx[ORC_Q], f1[ORC_Q];
+                for (int q = 0; q < ORC_Q; ++q) {
+                    fx[q] = f[q * N + x];
+                    f1[q] = f[q * N + x1];
+                }
+                face_rule(b, k, fx, ent, is_solid(mask, x1) ? NULL : f1);
+                for (int q = 0; q < ORC_Q; ++q)
+                    if (ent[q]) f[q * N + x] = fx[q];
+            }
+}
+
+/* Apply the rules of the open faces that are not reservoirs.  A rule writes
+ * only the entering populations of cells on its face and reads none of them
+ * (a Zou-He cell reads its parallel and leaving populations, a Neumann cell
+ * the cell one layer inward, which is on no open face), so the order of the
+ * cells does not matter. */
+static void apply_rule_faces(const orc_box *b, const uint8_t *mask, double *f)
+{
+    for (int k = 0; k < 6; ++k)
+        if (b->open[k] && !is_reservoir(b, k)) face_cells_apply(b, mask, f, k);
+}
+
 void orc_apply_open_faces(const orc_box *b, const uint8_t *mask, double *f)
 {
     build_tables();
@@ -196,11 +326,13 @@ void orc_apply_open_faces(const orc_box *b, const uint8_t *mask, double *f)
                     int face;
                     if (classify(b, mask, xx, y, z, -C[q][0], -C[q][1], -C[q][2], &src, &face) != LINK_OPEN)
                         continue;
+                    if (!is_reservoir(b, face)) continue;
                     double feq[ORC_Q];
                     face_equilibrium(b, face, feq);
                     f[q * N + x] = feq[q];
                 }
             }
+    apply_rule_faces(b, mask, f);
 }
 
 int orc_init_equilibrium(const orc_box *b, const uint8_t *mask, const double *rho0,
@@ -244,7 +376,8 @@ static void collide_all(const orc_box *b, const uint8_t *mask, const double *f, 
 /* Streaming pass (pull): the value arriving at x along c_q left x - c_q, unless
  * that cell is solid or beyond a wall, in which case the population that left
  * x along -c_q is reflected back at the link midpoint, or lies beyond an open
- * face, in which case it is the face reservoir's equilibrium population. */
+ * face, in which case it is the face reservoir's equilibrium population (for
+ * the other face rules, a placeholder that the rule replaces). */
 static void stream_all(const orc_box *b, const uint8_t *mask, const double *post, double *fnew)
 {
     int64_t N = ncells(b);
@@ -262,11 +395,13 @@ static void stream_all(const orc_box *b, const uint8_t *mask, const double *post
                     int kind = classify(b, mask, xx, y, z, -C[q][0], -C[q][1], -C[q][2], &src, &face);
                     if (kind == LINK_FLUID) {
                         fnew[q * N + x] = post[q * N + src];
-                    } else if (kind == LINK_OPEN) {
+                    } else if (kind == LINK_OPEN && is_reservoir(b, face)) {
                         double feq[ORC_Q];
                         face_equilibrium(b, face, feq);
                         fnew[q * N + x] = feq[q];
                     } else {
+                        /* solid, wall, or an open face with a rule: the rule
+                         * replaces this placeholder after the pass */
                         fnew[q * N + x] = post[OPP[q] * N + x];
                     }
                 }
@@ -283,9 +418,35 @@ int orc_run(const orc_box *b, const uint8_t *mask, double *f, int64_t nsteps)
     for (int64_t t = 0; t < nsteps; ++t) {
         collide_all(b, mask, f, post);
         stream_all(b, mask, post, f); /* f is overwritten only after post is complete */
+        apply_rule_faces(b, mask, f);
     }
     free(post);
     return 0;
+}
+
+/* f(t+1) at one fluid cell before the rules of open faces (pull over the
+ * post-collision values of the source cells, computed here one by one). */
+static void step_one_cell(const orc_box *b, const uint8_t *mask, const double *f, int64_t x, double o[ORC_Q])
+{
+    int64_t N = ncells(b);
+    int64_t xx = x % b->nx, y = (x / b->nx) % b->ny, z = x / (b->nx * b->ny);
+    for (int q = 0; q < ORC_Q; ++q) {
+        int64_t src = -1;
+        int face = -1;
+        int kind = classify(b, mask, xx, y, z, -C[q][0], -C[q][1], -C[q][2], &src, &face);
+        if (kind == LINK_OPEN && is_reservoir(b, face)) {
+            double feq[ORC_Q];
+            face_equilibrium(b, face, feq);
+            o[q] = feq[q];
+            continue;
+        }
+        int use_bb = kind != LINK_FLUID;
+        int64_t from = use_bb ? x : src;
+        double in[ORC_Q], post[ORC_Q];
+        for (int p = 0; p < ORC_Q; ++p) in[p] = f[p * N + from];
+        orc_collide(b, in, post);
+        o[q] = use_bb ? post[OPP[q]] : post[q];
+    }
 }
 
 int orc_step_cells(const orc_box *b, const uint8_t *mask, const double *f, int64_t ncell,
@@ -301,23 +462,18 @@ int orc_step_cells(const orc_box *b, const uint8_t *mask, const double *f, int64
             for (int q = 0; q < ORC_Q; ++q) o[q] = 0.0;
             continue;
         }
-        int64_t xx = x % b->nx, y = (x / b->nx) % b->ny, z = x / (b->nx * b->ny);
-        for (int q = 0; q < ORC_Q; ++q) {
-            int64_t src = -1;
-            int face = -1;
-            int kind = classify(b, mask, xx, y, z, -C[q][0], -C[q][1], -C[q][2], &src, &face);
-            if (kind == LINK_OPEN) {
-                double feq[ORC_Q];
-                face_equilibrium(b, face, feq);
-                o[q] = feq[q];
-                continue;
-            }
-            int use_bb = kind != LINK_FLUID;
-            int64_t from = use_bb ? x : src;
-            double in[ORC_Q], post[ORC_Q];
-            for (int p = 0; p < ORC_Q; ++p) in[p] = f[p * N + from];
-            orc_collide(b, in, post);
-            o[q] = use_bb ? post[OPP[q]] : post[q];
+        step_one_cell(b, mask, f, x, o);
+        int64_t p[3] = {x % b->nx, (x / b->nx) % b->ny, x / (b->nx * b->ny)};
+        for (int face = 0; face < 6; ++face) {
+            int ent[ORC_Q];
+            if (!b->open[face] || is_reservoir(b, face)) continue;
+            if (!entering_through(b, mask, p[0], p[1], p[2], face, ent)) continue;
+            int64_t p1[3] = {p[0], p[1], p[2]};
+            p1[face / 2] += (face % 2 == 0) ? 1 : -1;
+            int64_t x1 = p1[0] + b->nx * (p1[1] + b->ny * p1[2]);
+            double f1[ORC_Q];
+            if (!is_solid(mask, x1)) step_one_cell(b, mask, f, x1, f1);
+            face_rule(b, face, o, ent, is_solid(mask, x1) ? NULL : f1);
         }
     }
     return 0;

@@ -28,14 +28,34 @@ typedef struct {
     double tau;          /* BGK relaxation time; +inf gives omega = 0 (no collision) */
     double force[3];     /* constant body-force density, Guo forcing; zeros = off */
     /* Open faces, in the order -x, +x, -y, +y, -z, +z (only on non-periodic
-     * axes): open[k] = 1 replaces the wall beyond face k by a reservoir at
-     * equilibrium, so every population entering the box through face k is
-     * feq(face_rho[k], face_u[k]) (the equilibrium Dirichlet inlet of the
-     * PortLBM page, section 3.1, used at every open face). */
+     * axes): open[k] = 1 replaces the wall beyond face k by an open boundary
+     * whose rule face_kind[k] sets every population entering through it;
+     * face_rho[k] and face_u[k] are its prescribed values. */
     int32_t open[6];
     double face_rho[6];
     double face_u[6][3];
+    /* Rule of each open face (ORC_FACE_*).  The rules other than the
+     * equilibrium reservoir need every open face of the box on one axis and
+     * at least 3 cells along it. */
+    int32_t face_kind[6];
 } orc_box;
+
+/* Open-face rules (PortLBM page, section 3.1: equilibrium distribution from
+ * Dirichlet or Neumann values at the inlet, an adapted Zou-He condition at
+ * the outlet).  Each sets the populations entering through the face, after
+ * every streaming pass:
+ *  EQUILIBRIUM     feq(face_rho, face_u) (a reservoir; Dirichlet values)
+ *  NEUMANN         feq(rho, u) of the cell one layer inward along the face
+ *                  normal, in the same state (zero normal gradient); the
+ *                  reservoir's values if that cell is solid
+ *  ZOU_HE_PRESSURE density face_rho and tangential velocity from face_u;
+ *                  the normal velocity follows from mass
+ *  ZOU_HE_VELOCITY velocity face_u; the density follows from mass
+ * The Zou-He rules take each entering population from its opposite by
+ * non-equilibrium bounce-back, with the transverse momentum correction of
+ * the 3-D lattice, so that the cell's density (pressure rule) or velocity
+ * (velocity rule) and its tangential momentum are the prescribed ones. */
+enum { ORC_FACE_EQUILIBRIUM = 0, ORC_FACE_NEUMANN = 1, ORC_FACE_ZOU_HE_PRESSURE = 2, ORC_FACE_ZOU_HE_VELOCITY = 3 };
 
 /* Velocity set, weights and opposite-direction table. */
 void orc_lattice(int32_t c[ORC_Q][3], double w[ORC_Q], int32_t opp[ORC_Q]);
@@ -70,8 +90,8 @@ void orc_moments(const orc_box *b, const uint8_t *mask, const double *f, double 
 /* out = {mass, Px, Py, Pz, kinetic energy} summed over fluid cells in long double. */
 void orc_totals(const orc_box *b, const uint8_t *mask, const double *f, double out[5]);
 
-/* Set every population entering the box through an open face to the face's
- * equilibrium (the state invariant of open faces; init applies it). */
+/* Set every population entering the box through an open face by that face's
+ * rule (the state invariant of open faces; init and every step apply it). */
 void orc_apply_open_faces(const orc_box *b, const uint8_t *mask, double *f);
 
 /* Momentum-exchange force of the step that starts from f: sum over the

@@ -284,6 +284,250 @@ def test_apply_open_faces_is_what_init_does():
     assert np.any(f != plain)
 
 
+# ------------------------------------------------------ open-face rules
+#
+# Besides the equilibrium reservoir, an open face may hold a Neumann inlet
+# (the equilibrium of the inward cell's density and velocity) or a Zou-He
+# condition (prescribed density, or prescribed velocity).  Pins: what each
+# rule must make of a uniform stream and of the moments of any state.
+
+def _face_cells(box, face):
+    a, side = oracle.FACES.index(face) // 2, oracle.FACES.index(face) % 2
+    n = (box.nx, box.ny, box.nz)
+    at = 0 if side == 0 else n[a] - 1
+    z, y, x = np.meshgrid(np.arange(box.nz), np.arange(box.ny), np.arange(box.nx), indexing="ij")
+    sel = (x, y, z)[a].reshape(-1) == at
+    return np.nonzero(sel)[0], a, (1 if side == 0 else -1)
+
+
+def _noisy_state(box, mask, seed):
+    # a state far from local equilibrium: equilibrium of random fields plus
+    # random positive noise on every population
+    rho, u = li.random_fields(box.nx, box.ny, box.nz, seed=seed, drho=0.02, du=0.04)
+    plain = oracle.Box(box.nx, box.ny, box.nz, periodic=box.periodic, tau=box.tau, force=box.force)
+    f = oracle.init_equilibrium(plain, mask, rho, u)
+    rng = np.random.default_rng(seed)
+    f = f * (1.0 + 0.05 * rng.standard_normal(f.shape))
+    if mask is not None:
+        f[:, mask.reshape(-1) != 0] = 0.0
+    return f
+
+
+@pytest.mark.parametrize("rules", [("zou_he_velocity", "zou_he_pressure"), ("neumann", "neumann"),
+                                   ("equilibrium", "zou_he_pressure"), ("zou_he_pressure", "zou_he_velocity"),
+                                   ("neumann", "zou_he_pressure")])
+@pytest.mark.parametrize("axis", [0, 1, 2])
+def test_face_rules_keep_uniform_flow(rules, axis):
+    # a uniform stream at equilibrium is a fixed point of every rule whose
+    # prescribed values agree with it (the pressure rule prescribes only the
+    # density and the tangential velocity, so its normal velocity is whatever
+    # mass balance gives: the stream's)
+    rho0, u0 = 1.02, np.array([0.03, -0.01, 0.02])
+    dims = [6, 5, 4]
+    dims[axis] = 8
+    periodic = [1, 1, 1]
+    periodic[axis] = 0
+    lo, hi = oracle.FACES[2 * axis], oracle.FACES[2 * axis + 1]
+    faces = {lo: (rho0, tuple(u0), rules[0]), hi: (rho0, tuple(u0), rules[1])}
+    box = oracle.Box(*dims, periodic=tuple(periodic), tau=0.8, open_faces=faces)
+    n = box.n
+    f0 = oracle.init_equilibrium(box, None, np.full(n, rho0), np.tile(u0[:, None], (1, n)))
+    feq = oracle.equilibrium(rho0, u0)
+    assert np.max(np.abs(f0 - feq[:, None])) < 1e-16
+    f1 = oracle.run(box, f0, 30)
+    assert np.max(np.abs(f1 - f0)) < 1e-14
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("walls", [False, True])
+def test_zou_he_prescribes_its_moments(axis, walls):
+    # on any state, after the rule: a velocity face's cells carry exactly the
+    # prescribed velocity (u = (sum c f + F/2) / rho), a pressure face's cells
+    # the prescribed density and tangential velocity -- except at edges with a
+    # wall, where the wall's bounce-back supplies some entering populations
+    F = (2e-4, -1e-4, 3e-5)
+    dims = [7, 6, 5]
+    periodic = [1, 1, 1]
+    periodic[axis] = 0
+    other = 1 - axis
+    if walls:
+        periodic[other] = 0
+    lo, hi = oracle.FACES[2 * axis], oracle.FACES[2 * axis + 1]
+    u_in = np.array([0.02, 0.01, -0.015])
+    u_t = np.array([0.005, -0.01, 0.02])
+    faces = {lo: (1.0, tuple(u_in), "zou_he_velocity"), hi: (0.98, tuple(u_t), "zou_he_pressure")}
+    box = oracle.Box(*dims, periodic=tuple(periodic), tau=0.7, force=F, open_faces=faces)
+    mask = li.random_mask(*dims, fraction=0.1, seed=21)
+    f = oracle.apply_open_faces(box, _noisy_state(box, mask, 22), mask)
+    rho, u = oracle.moments(box, f, mask)
+    fluid = mask.reshape(-1) == 0
+    coords = np.stack(np.meshgrid(np.arange(dims[2]), np.arange(dims[1]), np.arange(dims[0]),
+                                  indexing="ij")[::-1]).reshape(3, -1)
+    inner = np.ones(box.n, bool)
+    if walls:
+        inner = (coords[other] > 0) & (coords[other] < dims[other] - 1)
+    cells, _, _ = _face_cells(box, lo)
+    cells = cells[fluid[cells] & inner[cells]]
+    assert cells.size > 5
+    np.testing.assert_allclose(u[:, cells], np.tile(u_in[:, None], (1, cells.size)), rtol=0, atol=1e-14)
+    cells, _, _ = _face_cells(box, hi)
+    cells = cells[fluid[cells] & inner[cells]]
+    np.testing.assert_allclose(rho[cells], 0.98, rtol=0, atol=1e-14)
+    for t in range(3):
+        if t != axis:
+            np.testing.assert_allclose(u[t, cells], u_t[t], rtol=0, atol=1e-14)
+    # and the prescribed velocity is not what the cells held before
+    rho_b, u_b = oracle.moments(box, _noisy_state(box, mask, 22), mask)
+    assert np.max(np.abs(rho_b[cells] - 0.98)) > 1e-3
+
+
+@pytest.mark.parametrize("axis", [0, 2])
+def test_zou_he_bounces_back_the_normal_non_equilibrium(axis):
+    # Zou and He's closure: the population along the inward normal and its
+    # opposite have the same non-equilibrium part (no force here, so the
+    # equilibrium is that of the cell's own moments)
+    dims = [5, 6, 5]
+    periodic = [1, 1, 1]
+    periodic[axis] = 0
+    lo, hi = oracle.FACES[2 * axis], oracle.FACES[2 * axis + 1]
+    faces = {lo: (1.0, (0.01, 0.02, 0.03), "zou_he_velocity"), hi: (1.01, (0.0, 0.0, 0.0), "zou_he_pressure")}
+    box = oracle.Box(*dims, periodic=tuple(periodic), tau=0.9, open_faces=faces)
+    f = oracle.apply_open_faces(box, _noisy_state(box, None, 31))
+    c, _, opp = oracle.lattice()
+    for face in (lo, hi):
+        cells, a, sigma = _face_cells(box, face)
+        qn = [q for q in range(19) if c[q][a] == sigma and np.count_nonzero(c[q]) == 1][0]
+        for x in cells:
+            r, v = oracle.cell_moments(box, f[:, x])
+            feq = oracle.equilibrium(r, v)
+            assert abs((f[qn, x] - feq[qn]) - (f[opp[qn], x] - feq[opp[qn]])) < 1e-15
+
+
+def test_neumann_copies_the_inward_equilibrium():
+    # at local equilibrium the Neumann rule hands each entering population the
+    # value the inward cell holds in that direction; where the inward cell is
+    # solid, the face's own values are used
+    box = oracle.Box(7, 5, 4, periodic=(0, 1, 1), tau=0.8,
+                     open_faces={"-x": (1.01, (0.02, 0.0, 0.0), "neumann"),
+                                 "+x": (0.99, (0.01, 0.01, 0.0), "neumann")})
+    mask = np.zeros((4, 5, 7), np.uint8)
+    mask[1, 2, 1] = 1   # inward of (0, 2, 1)
+    mask[3, 0, 5] = 1   # inward of (6, 0, 3)
+    mask = mask.reshape(-1)
+    rho, u = li.random_fields(7, 5, 4, seed=41, drho=0.03, du=0.05)
+    f = oracle.init_equilibrium(box, mask, rho, u)
+    plain = oracle.init_equilibrium(oracle.Box(7, 5, 4, periodic=(0, 1, 1), tau=0.8), mask, rho, u)
+    c, _, _ = oracle.lattice()
+    fz, pz = f.reshape(19, 4, 5, 7), plain.reshape(19, 4, 5, 7)
+    checked = 0
+    for x0, x1, side, face in ((0, 1, 1, "-x"), (6, 5, -1, "+x")):
+        r, v = box.open_faces[face][:2]
+        feq = oracle.equilibrium(r, v)
+        for z in range(4):
+            for y in range(5):
+                for q in range(19):
+                    got = fz[q, z, y, x0]
+                    if c[q][0] != side:
+                        assert got == pz[q, z, y, x0]
+                    elif mask.reshape(4, 5, 7)[z, y, x1]:
+                        assert got == feq[q]
+                    else:
+                        assert abs(got - pz[q, z, y, x1]) < 1e-16
+                        checked += 1
+    assert checked > 100
+
+
+def test_face_rules_touch_only_entering_populations():
+    # applying the rules twice changes nothing (no rule reads what another
+    # writes), and init is the plain equilibrium followed by the rules
+    faces = {"-y": (1.0, (0.0, 0.03, 0.01), "zou_he_velocity"), "+y": (1.0, (0.0, 0.0, 0.0), "neumann")}
+    box = oracle.Box(5, 6, 4, periodic=(1, 0, 1), tau=0.9, force=(0.0, 1e-4, 0.0), open_faces=faces)
+    mask = li.random_mask(5, 6, 4, fraction=0.15, seed=5)
+    f = oracle.apply_open_faces(box, _noisy_state(box, mask, 51), mask)
+    np.testing.assert_array_equal(oracle.apply_open_faces(box, f, mask), f)
+    rho, u = li.random_fields(5, 6, 4, seed=52)
+    plain = oracle.init_equilibrium(oracle.Box(5, 6, 4, periodic=(1, 0, 1), tau=0.9), mask, rho, u)
+    np.testing.assert_array_equal(oracle.init_equilibrium(box, mask, rho, u),
+                                  oracle.apply_open_faces(box, plain, mask))
+
+
+def test_face_rules_need_one_axis():
+    with pytest.raises(ValueError):
+        oracle.Box(5, 6, 4, periodic=(0, 0, 1), open_faces={"-x": (1.0, (0, 0, 0), "neumann"),
+                                                            "+y": (1.0, (0, 0, 0))})
+    with pytest.raises(ValueError):
+        oracle.Box(2, 6, 4, periodic=(0, 1, 1), open_faces={"-x": (1.0, (0, 0, 0), "zou_he_pressure")})
+
+
+def test_face_rules_close_mass_and_momentum_budget():
+    # per step: the box loses the post-collision populations on links leaving
+    # through the open faces and gains the entering populations the rules set
+    # (read from the new state); with walls on y and solids inside, the
+    # exchanged force is the rest of the momentum change
+    F = (1e-4, 0.0, 2e-5)
+    faces = {"-x": (1.0, (0.03, 0.0, 0.01), "zou_he_velocity"), "+x": (0.995, (0.0, 0.0, 0.0), "zou_he_pressure")}
+    box = oracle.Box(9, 6, 5, periodic=(0, 0, 1), tau=0.75, force=F, open_faces=faces)
+    mask = li.random_mask(9, 6, 5, fraction=0.12, seed=61)
+    nf = int(np.count_nonzero(mask == 0))
+    c, _, _ = oracle.lattice()
+    rho, u = li.random_fields(9, 6, 5, seed=62)
+    f = oracle.init_equilibrium(box, mask, rho, u)
+    solid = mask.reshape(5, 6, 9).astype(bool)
+    for _ in range(3):
+        m0 = oracle.totals(box, f, mask)
+        fx = oracle.momentum_exchange(box, f, mask)
+        f1 = oracle.run(box, f, 1, mask)
+        gain_m, gain_p = 0.0, np.zeros(3)
+        fz, f1z = f.reshape(19, 5, 6, 9), f1.reshape(19, 5, 6, 9)
+        for z in range(5):
+            for y in range(6):
+                for x, side in ((0, 1), (8, -1)):
+                    if solid[z, y, x]:
+                        continue
+                    post = oracle.collide(box, fz[:, z, y, x])
+                    for q in range(19):
+                        beyond_wall = (y == 0 and c[q][1] == 1) or (y == 5 and c[q][1] == -1)
+                        if c[q][0] == side and not beyond_wall:      # enters through the face
+                            gain_m += f1z[q, z, y, x]
+                            gain_p += f1z[q, z, y, x] * c[q]
+                        leaves_wall = (y == 0 and c[q][1] == -1) or (y == 5 and c[q][1] == 1)
+                        if c[q][0] == -side and not leaves_wall:     # leaves through it
+                            gain_m -= post[q]
+                            gain_p -= post[q] * c[q]
+        m1 = oracle.totals(box, f1, mask)
+        assert abs(m1["mass"] - m0["mass"] - gain_m) < 1e-13 * m0["mass"]
+        want_p = gain_p + nf * np.array(F) - fx["solid"] - fx["wall"]
+        np.testing.assert_allclose(m1["momentum"] - m0["momentum"], want_p, rtol=0, atol=1e-13 * m0["mass"])
+        f = f1
+
+
+def test_pressure_driven_channel():
+    # Zou-He pressure faces at both ends of a walled channel drive Poiseuille
+    # flow.  At steady state the density falls linearly by (rho_in - rho_out)
+    # over the nx - 1 links between the two face layers, and every column
+    # carries the profile that the same force density G = c_s^2 drho/dx gives
+    # under halfway bounce-back: the parabola G y'(H - y') / (2 nu rho) plus
+    # the constant slip G (16 (tau - 1/2)^2 - 3) / (24 nu rho) (the closed form
+    # of the forced channel pin above), up to compressibility, O(drho)
+    nx, ny, tau = 32, 10, 0.8
+    rin, rout = 1.0015, 0.9985
+    faces = {"-x": (rin, (0.0, 0.0, 0.0), "zou_he_pressure"), "+x": (rout, (0.0, 0.0, 0.0), "zou_he_pressure")}
+    box = oracle.Box(nx, ny, 1, periodic=(0, 0, 1), tau=tau, open_faces=faces)
+    f = oracle.run(box, oracle.init_equilibrium(box), 4000)
+    rho, u = oracle.moments(box, f)
+    rho, ux = rho.reshape(ny, nx), u[0].reshape(ny, nx)
+    nu = (tau - 0.5) / 3.0
+    slip = (16.0 * (tau - 0.5) ** 2 - 3.0) / (24.0 * nu)
+    yp = np.arange(ny) + 0.5
+    for m in (8, 16, 24):
+        grad = (rho[:, m - 1].mean() - rho[:, m + 1].mean()) / 2.0
+        assert abs(grad / ((rin - rout) / (nx - 1)) - 1.0) < 1e-3
+        G, r = grad / 3.0, rho[:, m].mean()
+        want = G * yp * (ny - yp) / (2.0 * nu * r) + G * slip / r
+        assert np.max(np.abs(ux[:, m] - want)) < 3e-4 * want.max()
+    assert np.max(np.abs(u[1].reshape(ny, nx)[:, 8:25])) < 1e-3 * ux.max()  # away from the entrance regions
+
+
 # ------------------------------------------------ P5 / P6 streaming exactness
 
 def _brute_stream(box, f, mask):
