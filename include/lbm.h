@@ -135,24 +135,57 @@ lbm_status lbm_set_workspace(lbm_sim *sim, void *ws, size_t bytes);
  * Invalidates the state: lbm_init_equilibrium must be called again.  Host only. */
 lbm_status lbm_set_geometry(lbm_sim *sim, const uint8_t *mask, const int32_t periodic[3]);
 
-/* Open faces (PortLBM page, section 3.1: the inlet takes the equilibrium
- * distribution of Dirichlet values; here every open face does).  Faces are
- * numbered -x, +x, -y, +y, -z, +z.  open[k] = 1 replaces the wall beyond face
- * k, whose axis must be non-periodic, by a reservoir at equilibrium: every
- * population entering the box through face k is feq(rho[k], u[3k..3k+2]) (the
- * second-order equilibrium of the collision), and populations leaving through
- * it are dropped.  Where a link crosses two faces (an edge of the box), a wall
- * wins over an open face, and of two open faces the one on the first axis in
- * x, y, z order is used.  The entering populations of the state are always the
- * reservoir's: lbm_init_equilibrium and lbm_write_populations store them
- * whatever the inputs hold there.  Bounce-back links to solid cells and walls
- * are unchanged; links through open faces carry no momentum-exchange force.
- *   open   host int32[6], 0 or 1.
+/* Kinds of open face (the values of lbm_set_open_faces' open[k]).  PortLBM
+ * page, section 3.1, boundary paragraph: the inlet takes the equilibrium
+ * distribution of Dirichlet or Neumann values, the outlet an adapted Zou-He
+ * condition.  Each sets the populations entering the box through the face:
+ *   LBM_FACE_EQUILIBRIUM      feq(rho[k], u[k]): a reservoir (Dirichlet);
+ *   LBM_FACE_NEUMANN          feq of the density and velocity of the cell one
+ *                             layer inward along the face normal, at the same
+ *                             time (zero normal gradient); feq(rho[k], u[k])
+ *                             where that cell is solid;
+ *   LBM_FACE_ZOU_HE_PRESSURE  Zou and He (Phys. Fluids 9, 1591, 1997):
+ *                             density rho[k] and the tangential components of
+ *                             u[k]; the normal velocity follows from mass;
+ *   LBM_FACE_ZOU_HE_VELOCITY  Zou-He with velocity u[k]; the density follows
+ *                             from mass (rho[k] unused).
+ * The Zou-He kinds take each entering population from its opposite by
+ * non-equilibrium bounce-back with the transverse momentum correction of the
+ * 3-D lattice (Hecht and Harting, J. Stat. Mech. 2010, P01018), the momentum
+ * being rho u - F/2 under a body force, so that a face cell's density
+ * (pressure) or velocity (velocity) and its tangential momentum are exactly the
+ * prescribed ones. */
+typedef enum {
+    LBM_FACE_CLOSED = 0,
+    LBM_FACE_EQUILIBRIUM = 1,
+    LBM_FACE_NEUMANN = 2,
+    LBM_FACE_ZOU_HE_PRESSURE = 3,
+    LBM_FACE_ZOU_HE_VELOCITY = 4
+} lbm_face_kind;
+
+/* Open faces.  Faces are numbered -x, +x, -y, +y, -z, +z.  open[k] != 0
+ * replaces the wall beyond face k, whose axis must be non-periodic, by an
+ * open boundary of kind open[k] (lbm_face_kind): populations leaving through
+ * it are dropped, and those entering through it are set by its kind.  Where a
+ * link crosses two faces (an edge of the box), a wall wins over an open face,
+ * and of two open faces the one on the first axis in x, y, z order is used.
+ * The entering populations of the state always obey the faces' kinds:
+ * lbm_init_equilibrium and lbm_write_populations apply them to what they
+ * store (lbm_load_state stores its input as it is), and every step applies
+ * them to the state it leaves (the kinds other than EQUILIBRIUM by a pass over
+ * the face's cells after the step).  Bounce-back links to solid cells and
+ * walls are unchanged; links through open faces carry no momentum-exchange
+ * force.
+ *   open   host int32[6], lbm_face_kind values.
  *   rho    host double[6] (> 0 where open), u host double[18]; read only
- *          where open[k] = 1 (may be NULL when no face is open).
+ *          where open[k] != 0 (may be NULL when no face is open).
  * lbm_set_geometry resets all faces to closed.  Invalidates the state.
- * LBM_ERR_INVALID_ARGUMENT for an open face on a periodic axis or a
- * non-finite or non-positive reservoir.  Host only. */
+ * LBM_ERR_INVALID_ARGUMENT for an open face on a periodic axis, an unknown
+ * kind, a non-finite or non-positive rho or non-finite u, or a
+ * ZOU_HE_VELOCITY face whose inward velocity component is >= 1;
+ * LBM_ERR_UNSUPPORTED if a kind other than EQUILIBRIUM is used while open
+ * faces lie on more than one axis or the box is less than 3 cells long on
+ * their axis.  Host only. */
 lbm_status lbm_set_open_faces(lbm_sim *sim, const int32_t open[6], const double rho[6], const double u[18]);
 
 /* f(0) = equilibrium(rho, u) on fluid cells, 0 on solid cells; t := 0.

@@ -165,14 +165,21 @@ def lbm_set_geometry(sim, mask, periodic):
 FACES = ("-x", "+x", "-y", "+y", "-z", "+z")
 
 
+# open-face kinds, in the order of lbm_face_kind from LBM_FACE_EQUILIBRIUM (1) on
+FACE_KINDS = ("equilibrium", "neumann", "zou_he_pressure", "zou_he_velocity")
+
+
 def lbm_set_open_faces(sim, faces):
-    """faces: {face name: (rho, (ux, uy, uz))}; faces not named are closed."""
+    """faces: {face name: (rho, (ux, uy, uz)) or (rho, (ux, uy, uz), kind)},
+    kind one of FACE_KINDS (default "equilibrium"); faces not named are closed."""
     op = (_i32 * 6)()
     rho = (ctypes.c_double * 6)(*([1.0] * 6))
     u = (ctypes.c_double * 18)()
-    for k, (r, v) in faces.items():
+    for k, spec in faces.items():
+        r, v = spec[0], spec[1]
+        kind = spec[2] if len(spec) > 2 else "equilibrium"
         i = FACES.index(k)
-        op[i] = 1
+        op[i] = 1 + FACE_KINDS.index(kind)
         rho[i] = float(r)
         for a in range(3):
             u[3 * i + a] = float(v[a])

@@ -22,7 +22,12 @@
 #include "../../include/lbm.h"
 #include "d3q19.hpp"
 #include "kernels.hpp"
+#include "kernels_faces.hpp"
 #include "launch.hpp"
+
+static_assert(lbm::kRuleNeumann == LBM_FACE_NEUMANN && lbm::kRuleZouHePressure == LBM_FACE_ZOU_HE_PRESSURE &&
+                  lbm::kRuleZouHeVelocity == LBM_FACE_ZOU_HE_VELOCITY,
+              "face kinds of the kernels and of the C ABI");
 
 struct lbm_sim {
     lbm_desc d;
@@ -39,6 +44,7 @@ struct lbm_sim {
     double omega;
     hipError_t last_hip;  // status of the last failed launch (hipSuccess if none)
     uint32_t open;        // open faces (bit k: -x, +x, -y, +y, -z, +z)
+    int32_t face_kind[6]; // 0 closed, 1 reservoir, 2 Neumann, 3 Zou-He pressure, 4 Zou-He velocity
     double face_rho[6];
     double face_u[6][3];
 };
@@ -90,6 +96,15 @@ size_t buffer_bytes(const lbm_desc& d)
     return (size_t)lbm::kQ * cells * elem_size(d);
 }
 
+// open faces that are equilibrium reservoirs (applied inside the steps)
+uint32_t reservoir_bits(const lbm_sim* s)
+{
+    uint32_t b = 0;
+    for (int k = 0; k < 6; ++k)
+        if (((s->open >> k) & 1u) && s->face_kind[k] == LBM_FACE_EQUILIBRIUM) b |= 1u << k;
+    return b;
+}
+
 lbm::LaunchGeom geom_of(const lbm_sim* s)
 {
     lbm::LaunchGeom g{};
@@ -98,6 +113,7 @@ lbm::LaunchGeom geom_of(const lbm_sim* s)
     g.nz = s->d.nz;
     for (int a = 0; a < 3; ++a) g.periodic[a] = s->periodic[a];
     g.open = s->open;
+    g.res = reservoir_bits(s);
     g.mask = s->mask;
     return g;
 }
@@ -114,7 +130,9 @@ lbm::LaunchPhys phys_of(const lbm_sim* s)
     for (int k = 0; k < 6; ++k) {
         p.face_rho[k] = s->face_rho[k];
         for (int a = 0; a < 3; ++a) p.face_u[k][a] = s->face_u[k][a];
+        p.face_kind[k] = s->face_kind[k];
     }
+    p.res = reservoir_bits(s);
     return p;
 }
 
@@ -155,6 +173,24 @@ lbm_status io(lbm_sim* s, int op, void* out0, void* out1, const void* in0, const
     else
         e = lbm::launch_io<double>(s->d.layout, st, op, (double*)a, (double*)b, g, p, (double*)out0,
                                    (double*)out1, (const double*)in0, (const double*)in1, s->stream);
+    return hip_status(s, e);
+}
+
+// The face rules of the open faces that are not reservoirs, on the stored
+// state (after an initialisation, a write of populations, or a step).
+lbm_status apply_face_rules(lbm_sim* s)
+{
+    if ((s->open & ~reservoir_bits(s)) == 0) return LBM_OK;
+    const lbm::LaunchGeom g = geom_of(s);
+    const lbm::LaunchPhys p = phys_of(s);
+    const int st = state_kind(s);
+    void* a = s->d.scheme == LBM_SCHEME_AB ? s->buf[s->cur] : s->buf[0];
+    const lbm::CompactTables* t = compact(s->d) ? &s->tables : nullptr;
+    hipError_t e;
+    if (s->d.precision == LBM_F32)
+        e = lbm::launch_face_rules<float>(s->d.layout, st, (float*)a, g, t, p, s->stream);
+    else
+        e = lbm::launch_face_rules<double>(s->d.layout, st, (double*)a, g, t, p, s->stream);
     return hip_status(s, e);
 }
 
@@ -263,6 +299,7 @@ lbm_status lbm_set_geometry(lbm_sim* sim, const uint8_t* mask, const int32_t per
     sim->mask = mask;
     for (int a = 0; a < 3; ++a) sim->periodic[a] = periodic[a];
     sim->open = 0;
+    for (int k = 0; k < 6; ++k) sim->face_kind[k] = 0;
     sim->initialized = false;
     sim->t = 0;
     sim->cur = 0;
@@ -272,19 +309,34 @@ lbm_status lbm_set_geometry(lbm_sim* sim, const uint8_t* mask, const int32_t per
 lbm_status lbm_set_open_faces(lbm_sim* sim, const int32_t open[6], const double rho[6], const double u[18])
 {
     if (sim == nullptr || open == nullptr) return LBM_ERR_INVALID_ARGUMENT;
-    uint32_t bits = 0;
+    uint32_t bits = 0, axes = 0;
+    bool rules = false;
     for (int k = 0; k < 6; ++k) {
-        if (open[k] != 0 && open[k] != 1) return LBM_ERR_INVALID_ARGUMENT;
+        if (open[k] < 0 || open[k] > LBM_FACE_ZOU_HE_VELOCITY) return LBM_ERR_INVALID_ARGUMENT;
         if (!open[k]) continue;
         if (sim->periodic[k / 2] || rho == nullptr || u == nullptr) return LBM_ERR_INVALID_ARGUMENT;
         if (!std::isfinite(rho[k]) || !(rho[k] > 0.0)) return LBM_ERR_INVALID_ARGUMENT;
         for (int a = 0; a < 3; ++a)
             if (!std::isfinite(u[3 * k + a])) return LBM_ERR_INVALID_ARGUMENT;
+        // the velocity rule's density is (par + 2 out) / (1 - sigma u_a)
+        const double sg = (k % 2 == 0) ? 1.0 : -1.0;
+        if (open[k] == LBM_FACE_ZOU_HE_VELOCITY && !(sg * u[3 * k + k / 2] < 1.0)) return LBM_ERR_INVALID_ARGUMENT;
         bits |= 1u << k;
+        axes |= 1u << (k / 2);
+        rules = rules || open[k] != LBM_FACE_EQUILIBRIUM;
+    }
+    if (rules) {
+        // every open face on one axis, at least 3 cells along it: the rules'
+        // cells are then independent (none reads what another writes)
+        const int64_t n[3] = {sim->d.nx, sim->d.ny, sim->d.nz};
+        if (axes != 1u && axes != 2u && axes != 4u) return LBM_ERR_UNSUPPORTED;
+        const int a = axes == 1u ? 0 : axes == 2u ? 1 : 2;
+        if (n[a] < 3) return LBM_ERR_UNSUPPORTED;
     }
     sim->open = bits;
     for (int k = 0; k < 6; ++k) {
         const bool o = (bits >> k) & 1u;
+        sim->face_kind[k] = o ? open[k] : 0;
         sim->face_rho[k] = o ? rho[k] : 1.0;
         for (int a = 0; a < 3; ++a) sim->face_u[k][a] = o ? u[3 * k + a] : 0.0;
     }
@@ -305,7 +357,8 @@ lbm_status lbm_init_equilibrium(lbm_sim* sim, const void* rho, const void* u)
         const lbm_status b = build_compact(sim);
         if (b != LBM_OK) return b;
     }
-    const lbm_status r = io(sim, lbm::kWriteEq, nullptr, nullptr, rho, u);
+    lbm_status r = io(sim, lbm::kWriteEq, nullptr, nullptr, rho, u);
+    if (r == LBM_OK) r = apply_face_rules(sim);
     if (r == LBM_OK) sim->initialized = true;
     return r;
 }
@@ -351,6 +404,8 @@ lbm_status run_steps(lbm_sim* sim, int64_t n, void* rho, void* u)
         if (e != hipSuccess) return hip_status(sim, e);
         if (sim->d.scheme == LBM_SCHEME_AB) sim->cur = 1 - sim->cur;
         sim->t += 1;
+        const lbm_status r = apply_face_rules(sim);
+        if (r != LBM_OK) return r;
     }
     return LBM_OK;
 }
@@ -391,7 +446,8 @@ lbm_status lbm_write_populations(lbm_sim* sim, const void* f)
 {
     if (sim == nullptr || f == nullptr) return LBM_ERR_INVALID_ARGUMENT;
     if (!sim->initialized) return LBM_ERR_BAD_STATE;
-    return io(sim, lbm::kWriteF, nullptr, nullptr, f, nullptr);
+    const lbm_status r = io(sim, lbm::kWriteF, nullptr, nullptr, f, nullptr);
+    return r == LBM_OK ? apply_face_rules(sim) : r;
 }
 
 lbm_status lbm_save_state(lbm_sim* sim, void* s)

@@ -38,7 +38,8 @@ struct Geom {
     uint32_t per_x, per_y, per_z;  // 1 = periodic, 0 = bounce-back wall beyond both faces
     uint32_t ntx, nty, ntiles;     // tiles per x-row of tiles, per y-column, total
     uint32_t xk;                   // workgroup chunk per XCD turn (1 = hardware order)
-    uint32_t open;                 // bit k: face k (-x, +x, -y, +y, -z, +z) is open
+    uint32_t open;                 // bit k: face k (-x, +x, -y, +y, -z, +z) is an open reservoir
+    uint32_t fix;                  // bit k: face k is open with a face rule (a wall to the steps)
     uint64_t n;                    // cells
     const uint8_t* mask;           // uint8[n], nonzero = solid; may be null
 };
@@ -59,6 +60,7 @@ struct Phys {
     // Open faces: the shifted equilibrium feq_q(rho_k, u_k) - w_q of face k's
     // reservoir, the value of every population entering through face k.
     T seq[6][kQ];
+    uint32_t res;  // bit k: face k is a reservoir (the others' entering values are stored)
 };
 
 // State transfers: canonical populations f out / in, moments out, equilibrium
@@ -144,18 +146,11 @@ __device__ __forceinline__ uint32_t xcd_chunked(uint32_t hw, uint32_t k)
     return ((l / k) * 8u + x) * k + l % k;
 }
 
-// Decode this work-item's cell; false if it lies outside the box.
-__device__ __forceinline__ bool locate(const Geom& g, Cell& c)
+// Index, wrapped neighbour offsets and face flags of the cell (c.x, c.y, c.z).
+// A face with a face rule is a wall here: the steps bounce its links back
+// into the own slots, whose entering values the rule then replaces.
+__device__ __forceinline__ void fill_cell(const Geom& g, Cell& c)
 {
-    const uint32_t tile = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
-    if (tile >= g.ntiles) return false;
-    const uint32_t tx = tile % g.ntx;
-    const uint32_t rest = tile / g.ntx;
-    const uint32_t ty = rest % g.nty;
-    c.z = rest / g.nty;
-    c.x = tx * blockDim.x + threadIdx.x;
-    c.y = ty * blockDim.y + threadIdx.y;
-    if (c.x >= g.nx || c.y >= g.ny) return false;
     c.id = c.x + g.nx * (c.y + g.ny * c.z);
     const uint32_t xm = c.x == 0 ? g.nx - 1 : c.x - 1, xp = c.x + 1 == g.nx ? 0 : c.x + 1;
     const uint32_t ym = c.y == 0 ? g.ny - 1 : c.y - 1, yp = c.y + 1 == g.ny ? 0 : c.y + 1;
@@ -180,6 +175,21 @@ __device__ __forceinline__ bool locate(const Geom& g, Cell& c)
             c.wall[a][sd] = at[a][sd] && !open;
             c.open[a][sd] = at[a][sd] && open;
         }
+}
+
+// Decode this work-item's cell; false if it lies outside the box.
+__device__ __forceinline__ bool locate(const Geom& g, Cell& c)
+{
+    const uint32_t tile = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
+    if (tile >= g.ntiles) return false;
+    const uint32_t tx = tile % g.ntx;
+    const uint32_t rest = tile / g.ntx;
+    const uint32_t ty = rest % g.nty;
+    c.z = rest / g.nty;
+    c.x = tx * blockDim.x + threadIdx.x;
+    c.y = ty * blockDim.y + threadIdx.y;
+    if (c.x >= g.nx || c.y >= g.ny) return false;
+    fill_cell(g, c);
     return true;
 }
 
@@ -193,6 +203,26 @@ __device__ __forceinline__ bool beyond_wall(const Cell& c, int dx, int dy, int d
 {
     return (dx < 0 && c.wall[0][0]) || (dx > 0 && c.wall[0][1]) || (dy < 0 && c.wall[1][0]) ||
            (dy > 0 && c.wall[1][1]) || (dz < 0 && c.wall[2][0]) || (dz > 0 && c.wall[2][1]);
+}
+
+// x + (dx, dy, dz) lies beyond a face with a face rule and beyond no wall
+// (such links carry flux, not force on a wall).
+__device__ __forceinline__ bool beyond_rule_face(const Geom& g, const Cell& c, int dx, int dy, int dz)
+{
+    const int d[3] = {dx, dy, dz};
+    bool rule = false, wall = false;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        if (d[a] == 0) continue;
+        const int sd = d[a] < 0 ? 0 : 1;
+        if (!c.wall[a][sd]) continue;
+        if ((g.fix >> (2 * a + sd)) & 1u) {
+            rule = true;
+        } else {
+            wall = true;
+        }
+    }
+    return rule && !wall;
 }
 
 __device__ __forceinline__ bool beyond_open(const Cell& c, int dx, int dy, int dz)

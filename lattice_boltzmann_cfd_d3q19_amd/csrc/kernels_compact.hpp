@@ -36,6 +36,13 @@ constexpr uint32_t kOpen = 0xFFFFFFF0u;
 __device__ __forceinline__ bool no_fluid(uint32_t nbv) { return nbv >= kOpen; }
 __device__ __forceinline__ bool bounced(uint32_t nbv) { return nbv >= kWall; }
 __device__ __forceinline__ bool is_open(uint32_t nbv) { return nbv >= kOpen && nbv < kWall; }
+// beyond an open face that is a reservoir (res: bit k for face k); the other
+// open faces have face rules, and their entering values are stored like
+// bounced ones
+__device__ __forceinline__ bool is_res(uint32_t nbv, uint32_t res)
+{
+    return is_open(nbv) && ((res >> ((nbv - kOpen) & 7u)) & 1u);
+}
 
 // Reservoir value of population q entering through the open face that the
 // table entry nbv (of the upstream cell x - c_q) names.
@@ -55,7 +62,7 @@ template <int q = 0, typename T>
 __device__ __forceinline__ void apply_open_nb(T (&f)[kQ], const uint32_t (&nb)[kQ], const Phys<T>& p)
 {
     if constexpr (q < kQ) {
-        if constexpr (q != 9) f[q] = is_open(nb[opp(q)]) ? entering_value_nb<q>(p, nb[opp(q)]) : f[q];
+        if constexpr (q != 9) f[q] = is_res(nb[opp(q)], p.res) ? entering_value_nb<q>(p, nb[opp(q)]) : f[q];
         apply_open_nb<q + 1>(f, nb, p);
     }
 }
@@ -81,7 +88,8 @@ struct CompactGeom {
     uint32_t pxy;  // (nx + 2)(ny + 2)
     uint32_t s;    // population stride (fluid cells rounded up to 64); 2 s sizeof(T) < 2^32
     uint32_t xk;   // workgroup chunk per XCD turn of the gather kernels (1 = hardware order)
-    uint32_t open; // bit k: face k is open (some table entries are kOpen + k)
+    uint32_t open; // bit k: face k is an open reservoir (table entries kOpen + k mark
+                   // every open face; the rule faces act as walls to the steps)
 };
 
 // Compact indices of the 18 neighbours x + c_d (kInvalid: solid, kWall: wall),
@@ -205,7 +213,7 @@ template <int d = 0, typename T>
 __device__ __forceinline__ void open_outflow(T (&f)[kQ], const uint32_t (&nb)[kQ], const Phys<T>& p)
 {
     if constexpr (d < kQ) {
-        if constexpr (d != 9) f[d] = is_open(nb[d]) ? entering_value_nb<opp(d)>(p, nb[d]) : f[d];
+        if constexpr (d != 9) f[d] = is_res(nb[d], p.res) ? entering_value_nb<opp(d)>(p, nb[d]) : f[d];
         open_outflow<d + 1>(f, nb, p);
     }
 }
@@ -404,7 +412,7 @@ __global__ void __launch_bounds__(kBlockThreads) io_compact_kernel(T* __restrict
             if (cg.open) apply_open_nb(f, nb, p);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            if (S != kAAEven && is_open(nb[opp(q)])) continue;
+            if (S != kAAEven && is_res(nb[opp(q)], p.res)) continue;
             *compact_state_slot<S>(a, s, i, nb, q) = f[q];
         }
     }

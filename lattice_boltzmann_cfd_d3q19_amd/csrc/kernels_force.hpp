@@ -9,8 +9,8 @@
 // that starts from the stored state: gather the cell's 19 populations through
 // the state map, collide (the same function as the step kernels), and sum
 // 2 f*_q c_q over the bounce-back links, separately for links that end in a
-// solid cell of the mask and for links that leave the box through a
-// non-periodic face.  Sums are in double: per workgroup in a fixed order,
+// solid cell of the mask and for links that leave the box through a wall
+// (open faces carry flux, not force).  Sums are in double: per workgroup in a fixed order,
 // then over the workgroups in a fixed order, so the result is deterministic.
 #pragma once
 
@@ -89,8 +89,11 @@ __global__ void __launch_bounds__(kBlockThreads) mex_kernel(T* __restrict__ a, G
         for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g.n, c, bits, q);
         if constexpr (S != kAAEven) apply_open(s, open_bits(g, c), p, c);
         collide<T, true>(s, p);
-        // x + c_q is solid or beyond a wall iff the upstream bit of opp(q) is set
-        add_links(acc, s, c, [&](int q) { return ((bits >> opp(q)) & 1u) != 0; });
+        // x + c_q is solid or beyond a wall iff the upstream bit of opp(q) is
+        // set; a face with a face rule sets it too, but its links carry flux
+        add_links(acc, s, c, [&](int q) {
+            return ((bits >> opp(q)) & 1u) != 0 && !beyond_rule_face(g, c, kCx[q], kCy[q], kCz[q]);
+        });
     }
     block_sum6(acc, partial + 6 * (size_t)blockIdx.x);
 }

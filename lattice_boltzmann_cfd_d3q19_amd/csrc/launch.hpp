@@ -10,6 +10,7 @@ struct LaunchGeom {
     int64_t nx, ny, nz;
     int32_t periodic[3];
     uint32_t open;  // bit k: face k (-x, +x, -y, +y, -z, +z) is open (its axis is not periodic)
+    uint32_t res;   // bit k: open face k is an equilibrium reservoir (the others have face rules)
     const uint8_t* mask;
 };
 
@@ -17,8 +18,10 @@ struct LaunchPhys {
     double omega;
     double force[3];
     bool has_force;
-    double face_rho[6];     // reservoir of each open face
+    double face_rho[6];     // prescribed values of each open face
     double face_u[6][3];
+    int32_t face_kind[6];   // 0 closed, 1 reservoir, kRuleNeumann, kRuleZouHePressure, kRuleZouHeVelocity
+    uint32_t res;           // bit k: face_kind[k] == 1
 };
 
 // One fused step of kind `kind` (kAB: a = source, b = destination; kAAEven /
@@ -61,6 +64,13 @@ hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& g, const 
 template <typename T>
 hipError_t launch_io_compact(int state, int op, T* a, const LaunchGeom& g, const CompactTables& t,
                              const LaunchPhys& p, T* out0, T* out1, const T* in0, const T* in1, hipStream_t s);
+
+// Face rules of the open faces that are not reservoirs, applied to the state
+// of kind `state` that a step (or an initialisation) just left in `a`; one
+// launch per such face.  t: the compact tables, or null for a dense layout.
+template <typename T>
+hipError_t launch_face_rules(int layout, int state, T* a, const LaunchGeom& g, const CompactTables* t,
+                             const LaunchPhys& p, hipStream_t s);
 
 // Momentum exchange with the solids for the step that starts from the stored
 // state: force[0..2] on the mask's solid cells, force[3..5] on the walls

@@ -10,6 +10,8 @@ template hipError_t launch_step_compact<float>(int, float*, float*, const Launch
                                                const LaunchPhys&, float*, float*, hipStream_t);
 template hipError_t launch_io_compact<float>(int, int, float*, const LaunchGeom&, const CompactTables&,
                                              const LaunchPhys&, float*, float*, const float*, const float*, hipStream_t);
+template hipError_t launch_face_rules<float>(int, int, float*, const LaunchGeom&, const CompactTables*, const LaunchPhys&,
+                                            hipStream_t);
 template hipError_t launch_momentum_exchange<float>(int, int, float*, const LaunchGeom&, const CompactTables*,
                                                     const LaunchPhys&, double*, double*, hipStream_t);
 

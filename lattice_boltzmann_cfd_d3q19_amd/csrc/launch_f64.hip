@@ -10,6 +10,8 @@ template hipError_t launch_step_compact<double>(int, double*, double*, const Lau
                                                const LaunchPhys&, double*, double*, hipStream_t);
 template hipError_t launch_io_compact<double>(int, int, double*, const LaunchGeom&, const CompactTables&,
                                              const LaunchPhys&, double*, double*, const double*, const double*, hipStream_t);
+template hipError_t launch_face_rules<double>(int, int, double*, const LaunchGeom&, const CompactTables*, const LaunchPhys&,
+                                            hipStream_t);
 template hipError_t launch_momentum_exchange<double>(int, int, double*, const LaunchGeom&, const CompactTables*,
                                                     const LaunchPhys&, double*, double*, hipStream_t);
 }  // namespace lbm

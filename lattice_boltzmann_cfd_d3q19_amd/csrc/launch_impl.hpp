@@ -5,6 +5,7 @@
 
 #include "kernels.hpp"
 #include "kernels_compact.hpp"
+#include "kernels_faces.hpp"
 #include "kernels_force.hpp"
 #include "launch.hpp"
 
@@ -31,7 +32,8 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
     g.per_x = lg.periodic[0] != 0;
     g.per_y = lg.periodic[1] != 0;
     g.per_z = lg.periodic[2] != 0;
-    g.open = lg.open;
+    g.open = lg.res;
+    g.fix = lg.open & ~lg.res;
     g.ntx = (g.nx + bx - 1) / bx;
     g.nty = (g.ny + by - 1) / by;
     g.ntiles = g.ntx * g.nty * g.nz;
@@ -84,6 +86,7 @@ inline Phys<T> make_phys(const LaunchPhys& lp)
             p.seq[k][q] = (T)(feq - (double)wt);
         }
     }
+    p.res = lp.res;
     return p;
 }
 
@@ -136,7 +139,7 @@ hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, c
     const Shape s = make_shape(lg, layout == kCollision);
     const Phys<T> p = make_phys<T>(lp);
     const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz};
-    const int bnd = lg.open != 0 ? 2 : (lg.mask != nullptr || !lg.periodic[0] || !lg.periodic[1] || !lg.periodic[2]);
+    const int bnd = lg.res != 0 ? 2 : (lg.mask != nullptr || !lg.periodic[0] || !lg.periodic[1] || !lg.periodic[2]);
     switch (layout) {
     case kStream: return launch_step_l<T, kStream>(kind, a, b, s, p, mo, bnd, lp.has_force, st);
     case kBundle: return launch_step_l<T, kBundle>(kind, a, b, s, p, mo, bnd, lp.has_force, st);
@@ -208,7 +211,7 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     g.px = (uint32_t)lg.nx + 2;
     g.pxy = (uint32_t)((lg.nx + 2) * (lg.ny + 2));
     g.s = (uint32_t)t.stride;
-    g.open = lg.open;
+    g.open = lg.res;
     // XCD chunk of the gather kernels: an eighth of the workgroups of an
     // average z-plane, so the rows at z +- 1 fall on the same XCD as the
     // rows they are gathered by.  Measured (odd in-place step): 256^3 porous
@@ -323,6 +326,95 @@ hipError_t launch_io_compact(int state, int op, T* a, const LaunchGeom& lg, cons
     case kAAOdd: return launch_io_compact_s<T, kAAOdd>(op, a, cg, s, p, o0, o1, i0, i1, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+// ------------------------------------------------------------ face rules
+
+template <typename T>
+inline FaceRule<T> make_face_rule(const LaunchGeom& lg, const LaunchPhys& lp, const Phys<T>& p, int k)
+{
+    FaceRule<T> r{};
+    const int ax = k / 2;
+    const double sg = (k % 2 == 0) ? 1.0 : -1.0;
+    const double rho = lp.face_rho[k], *u = lp.face_u[k];
+    r.k = (uint32_t)k;
+    r.kind = (uint32_t)lp.face_kind[k];
+    r.nx = (uint32_t)lg.nx;
+    r.ny = (uint32_t)lg.ny;
+    r.nz = (uint32_t)lg.nz;
+    r.n0 = ax == 0 ? r.ny : r.nx;
+    r.ncell = ax == 0 ? r.ny * r.nz : ax == 1 ? r.nx * r.nz : r.nx * r.ny;
+    r.drho = (T)(rho - 1.0);
+    for (int t = 0; t < 3; ++t) {
+        r.jt[t] = (T)(rho * u[t] - 0.5 * lp.force[t]);
+        r.u[t] = (T)u[t];
+    }
+    r.ua_s = (T)(sg * u[ax]);
+    r.inv_den = (T)(1.0 / (1.0 - sg * u[ax]));
+    r.hfa_s = (T)(0.5 * sg * lp.force[ax]);
+    for (int q = 0; q < kQ; ++q) r.seq[q] = p.seq[k][q];
+    return r;
+}
+
+template <typename T, int L>
+hipError_t launch_face_l(int state, T* a, const Geom& g, const Phys<T>& p, const FaceRule<T>& r, hipStream_t st)
+{
+    Geom gg = g;
+    Phys<T> pp = p;
+    FaceRule<T> rr = r;
+    void* args[] = {&a, &gg, &pp, &rr};
+    const dim3 grid((r.ncell + kBlockThreads - 1) / kBlockThreads), block(kBlockThreads);
+    switch (state) {
+    case kAB: return hipLaunchKernel((const void*)&face_kernel<T, L, kAB>, grid, block, args, 0, st);
+    case kAAEven: return hipLaunchKernel((const void*)&face_kernel<T, L, kAAEven>, grid, block, args, 0, st);
+    case kAAOdd: return hipLaunchKernel((const void*)&face_kernel<T, L, kAAOdd>, grid, block, args, 0, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_face_compact(int state, T* a, const CompactGeom& cg, const Phys<T>& p, const FaceRule<T>& r,
+                               hipStream_t st)
+{
+    CompactGeom gg = cg;
+    Phys<T> pp = p;
+    FaceRule<T> rr = r;
+    void* args[] = {&a, &gg, &pp, &rr};
+    const dim3 grid((r.ncell + kBlockThreads - 1) / kBlockThreads), block(kBlockThreads);
+    switch (state) {
+    case kAB: return hipLaunchKernel((const void*)&face_compact_kernel<T, kAB>, grid, block, args, 0, st);
+    case kAAEven: return hipLaunchKernel((const void*)&face_compact_kernel<T, kAAEven>, grid, block, args, 0, st);
+    case kAAOdd: return hipLaunchKernel((const void*)&face_compact_kernel<T, kAAOdd>, grid, block, args, 0, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_face_rules(int layout, int state, T* a, const LaunchGeom& lg, const CompactTables* t,
+                             const LaunchPhys& lp, hipStream_t st)
+{
+    const uint32_t rules = lg.open & ~lg.res;
+    if (rules == 0) return hipSuccess;
+    const Shape sh = make_shape(lg);
+    const Phys<T> p = make_phys<T>(lp);
+    for (int k = 0; k < 6; ++k) {
+        if (!((rules >> k) & 1u)) continue;
+        const FaceRule<T> r = make_face_rule<T>(lg, lp, p, k);
+        if (r.ncell == 0) continue;
+        hipError_t e;
+        if (t != nullptr) {
+            e = launch_face_compact<T>(state, a, compact_geom(lg, *t), p, r, st);
+        } else {
+            switch (layout) {
+            case kStream: e = launch_face_l<T, kStream>(state, a, sh.g, p, r, st); break;
+            case kBundle: e = launch_face_l<T, kBundle>(state, a, sh.g, p, r, st); break;
+            case kCollision: e = launch_face_l<T, kCollision>(state, a, sh.g, p, r, st); break;
+            default: return hipErrorInvalidValue;
+            }
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // ------------------------------------------------------ momentum exchange

@@ -70,9 +70,11 @@ class Lattice:
                    "lbm_set_geometry")
 
     def set_open_faces(self, faces):
-        """faces: {"-x" | "+x" | "-y" | "+y" | "-z" | "+z": (rho, (ux, uy, uz))} on
-        non-periodic axes; populations entering through them are the
-        reservoir's equilibrium.  Call after set_geometry, before init."""
+        """faces: {"-x" | "+x" | "-y" | "+y" | "-z" | "+z": (rho, (ux, uy, uz)[, kind])}
+        on non-periodic axes, kind one of capi.FACE_KINDS ("equilibrium" by
+        default: a reservoir whose equilibrium enters the box; "neumann",
+        "zou_he_pressure", "zou_he_velocity").  Call after set_geometry,
+        before init."""
         capi.check(capi.lbm_set_open_faces(self.handle, faces), "lbm_set_open_faces")
 
     def _dev(self, a, shape):

@@ -164,6 +164,48 @@ def test_open_faces_arguments():
     assert capi.lbm_set_open_faces(None, {}) == capi.LBM_ERR_INVALID_ARGUMENT
 
 
+def _raw_open_faces(h, kinds, rho=1.0, u=(0.0, 0.0, 0.0)):
+    import ctypes
+    op = (ctypes.c_int32 * 6)(*kinds)
+    r = (ctypes.c_double * 6)(*([rho] * 6))
+    v = (ctypes.c_double * 18)(*(list(u) * 6))
+    return capi._lib.lbm_set_open_faces(h, op, r, v)
+
+
+def test_face_kinds_arguments():
+    st, h = capi.lbm_create(capi.make_desc(8, 8, 8), FAKE)
+    assert st == capi.LBM_OK
+    try:
+        assert capi.lbm_set_geometry(h, None, (0, 0, 1)) == capi.LBM_OK
+        for kind in capi.FACE_KINDS:
+            assert capi.lbm_set_open_faces(h, {"-x": (1.0, (0.02, 0, 0), kind),
+                                                "+x": (1.0, (0.0, 0, 0), "zou_he_pressure")}) == capi.LBM_OK
+        # kinds beyond the enum
+        assert _raw_open_faces(h, (5, 0, 0, 0, 0, 0)) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert _raw_open_faces(h, (-1, 0, 0, 0, 0, 0)) == capi.LBM_ERR_INVALID_ARGUMENT
+        # a rule face needs every open face on its axis
+        assert capi.lbm_set_open_faces(h, {"-x": (1.0, (0, 0, 0), "neumann"),
+                                           "+y": (1.0, (0, 0, 0))}) == capi.LBM_ERR_UNSUPPORTED
+        assert capi.lbm_set_open_faces(h, {"-x": (1.0, (0, 0, 0)), "+y": (1.0, (0, 0, 0))}) == capi.LBM_OK
+        # the velocity rule's density needs 1 - sigma u_a > 0 (inward speed below 1)
+        assert capi.lbm_set_open_faces(h, {"-x": (1.0, (1.0, 0, 0), "zou_he_velocity")}) == \
+            capi.LBM_ERR_INVALID_ARGUMENT
+        assert capi.lbm_set_open_faces(h, {"+x": (1.0, (-1.0, 0, 0), "zou_he_velocity")}) == \
+            capi.LBM_ERR_INVALID_ARGUMENT
+        assert capi.lbm_set_open_faces(h, {"+x": (1.0, (1.0, 0, 0), "zou_he_velocity")}) == capi.LBM_OK
+    finally:
+        capi.lbm_destroy(h)
+    # at least 3 cells along the rule face's axis
+    st, h = capi.lbm_create(capi.make_desc(2, 8, 8), FAKE)
+    assert st == capi.LBM_OK
+    try:
+        assert capi.lbm_set_geometry(h, None, (0, 1, 1)) == capi.LBM_OK
+        assert capi.lbm_set_open_faces(h, {"-x": (1.0, (0, 0, 0), "zou_he_pressure")}) == capi.LBM_ERR_UNSUPPORTED
+        assert capi.lbm_set_open_faces(h, {"-x": (1.0, (0, 0, 0))}) == capi.LBM_OK
+    finally:
+        capi.lbm_destroy(h)
+
+
 def test_null_handle_and_status_strings():
     assert capi.lbm_destroy(None) == capi.LBM_OK
     assert capi.lbm_time(None) == -1

@@ -1,6 +1,7 @@
-"""Open faces (reservoirs at equilibrium) on the GPU against the oracle:
-canonical populations after 100 / 101 steps from the same seeded inputs, every
-layout and scheme, fp32 and fp64, and the uniform-stream fixed point."""
+"""Open faces on the GPU against the oracle: reservoirs at equilibrium and the
+face rules (Neumann, Zou-He pressure and velocity).  Canonical populations
+after 100 / 101 steps from the same seeded inputs, every layout and scheme,
+fp32 and fp64; the uniform-stream fixed point; no force on rule-face links."""
 import numpy as np
 import pytest
 
@@ -25,6 +26,25 @@ def _open_case(name):
         faces = {"-x": (1.01, (0.03, 0.01, 0.0)), "+x": (0.99, (0.02, 0.0, -0.01)),
                  "-y": (1.0, (0.0, 0.02, 0.01)), "+z": (1.02, (0.01, -0.01, -0.02))}
         mask = li.random_mask(17, 15, 13, fraction=0.1, seed=9)
+    elif name == "zou_he_channel":
+        # Zou-He velocity inlet and pressure outlet on x, walls in y (edges
+        # where the wall wins), periodic z, a body force and a sphere
+        shape, per, tau, F = (26, 14, 12), (0, 0, 1), 0.7, (1e-5, 0.0, 2e-6)
+        faces = {"-x": (1.0, (0.04, 0.0, 0.005), "zou_he_velocity"), "+x": (0.998, (0.0, 0.0, 0.0), "zou_he_pressure")}
+        mask = li.sphere_mask(26, 14, 12, radius=3)
+    elif name == "neumann_y":
+        # an equilibrium reservoir on -y and a Neumann face on +y, walls in z,
+        # periodic x; solids next to the faces (inward cells solid too)
+        shape, per, tau, F = (13, 21, 11), (1, 0, 0), 0.65, (0.0, 2e-5, 1e-5)
+        faces = {"-y": (1.01, (0.0, 0.03, 0.01)), "+y": (1.0, (0.01, 0.0, 0.0), "neumann")}
+        mask = li.random_mask(13, 21, 11, fraction=0.12, seed=19)
+    elif name == "zou_he_z":
+        # Zou-He velocity inlet with a tangential component on -z, pressure
+        # outlet with a tangential velocity on +z; walls in x, periodic y
+        shape, per, tau, F = (12, 11, 17), (0, 1, 0), 0.8, (0.0, 0.0, 2e-5)
+        faces = {"-z": (1.0, (0.01, -0.01, 0.03), "zou_he_velocity"),
+                 "+z": (0.995, (0.0, 0.01, 0.0), "zou_he_pressure")}
+        mask = li.random_mask(12, 11, 17, fraction=0.08, seed=23)
     else:
         raise KeyError(name)
     return shape, per, tau, F, faces, mask
@@ -41,7 +61,8 @@ def _make_open(shape, precision, layout, scheme, tau, F, faces, mask, per, rho, 
 
 
 @pytest.mark.parametrize("precision", ["f32", "f64"])
-@pytest.mark.parametrize("name,nsteps", [("inlet_outlet", 100), ("open_edges", 101)])
+@pytest.mark.parametrize("name,nsteps", [("inlet_outlet", 100), ("open_edges", 101), ("zou_he_channel", 100),
+                                         ("neumann_y", 101), ("zou_he_z", 100)])
 def test_open_faces_all_layouts_schemes(name, nsteps, precision):
     need_gpu()
     shape, per, tau, F, faces, mask = _open_case(name)
@@ -88,3 +109,52 @@ def test_uniform_stream_is_a_fixed_point(precision):
             f1 = host_f(lat)
             tol = 2e-7 if precision == "f32" else 1e-15
             assert np.max(np.abs(f1 - f0)) <= tol, (layout, scheme, np.max(np.abs(f1 - f0)))
+
+
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+@pytest.mark.parametrize("rules", [("zou_he_velocity", "zou_he_pressure"), ("neumann", "neumann")])
+def test_uniform_stream_is_a_fixed_point_of_the_rules(precision, rules):
+    need_gpu()
+    shape, per = (16, 10, 9), (0, 1, 1)
+    uu = (0.03, -0.01, 0.02)
+    faces = {"-x": (1.0, uu, rules[0]), "+x": (1.0, uu, rules[1])}
+    n = int(np.prod(shape))
+    rho = cast(np.ones(n), precision)
+    u = cast(np.tile(np.array(uu)[:, None], (1, n)), precision)
+    for layout in ("compact", "stream", "bundle"):
+        for scheme in SCHEMES:
+            say("uniform rules", rules, precision, layout, scheme)
+            lat = _make_open(shape, precision, layout, scheme, 0.8, (0.0, 0.0, 0.0), faces, None, per, rho, u)
+            f0 = host_f(lat)
+            lat.step(40)
+            f1 = host_f(lat)
+            tol = 2e-7 if precision == "f32" else 1e-15
+            assert np.max(np.abs(f1 - f0)) <= tol, (layout, scheme, np.max(np.abs(f1 - f0)))
+
+
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+def test_rule_faces_carry_no_force(precision):
+    # the exchanged force counts the solid and wall links only: on the GPU's
+    # own state it equals the oracle's, which skips every open-face link
+    from test_gpu_momentum_exchange import exact_f
+    import torch
+    need_gpu()
+    shape, per, tau, F, faces, mask = _open_case("zou_he_channel")
+    rho, u = li.random_fields(*shape, seed=33)
+    rho, u = cast(rho, precision), cast(0.5 * u, precision)
+    box = oracle.Box(*shape, periodic=per, tau=tau, force=F, open_faces=faces)
+    n = int(np.prod(shape))
+    atol = (4e-9 if precision == "f32" else 1e-15) * n
+    for layout in LAYOUTS:
+        for scheme in SCHEMES:
+            lat = _make_open(shape, precision, layout, scheme, tau, F, faces, mask, per, rho, u)
+            for steps in (7, 1):
+                lat.step(steps)
+                say("rule-face force", precision, layout, scheme, "t =", lat.t)
+                solid, wall = lat.momentum_exchange()
+                torch.cuda.synchronize()
+                want = oracle.momentum_exchange(box, exact_f(lat, precision, mask), mask)
+                err = max(np.max(np.abs(solid.cpu().numpy() - want["solid"])),
+                          np.max(np.abs(wall.cpu().numpy() - want["wall"])))
+                say("  max-abs", err)
+                assert err <= atol, (layout, scheme, lat.t, err)
