@@ -54,15 +54,16 @@ def workload(name):
         return dict(shape=(64, 64, 256), periodic=(1, 0, 1), tau=0.9, force=(0.0, 0.0, 1e-6), mask=None,
                     rho=None, u=None, precision="f64", extra={})
     if name == "karman":
-        # open channel along x: reservoirs at equilibrium (rho 1, u 0.05 along x)
-        # on both x faces, walls in y, periodic z; a cylinder of radius 20 a
-        # quarter-cell off the centre line, Re = u D / nu = 100 (tau 0.56)
+        # open channel along x, PortLBM's boundary set: an equilibrium
+        # (Dirichlet) inlet at rho 1, u 0.05 along x on -x, a Zou-He pressure
+        # outlet at rho 1 on +x, walls in y, periodic z; a cylinder of radius
+        # 20 a quarter-cell off the centre line, Re = u D / nu = 100 (tau 0.56)
         nx, ny, nz = 768, 192, 96
         u_in = (0.05, 0.0, 0.0)
         return dict(shape=(nx, ny, nz), periodic=(0, 0, 1), tau=0.56, force=(0.0, 0.0, 0.0),
                     mask=li.cylinder_mask(nx, ny, nz, 2 * 160, 2 * 96 + 1, 20), rho=None,
                     u=np.tile(np.array(u_in, np.float32)[:, None], (1, nx * ny * nz)), precision="f32",
-                    open_faces={"-x": (1.0, u_in), "+x": (1.0, u_in)}, extra={})
+                    open_faces={"-x": (1.0, u_in), "+x": (1.0, (0.0, 0.0, 0.0), "zou_he_pressure")}, extra={})
     if name == "periodic256_mask0":
         import numpy as np
         return dict(shape=(256, 256, 256), periodic=(1, 1, 1), tau=0.65, force=(1e-6, 0.0, 0.0),

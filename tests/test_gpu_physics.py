@@ -151,3 +151,39 @@ def test_porous_256_schemes_agree_1000_steps():
         torch.cuda.empty_cache()
     assert torch.equal(out[("aa", "stream")], out[("ab", "stream")])
     assert torch.equal(out[("aa", "stream")], out[("aa", "compact")])
+
+
+@pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "ab")])
+def test_pressure_driven_channel_fp64(layout, scheme):
+    """Zou-He pressure faces at both ends of a 96 x 24 x 4 walled channel (fp64,
+    tau 0.8, rho 1.0015 -> 0.9985): at steady state the density falls
+    linearly over the 95 links between the face layers and every column
+    carries the forced-channel closed form for G = c_s^2 drho/dx -- the
+    parabola G y'(H - y') / (2 nu rho) plus the bounce-back slip
+    G (16 (tau - 1/2)^2 - 3) / (24 nu rho) -- up to compressibility, O(drho)."""
+    need_gpu()
+    from lattice_boltzmann_cfd_d3q19_amd import Lattice
+    nx, ny, nz, tau = 96, 24, 4, 0.8
+    rin, rout = 1.0015, 0.9985
+    lat = Lattice(nx, ny, nz, precision="f64", layout=layout, scheme=scheme, tau=tau)
+    lat.set_geometry(None, (0, 0, 1))
+    lat.set_open_faces({"-x": (rin, (0.0, 0.0, 0.0), "zou_he_pressure"),
+                        "+x": (rout, (0.0, 0.0, 0.0), "zou_he_pressure")})
+    lat.init()
+    lat.step(30000)
+    rho, u = host_moments(lat)
+    rho, ux, uy = rho.reshape(nz, ny, nx), u[0].reshape(nz, ny, nx), u[1].reshape(nz, ny, nx)
+    assert np.max(np.abs(ux - ux[:1])) <= 1e-12 * np.abs(ux).max()     # z invariant
+    nu = (tau - 0.5) / 3.0
+    slip = (16.0 * (tau - 0.5) ** 2 - 3.0) / (24.0 * nu)
+    yp = np.arange(ny) + 0.5
+    for m in (24, 48, 72):
+        grad = (rho[0, :, m - 1].mean() - rho[0, :, m + 1].mean()) / 2.0
+        say("pressure channel", layout, scheme, "x =", m, "grad / ideal", grad / ((rin - rout) / (nx - 1)))
+        assert abs(grad / ((rin - rout) / (nx - 1)) - 1.0) < 1e-3
+        G, r = grad / 3.0, rho[0, :, m].mean()
+        want = G * yp * (ny - yp) / (2.0 * nu * r) + G * slip / r
+        err = np.max(np.abs(ux[0, :, m] - want)) / want.max()
+        say("  profile err / u_max", err)
+        assert err < 3e-4
+    assert np.max(np.abs(uy[:, :, 24:73])) < 1e-3 * ux.max()
