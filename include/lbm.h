@@ -21,6 +21,16 @@
  *                  write (opposite(q), x); odd steps read (opposite(q), x - c_q)
  *                  and write (q, x + c_q).  Each cell writes exactly the slots
  *                  it read.
+ *   LBM_SCHEME_ESOPULL  one lattice, in place, the esoteric pull that PortLBM
+ *                  (section 3.3) names among the in-place schemes (Lehmann,
+ *                  Computation 10, 92, 2022): each pair of opposite directions
+ *                  (q, 18 - q), q < 9, has two slots per cell; a step reads f_q
+ *                  from the own cell and f_(18-q) from the neighbour x + c_q,
+ *                  and writes the collided f_(18-q) and f_q back into those two
+ *                  slots, whose roles swap every step.  Bounce-back links keep
+ *                  their value in slots no other link uses (a solid
+ *                  neighbour's, the wrapped cell's beyond a face; in the
+ *                  compact layout nine extra planes).
  * Population layouts (PortLBM section 3.2, Fig. 2):
  *   LBM_LAYOUT_STREAM     SoA: all cells of direction 0, then direction 1, ...
  *   LBM_LAYOUT_BUNDLE     SoAoS: directions grouped in bundles of equal
@@ -36,7 +46,10 @@
  *                         tables; in porous media it moves only fluid bytes.
  *                         Limits (else LBM_ERR_UNSUPPORTED): 4 (nx+2)(ny+2)
  *                         (nz+2) < 2^32 and 2 * 64-rounded N * sizeof(T) <
- *                         2^32 (32-bit byte offsets inside the kernels).
+ *                         2^32 (32-bit byte offsets inside the kernels; 3 *
+ *                         instead of 2 * for ESOPULL, which keeps each pair in
+ *                         three planes 3q, 3q + 1 and 3q + 2 (bounce-back),
+ *                         and the rest population in plane 27).
  *
  * Conventions shared by every entry point:
  *  - Cell index: cell = x + nx * (y + ny * z), N = nx * ny * nz.
@@ -86,6 +99,7 @@ typedef int32_t lbm_status;
 
 #define LBM_SCHEME_AB 0
 #define LBM_SCHEME_AA 1
+#define LBM_SCHEME_ESOPULL 2
 
 typedef struct lbm_desc {
     int64_t nx, ny, nz;  /* box size in cells, each >= 1 */
@@ -101,8 +115,9 @@ typedef struct lbm_desc {
 typedef struct lbm_sim lbm_sim; /* opaque handle (host memory only) */
 
 /* Size of one population buffer, 19 * N * sizeof(T) bytes (compact layout:
- * 19 * roundup(N, 64) * sizeof(T), room for an all-fluid box), and how many
- * the scheme needs (2 for AB, 1 for AA).  Host only; never touches the GPU. */
+ * 19 * roundup(N, 64) * sizeof(T), room for an all-fluid box; 28 planes
+ * instead of 19 for the compact esoteric pull), and how many the scheme
+ * needs (2 for AB, 1 for AA and ESOPULL).  Host only; never touches the GPU. */
 lbm_status lbm_buffer_bytes(const lbm_desc *desc, size_t *bytes_per_buffer, int32_t *n_buffers);
 
 /* Device workspace the layout needs for geometry tables: 0 for the dense

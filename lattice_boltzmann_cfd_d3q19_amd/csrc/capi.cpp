@@ -11,6 +11,9 @@
 //   AA: the single buffer holds f(t) in natural slots when t is even, and the
 //       post-collision values of step t-1 in the swapped slots of the
 //       in-place pattern when t is odd (fieldcraft page, first section).
+//   ESOPULL: the single buffer holds f(t) in the slots of the esoteric pull
+//       of parity t % 2 (each pair's own-cell and neighbour slots swap roles
+//       every step).
 // Either way the values are stored shifted by the lattice weights (f - w).
 #include <hip/hip_runtime.h>
 
@@ -65,7 +68,8 @@ lbm_status validate_desc(const lbm_desc* d)
     if (d->layout != LBM_LAYOUT_STREAM && d->layout != LBM_LAYOUT_BUNDLE && d->layout != LBM_LAYOUT_COLLISION &&
         d->layout != LBM_LAYOUT_COMPACT)
         return LBM_ERR_INVALID_ARGUMENT;
-    if (d->scheme != LBM_SCHEME_AB && d->scheme != LBM_SCHEME_AA) return LBM_ERR_INVALID_ARGUMENT;
+    if (d->scheme != LBM_SCHEME_AB && d->scheme != LBM_SCHEME_AA && d->scheme != LBM_SCHEME_ESOPULL)
+        return LBM_ERR_INVALID_ARGUMENT;
     if (d->reserved != 0) return LBM_ERR_INVALID_ARGUMENT;
     if (std::isnan(d->tau) || !(d->tau > 0.5)) return LBM_ERR_INVALID_ARGUMENT;
     for (int a = 0; a < 3; ++a)
@@ -79,8 +83,11 @@ lbm_status validate_desc(const lbm_desc* d)
     // block of populations with 32-bit byte offsets
     if (compact(*d) && 4.0 * (double)(d->nx + 2) * (double)(d->ny + 2) * (double)(d->nz + 2) >= 4294967296.0)
         return LBM_ERR_UNSUPPORTED;
-    if (compact(*d) && 2.0 * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)((ncells_of(*d) + 63) / 64 * 64) >=
-                           4294967296.0)
+    // (three-plane blocks for the esoteric pull)
+    const double block_planes = d->scheme == LBM_SCHEME_ESOPULL ? 3.0 : 2.0;
+    if (compact(*d) &&
+        block_planes * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)((ncells_of(*d) + 63) / 64 * 64) >=
+            4294967296.0)
         return LBM_ERR_UNSUPPORTED;
     return LBM_OK;
 }
@@ -89,11 +96,13 @@ size_t elem_size(const lbm_desc& d) { return d.precision == LBM_F64 ? 8 : 4; }
 
 uint64_t ncells(const lbm_desc& d) { return (uint64_t)d.nx * (uint64_t)d.ny * (uint64_t)d.nz; }
 
-// Population buffer size; the compact layout reserves room for an all-fluid box.
+// Population buffer size; the compact layout reserves room for an all-fluid
+// box, and its esoteric pull nine more planes (the bounce-back slots).
 size_t buffer_bytes(const lbm_desc& d)
 {
     const uint64_t cells = compact(d) ? (ncells(d) + 63) / 64 * 64 : ncells(d);
-    return (size_t)lbm::kQ * cells * elem_size(d);
+    const uint64_t planes = compact(d) && d.scheme == LBM_SCHEME_ESOPULL ? lbm::kEsoPlanes : lbm::kQ;
+    return (size_t)planes * cells * elem_size(d);
 }
 
 // open faces that are equilibrium reservoirs (applied inside the steps)
@@ -140,6 +149,7 @@ lbm::LaunchPhys phys_of(const lbm_sim* s)
 int state_kind(const lbm_sim* s)
 {
     if (s->d.scheme == LBM_SCHEME_AB) return lbm::kAB;
+    if (s->d.scheme == LBM_SCHEME_ESOPULL) return (s->t % 2 == 0) ? lbm::kEsoEven : lbm::kEsoOdd;
     return (s->t % 2 == 0) ? lbm::kAAEven : lbm::kAAOdd;
 }
 
@@ -249,7 +259,7 @@ lbm_status lbm_create(const lbm_desc* desc, void* buf0, void* buf1, void* hip_st
     const lbm_status v = validate_desc(desc);
     if (v != LBM_OK) return v;
     if (buf0 == nullptr) return LBM_ERR_INVALID_ARGUMENT;
-    if (desc->scheme == LBM_SCHEME_AA && buf1 != nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if (desc->scheme != LBM_SCHEME_AB && buf1 != nullptr) return LBM_ERR_INVALID_ARGUMENT;
     if (desc->scheme == LBM_SCHEME_AB && buf1 == nullptr) return LBM_ERR_INVALID_ARGUMENT;
     if ((uintptr_t)buf0 % kAlign != 0 || (buf1 && (uintptr_t)buf1 % kAlign != 0)) return LBM_ERR_MISALIGNED;
     if (buf1 != nullptr) {
@@ -381,7 +391,7 @@ lbm_status run_steps(lbm_sim* sim, int64_t n, void* rho, void* u)
             a = sim->buf[sim->cur];
             b = sim->buf[1 - sim->cur];
         } else {
-            kind = (sim->t % 2 == 0) ? lbm::kAAEven : lbm::kAAOdd;
+            kind = state_kind(sim);
             a = sim->buf[0];
         }
         void* ro = i + 1 == n ? rho : nullptr;

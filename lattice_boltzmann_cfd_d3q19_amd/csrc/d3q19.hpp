@@ -54,7 +54,13 @@ enum Layout : int { kStream = 0, kBundle = 1, kCollision = 2 };
 // What a kernel does with the stored populations:
 //   kAB      two-lattice fused pull (reads src, writes dst);
 //   kAAEven  one lattice, even step: read (q,x), write (opp q, x);
-//   kAAOdd   one lattice, odd step: read (opp q, x - c_q), write (q, x + c_q).
-enum Kind : int { kAB = 0, kAAEven = 1, kAAOdd = 2 };
+//   kAAOdd   one lattice, odd step: read (opp q, x - c_q), write (q, x + c_q);
+//   kEsoEven, kEsoOdd  one lattice, esoteric pull: each pair of opposite
+//            directions is read from the own cell and from the neighbour along
+//            one of them and written back to the same two slots, whose roles
+//            swap from one step to the next (even / odd step).
+enum Kind : int { kAB = 0, kAAEven = 1, kAAOdd = 2, kEsoEven = 3, kEsoOdd = 4 };
+
+constexpr bool is_eso(int k) { return k == kEsoEven || k == kEsoOdd; }
 
 }  // namespace lbm

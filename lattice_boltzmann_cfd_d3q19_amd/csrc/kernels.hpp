@@ -599,9 +599,48 @@ __device__ __forceinline__ void shifted_equilibrium(T rho, T ux, T uy, T uz, T (
 // Both candidate offsets are formed and one is selected (v_cndmask): the
 // arms are a uniform plane offset plus a per-lane add, cheap enough that the
 // select is not turned into a divergent branch around the load.
-template <int S, int L, typename T>
-__device__ __forceinline__ T* state_slot(T* buf, uint64_t n, const Cell& c, uint32_t bits, int q)
+//
+// Esoteric pull (kEsoEven / kEsoOdd, parity P): the pair p < 9, c = c_p,
+// keeps two slots per cell, S0 = plane p and S1 = plane opp(p).  A step of
+// parity P reads f_p from the own slot (x, S_P) -- where the cell x - c put
+// f*_p -- and f_opp(p) from (x + c, S_{1-P}) -- where x + c put f*_opp(p) --
+// and writes f*_opp(p) into the first and f*_p into the second: the next step
+// finds them as the populations that reached x - c and x + c.  A link that
+// ends outside the fluid keeps its value in a slot no other cell touches: the
+// own side (x - c solid or beyond a face) in the own S0; the neighbour side in
+// the S0 of x + c if that is a solid cell, and in the S1 of the wrapped cell
+// if x + c lies beyond a face (that cell's own side then lies beyond the
+// opposite face and uses its S0).  obits: the reservoir links (open_bits).
+template <int S, int L>
+__device__ __forceinline__ uint64_t eso_off(uint64_t n, const Cell& c, uint32_t bits, uint32_t obits, int q)
 {
+    constexpr bool odd = S == kEsoOdd;
+    if (q == 9) return slot_off<L>(n, 9, c.id);
+    const bool out = ((bits | obits) >> q) & 1u;  // the upstream cell x - c_q is not fluid
+    if (q < 9) {
+        const uint64_t s0 = slot_off<L>(n, q, c.id);
+        if constexpr (!odd) {
+            return s0;
+        } else {
+            const uint64_t s1 = slot_off<L>(n, opp(q), c.id);
+            return out ? s0 : s1;
+        }
+    } else {
+        const int p = opp(q);  // x + c_p = x - c_q
+        const uint32_t up = nbr(c, kCx[p], kCy[p], kCz[p]);
+        const uint64_t s1 = slot_off<L>(n, q, up), s0 = slot_off<L>(n, p, up);
+        const bool face = beyond_wall(c, kCx[p], kCy[p], kCz[p]) || beyond_open(c, kCx[p], kCy[p], kCz[p]);
+        // normal: S_{1-P} of the neighbour; solid: its S0; beyond a face: S1
+        const uint64_t normal = odd ? s0 : s1;
+        return !out ? normal : face ? s1 : s0;
+    }
+}
+
+template <int S, int L, typename T>
+__device__ __forceinline__ T* state_slot(T* buf, uint64_t n, const Cell& c, uint32_t bits, int q,
+                                         uint32_t obits = 0u)
+{
+    if constexpr (is_eso(S)) return buf + eso_off<S, L>(n, c, bits, obits, q);
     const bool bb = (bits >> q) & 1u;
     const uint32_t up = nbr(c, -kCx[q], -kCy[q], -kCz[q]);
     if constexpr (S == kAB) {
@@ -619,8 +658,8 @@ __device__ __forceinline__ T* state_slot(T* buf, uint64_t n, const Cell& c, uint
 
 constexpr int kBlockThreads = 256;
 
-// One fused time step.  K: kAB (a = source, b = destination), kAAEven or
-// kAAOdd (a = the single lattice).  BND: 0 = fully periodic, no mask;
+// One fused time step.  K: kAB (a = source, b = destination), kAAEven,
+// kAAOdd, kEsoEven or kEsoOdd (a = the single lattice).  BND: 0 = fully periodic, no mask;
 // 1 = a mask or a wall exists; 2 = also open faces (a separate instance, so
 // the reservoir selects cost the other kernels no registers).  OUT: also
 // write the density and velocity the collision used (0 on solid cells).
@@ -647,8 +686,10 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
             f[q] = ld_pop(state_slot<kAB, L>(a, n, c, bits, q));
         } else if constexpr (K == kAAEven) {
             f[q] = ld_pop(slot<L>(a, n, q, c.id));
-        } else {
+        } else if constexpr (K == kAAOdd) {
             f[q] = ld_pop(state_slot<kAAOdd, L>(a, n, c, bits, q));
+        } else {
+            f[q] = ld_pop(a + eso_off<K, L>(n, c, bits, obits, q));
         }
     }
     // the even step's natural slots already hold the reservoir values (the odd
@@ -666,6 +707,9 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
             st_pop(slot<L>(b, n, q, c.id), f[q]);
         } else if constexpr (K == kAAEven) {
             st_pop(slot<L>(a, n, opp(q), c.id), f[q]);
+        } else if constexpr (is_eso(K)) {
+            // into the slot f_opp(q) was read from
+            st_pop(a + eso_off<K, L>(n, c, bits, obits, opp(q)), f[q]);
         } else {
             // toward x + c_q, or straight back into (opp q, x) if that cell is
             // solid or beyond a wall (its upstream bit for opp q is set); if
@@ -702,7 +746,9 @@ __global__ void __launch_bounds__(kBlockThreads) io_kernel(T* __restrict__ a, T*
             out0[c.id] = T(0);
 #pragma unroll
             for (int d = 0; d < 3; ++d) out1[(uint64_t)d * n + c.id] = T(0);
-        } else {
+        } else if constexpr (!is_eso(S)) {
+            // (in the esoteric pull a solid cell's slots hold the bounce-back
+            // values of its fluid neighbours' links: not cleared here)
 #pragma unroll
             for (int q = 0; q < kQ; ++q) {
                 *slot<L>(a, n, q, c.id) = T(0);
@@ -716,7 +762,7 @@ __global__ void __launch_bounds__(kBlockThreads) io_kernel(T* __restrict__ a, T*
     T f[kQ];
     if constexpr (OP == kReadF || OP == kReadMoments || OP == kReadS) {
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) f[q] = *state_slot<S, L>(a, n, c, bits, q);
+        for (int q = 0; q < kQ; ++q) f[q] = *state_slot<S, L>(a, n, c, bits, q, obits);
         if constexpr (S != kAAEven) apply_open(f, obits, p, c);
         if constexpr (OP == kReadF) {
 #pragma unroll
@@ -756,7 +802,7 @@ __global__ void __launch_bounds__(kBlockThreads) io_kernel(T* __restrict__ a, T*
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
             if (S != kAAEven && ((obits >> q) & 1u)) continue;
-            *state_slot<S, L>(a, n, c, bits, q) = f[q];
+            *state_slot<S, L>(a, n, c, bits, q, obits) = f[q];
         }
     }
 }

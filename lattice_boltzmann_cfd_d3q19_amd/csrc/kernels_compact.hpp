@@ -158,6 +158,16 @@ constexpr int pair_of(int q) { return q < 9 ? q : q > 9 ? kQ - 1 - q : 9; }
 constexpr int sub_of(int q) { return q > 9 ? 1 : 0; }
 constexpr int plane_of(int q) { return 2 * pair_of(q) + sub_of(q); }
 
+// Esoteric pull on the compact store: pair k < 9 has three planes, 3k (S0),
+// 3k + 1 (S1) and 3k + 2 (B); the rest population is plane 27 (28 planes in
+// all).  At a step of parity P the own side of pair k is (S_P, i), or (S0, i)
+// if x - c_k is not fluid; the neighbour side is (S_{1-P}, nb[k]) for a fluid
+// neighbour, else the own cell's B plane: a slot only this link uses, since
+// solid cells and the halo have no storage here.
+constexpr int kEsoPlanes = 28;
+__device__ __forceinline__ constexpr int eso_plane(int k, int sub) { return 3 * k + sub; }
+constexpr int kEsoRestPlane = 27;
+
 // Element offset (from the start of the buffer) of canonical f_q(x, t) of
 // fluid cell i for stored state kind S (same maps as the dense layouts;
 // x - c_q = x + c_opp(q)); used by the state transfers.
@@ -165,7 +175,13 @@ template <int S>
 __device__ __forceinline__ uint64_t compact_state_off(uint64_t s, uint32_t i, const uint32_t (&nb)[kQ], int q)
 {
     const uint32_t up = nb[opp(q)];
-    if constexpr (S == kAB) {
+    if constexpr (is_eso(S)) {
+        constexpr int P = S == kEsoOdd ? 1 : 0;
+        if (q == 9) return (uint64_t)kEsoRestPlane * s + i;
+        if (q < 9) return (uint64_t)eso_plane(q, no_fluid(up) ? 0 : P) * s + i;
+        const int k = opp(q);  // neighbour side: x + c_k = x - c_q
+        return no_fluid(up) ? (uint64_t)eso_plane(k, 2) * s + i : (uint64_t)eso_plane(k, 1 - P) * s + up;
+    } else if constexpr (S == kAB) {
         return no_fluid(up) ? (uint64_t)plane_of(opp(q)) * s + i : (uint64_t)plane_of(q) * s + up;
     } else if constexpr (S == kAAEven) {
         return (uint64_t)plane_of(q) * s + i;
@@ -302,6 +318,54 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<false>(pair_block(A, pair_of(q), sb), off[q], f[q]);
     }
+}
+
+// Esoteric-pull step on the compact store (K = kEsoEven / kEsoOdd; the
+// plane map is described at compact_state_off).  Every access of pair k lies
+// in its three-plane block: one uniform base plus a 32-bit byte offset
+// (3 s sizeof(T) < 2^32 is checked on the host).  The own side is read and
+// written at the cell's own index, the neighbour side at the index of x + c_k.
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT>
+__global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restrict__ a, CompactGeom g, Phys<T> p,
+                                                                    MomOut<T> mo)
+{
+    static_assert(is_eso(K), "esoteric-pull step");
+    constexpr uint32_t P = K == kEsoOdd ? 1u : 0u;
+    const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
+    const uint32_t i = wg * kGatherThreads + threadIdx.x;
+    if (i >= g.nf) return;
+    const uint32_t sb = g.s * (uint32_t)sizeof(T);
+    const uint32_t own = i * (uint32_t)sizeof(T);
+    char* const A = (char*)a;
+    uint32_t nb[kQ];
+    neighbours_rows(g, g.cellp[i], nb);
+    uint32_t own_off[9], nb_off[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        own_off[k] = no_fluid(nb[opp(k)]) ? own : own + P * sb;
+        const uint32_t via_nb = (1u - P) * sb + nb[k] * (uint32_t)sizeof(T);
+        nb_off[k] = no_fluid(nb[k]) ? 2u * sb + own : via_nb;
+    }
+    char* const rest = A + (uint64_t)kEsoRestPlane * sb;
+    T f[kQ];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        const char* blk = A + (uint64_t)(3 * k) * sb;
+        f[k] = ld_at<T>(blk, own_off[k]);
+        f[opp(k)] = ld_at<T>(blk, nb_off[k]);
+    }
+    f[9] = ld_at<T>(rest, own);
+    if constexpr (OPEN) apply_open_nb(f, nb, p);
+    T rho, ux, uy, uz;
+    collide<T, FORCE>(f, p, rho, ux, uy, uz);
+    if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        char* blk = A + (uint64_t)(3 * k) * sb;
+        st_at<false>(blk, nb_off[k], f[k]);         // f*_k streams to x + c_k
+        st_at<false>(blk, own_off[k], f[opp(k)]);   // f*_opp(k) streams to x - c_k
+    }
+    st_at<false>(rest, own, f[9]);
 }
 
 // Even step of the in-place pattern: purely local, read (q, i), write

@@ -161,9 +161,10 @@ __global__ void __launch_bounds__(kBlockThreads) face_kernel(T* __restrict__ a, 
     const uint32_t ax = r.k >> 1;
     const int sg = (r.k & 1u) ? -1 : 1;
     const uint32_t bits = link_bits<true>(g, c);
+    const uint32_t obits = open_bits(g, c);
     T s[kQ];
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g.n, c, bits, q);
+    for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g.n, c, bits, q, obits);
     // entering through this face: c_q[ax] = sigma, unless the upstream cell
     // also lies beyond a wall of another axis (an edge: the wall wins)
     uint32_t ent = 0;
@@ -183,9 +184,9 @@ __global__ void __launch_bounds__(kBlockThreads) face_kernel(T* __restrict__ a, 
         const bool solid1 = g.mask != nullptr && g.mask[c1.id] != 0;
         T s1[kQ], e[kQ];
         if (!solid1) {
-            const uint32_t bits1 = link_bits<true>(g, c1);
+            const uint32_t bits1 = link_bits<true>(g, c1), obits1 = open_bits(g, c1);
 #pragma unroll
-            for (int q = 0; q < kQ; ++q) s1[q] = *state_slot<S, L>(a, g.n, c1, bits1, q);
+            for (int q = 0; q < kQ; ++q) s1[q] = *state_slot<S, L>(a, g.n, c1, bits1, q, obits1);
         }
         neumann_values(e, s1, solid1, r, p);
 #pragma unroll
@@ -197,7 +198,7 @@ __global__ void __launch_bounds__(kBlockThreads) face_kernel(T* __restrict__ a, 
     // a wall to the steps), so these are the own bounce slots
 #pragma unroll
     for (int q = 0; q < kQ; ++q)
-        if ((ent >> q) & 1u) *state_slot<S, L>(a, g.n, c, bits, q) = s[q];
+        if ((ent >> q) & 1u) *state_slot<S, L>(a, g.n, c, bits, q, obits) = s[q];
 }
 
 // Compact layout: the same on the fluid-compacted store; the index table

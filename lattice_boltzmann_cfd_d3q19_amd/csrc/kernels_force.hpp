@@ -84,10 +84,11 @@ __global__ void __launch_bounds__(kBlockThreads) mex_kernel(T* __restrict__ a, G
     Cell c;
     if (locate(g, c) && !(g.mask != nullptr && g.mask[c.id] != 0)) {
         const uint32_t bits = link_bits<true>(g, c);
+        const uint32_t obits = open_bits(g, c);
         T s[kQ];
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g.n, c, bits, q);
-        if constexpr (S != kAAEven) apply_open(s, open_bits(g, c), p, c);
+        for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g.n, c, bits, q, obits);
+        if constexpr (S != kAAEven) apply_open(s, obits, p, c);
         collide<T, true>(s, p);
         // x + c_q is solid or beyond a wall iff the upstream bit of opp(q) is
         // set; a face with a face rule sets it too, but its links carry flux
@@ -127,6 +128,10 @@ __global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restric
         T f[kQ];
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
+            if constexpr (is_eso(S)) {
+                f[q] = a[compact_state_off<S>(g.s, i, nb, q)];
+                continue;
+            }
             uint32_t off;
             if constexpr (S == kAAEven) {
                 off = sub_of(q) ? own1 : own0;

@@ -125,6 +125,8 @@ hipError_t launch_step_l(int kind, T* a, T* b, const Shape& s, const Phys<T>& p,
     case kAB: return launch_step_k<T, L, kAB>(a, b, s, p, mo, bnd, force, st);
     case kAAEven: return launch_step_k<T, L, kAAEven>(a, b, s, p, mo, bnd, force, st);
     case kAAOdd: return launch_step_k<T, L, kAAOdd>(a, b, s, p, mo, bnd, force, st);
+    case kEsoEven: return launch_step_k<T, L, kEsoEven>(a, b, s, p, mo, bnd, force, st);
+    case kEsoOdd: return launch_step_k<T, L, kEsoOdd>(a, b, s, p, mo, bnd, force, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -181,6 +183,8 @@ hipError_t launch_io_l(int state, int op, T* a, T* b, const Shape& s, const Phys
     case kAB: return launch_io_s<T, L, kAB>(op, a, b, s, p, o0, o1, i0, i1, st);
     case kAAEven: return launch_io_s<T, L, kAAEven>(op, a, b, s, p, o0, o1, i0, i1, st);
     case kAAOdd: return launch_io_s<T, L, kAAOdd>(op, a, b, s, p, o0, o1, i0, i1, st);
+    case kEsoEven: return launch_io_s<T, L, kEsoEven>(op, a, b, s, p, o0, o1, i0, i1, st);
+    case kEsoOdd: return launch_io_s<T, L, kEsoOdd>(op, a, b, s, p, o0, o1, i0, i1, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -253,10 +257,28 @@ hipError_t launch_even_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, h
     return hipLaunchKernel(k, grid, block, args, 0, st);
 }
 
+template <typename T, int K, bool FORCE>
+hipError_t launch_eso_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, hipStream_t st)
+{
+    if (g.nf == 0) return hipSuccess;
+    void* args[] = {&a, &g, &p, &mo};
+    uint32_t nwg = (g.nf + kGatherThreads - 1) / kGatherThreads;
+    if (g.xk > 1) nwg = (nwg + 8 * g.xk - 1) / (8 * g.xk) * (8 * g.xk);
+    const dim3 grid(nwg), block(kGatherThreads);
+    const bool out = mo.rho != nullptr;
+    const void* k = g.open ? (out ? (const void*)&eso_compact_kernel<T, K, FORCE, true, true>
+                                  : (const void*)&eso_compact_kernel<T, K, FORCE, true, false>)
+                           : (out ? (const void*)&eso_compact_kernel<T, K, FORCE, false, true>
+                                  : (const void*)&eso_compact_kernel<T, K, FORCE, false, false>);
+    return hipLaunchKernel(k, grid, block, args, 0, st);
+}
+
 template <typename T, int K>
 hipError_t launch_step_compact_k(T* a, T* b, CompactGeom g, Phys<T> p, MomOut<T> mo, bool force, hipStream_t st)
 {
-    if constexpr (K == kAAEven) {
+    if constexpr (is_eso(K)) {
+        return force ? launch_eso_compact_t<T, K, true>(a, g, p, mo, st) : launch_eso_compact_t<T, K, false>(a, g, p, mo, st);
+    } else if constexpr (K == kAAEven) {
         return force ? launch_even_compact_t<T, true>(a, g, p, mo, st) : launch_even_compact_t<T, false>(a, g, p, mo, st);
     } else {
         return force ? launch_step_compact_t<T, K, true>(a, b, g, p, mo, st)
@@ -285,6 +307,8 @@ hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& lg, const
     case kAB: return launch_step_compact_k<T, kAB>(a, b, g, p, mo, lp.has_force, st);
     case kAAEven: return launch_step_compact_k<T, kAAEven>(a, b, g, p, mo, lp.has_force, st);
     case kAAOdd: return launch_step_compact_k<T, kAAOdd>(a, b, g, p, mo, lp.has_force, st);
+    case kEsoEven: return launch_step_compact_k<T, kEsoEven>(a, b, g, p, mo, lp.has_force, st);
+    case kEsoOdd: return launch_step_compact_k<T, kEsoOdd>(a, b, g, p, mo, lp.has_force, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -324,6 +348,8 @@ hipError_t launch_io_compact(int state, int op, T* a, const LaunchGeom& lg, cons
     case kAB: return launch_io_compact_s<T, kAB>(op, a, cg, s, p, o0, o1, i0, i1, st);
     case kAAEven: return launch_io_compact_s<T, kAAEven>(op, a, cg, s, p, o0, o1, i0, i1, st);
     case kAAOdd: return launch_io_compact_s<T, kAAOdd>(op, a, cg, s, p, o0, o1, i0, i1, st);
+    case kEsoEven: return launch_io_compact_s<T, kEsoEven>(op, a, cg, s, p, o0, o1, i0, i1, st);
+    case kEsoOdd: return launch_io_compact_s<T, kEsoOdd>(op, a, cg, s, p, o0, o1, i0, i1, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -368,6 +394,8 @@ hipError_t launch_face_l(int state, T* a, const Geom& g, const Phys<T>& p, const
     case kAB: return hipLaunchKernel((const void*)&face_kernel<T, L, kAB>, grid, block, args, 0, st);
     case kAAEven: return hipLaunchKernel((const void*)&face_kernel<T, L, kAAEven>, grid, block, args, 0, st);
     case kAAOdd: return hipLaunchKernel((const void*)&face_kernel<T, L, kAAOdd>, grid, block, args, 0, st);
+    case kEsoEven: return hipLaunchKernel((const void*)&face_kernel<T, L, kEsoEven>, grid, block, args, 0, st);
+    case kEsoOdd: return hipLaunchKernel((const void*)&face_kernel<T, L, kEsoOdd>, grid, block, args, 0, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -385,6 +413,8 @@ hipError_t launch_face_compact(int state, T* a, const CompactGeom& cg, const Phy
     case kAB: return hipLaunchKernel((const void*)&face_compact_kernel<T, kAB>, grid, block, args, 0, st);
     case kAAEven: return hipLaunchKernel((const void*)&face_compact_kernel<T, kAAEven>, grid, block, args, 0, st);
     case kAAOdd: return hipLaunchKernel((const void*)&face_compact_kernel<T, kAAOdd>, grid, block, args, 0, st);
+    case kEsoEven: return hipLaunchKernel((const void*)&face_compact_kernel<T, kEsoEven>, grid, block, args, 0, st);
+    case kEsoOdd: return hipLaunchKernel((const void*)&face_compact_kernel<T, kEsoOdd>, grid, block, args, 0, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -444,6 +474,8 @@ hipError_t launch_mex_l(int state, T* a, const Shape& sh, const Phys<T>& p, doub
     case kAB: return launch_mex_t<T, L, kAB>(a, sh, p, partial, st);
     case kAAEven: return launch_mex_t<T, L, kAAEven>(a, sh, p, partial, st);
     case kAAOdd: return launch_mex_t<T, L, kAAOdd>(a, sh, p, partial, st);
+    case kEsoEven: return launch_mex_t<T, L, kEsoEven>(a, sh, p, partial, st);
+    case kEsoOdd: return launch_mex_t<T, L, kEsoOdd>(a, sh, p, partial, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -466,6 +498,8 @@ hipError_t launch_momentum_exchange(int layout, int state, T* a, const LaunchGeo
             case kAB: e = launch_mex_compact_t<T, kAB>(a, cg, p, partial, st); break;
             case kAAEven: e = launch_mex_compact_t<T, kAAEven>(a, cg, p, partial, st); break;
             case kAAOdd: e = launch_mex_compact_t<T, kAAOdd>(a, cg, p, partial, st); break;
+            case kEsoEven: e = launch_mex_compact_t<T, kEsoEven>(a, cg, p, partial, st); break;
+            case kEsoOdd: e = launch_mex_compact_t<T, kEsoOdd>(a, cg, p, partial, st); break;
             default: return hipErrorInvalidValue;
             }
         }

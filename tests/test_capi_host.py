@@ -92,6 +92,26 @@ def test_compact_offset_limits():
     assert capi.lbm_buffer_bytes(capi.make_desc(1022, 1022, 1022, capi.LBM_F32, **big))[0] == capi.LBM_ERR_UNSUPPORTED
 
 
+def test_esoteric_pull_buffers():
+    # one buffer; 19 planes in the dense layouts, 28 in the compact one (three
+    # per pair: two swapping slots and a bounce-back slot, and the rest
+    # population), whose three-plane blocks are addressed with 32-bit offsets
+    for layout, planes in ((capi.LBM_LAYOUT_STREAM, 19), (capi.LBM_LAYOUT_COLLISION, 19),
+                           (capi.LBM_LAYOUT_COMPACT, 28)):
+        d = capi.make_desc(16, 8, 5, capi.LBM_F32, layout=layout, scheme=capi.LBM_SCHEME_ESOPULL)
+        st, nbytes, nbuf = capi.lbm_buffer_bytes(d)
+        cells = 640 if layout == capi.LBM_LAYOUT_COMPACT else 640
+        assert st == capi.LBM_OK and nbuf == 1 and nbytes == planes * cells * 4
+        assert capi.lbm_create(d, FAKE, FAKE + (1 << 20))[0] == capi.LBM_ERR_INVALID_ARGUMENT
+        st, h = capi.lbm_create(d, FAKE)
+        assert st == capi.LBM_OK
+        capi.lbm_destroy(h)
+    big = dict(layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_ESOPULL)
+    # 3 * roundup(N, 64) * 4 < 2^32 <=> N < 2^28 / 0.75
+    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 341, capi.LBM_F32, **big))[0] == capi.LBM_OK
+    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 342, capi.LBM_F32, **big))[0] == capi.LBM_ERR_UNSUPPORTED
+
+
 def test_buffer_rules():
     aa = capi.make_desc(8, 8, 8, scheme=capi.LBM_SCHEME_AA)
     ab = capi.make_desc(8, 8, 8, scheme=capi.LBM_SCHEME_AB)

@@ -238,7 +238,9 @@ def _full_size(name):
     ("sphere128", "compact", "aa"), ("channel_f64", "compact", "ab"), ("porous256", "compact", "aa"),
     ("porous256", "compact", "ab"),
     ("channel_f64", "stream", "aa"), ("channel_f64", "stream", "ab"),
-    ("porous256", "stream", "aa"), ("porous256", "stream", "ab")])
+    ("porous256", "stream", "aa"), ("porous256", "stream", "ab"),
+    ("porous256", "compact", "eso"), ("porous256", "stream", "eso"), ("sphere128", "collision", "eso"),
+    ("channel_f64", "bundle", "eso")])
 def test_full_size_sampled_steps(name, layout, scheme):
     """At the benchmark sizes: advance a few steps, then check two consecutive
     steps (odd -> even and even -> odd for AA) at sampled cells against the
