@@ -309,3 +309,45 @@ def test_compact_tables_bit_exact(periodic):
     yy, xx = np.divmod(rem, nx)
     want_cellp = ((xx + 1) + px * (yy + 1) + px * py * (zz + 1)).astype(np.uint32)
     assert np.array_equal(ws[cell_off:cell_off + nf], want_cellp)
+
+
+@pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "ab"), ("compact", "eso")])
+def test_full_size_open_channel_sampled_steps(layout, scheme):
+    """The 768 x 192 x 96 open channel at full size: equilibrium inlet on -x,
+    Zou-He pressure outlet on +x, walls in y, periodic z, a cylinder of
+    radius 20.  Two consecutive steps at sampled cells -- random ones, cells
+    next to the cylinder, and cells of both open faces including their edges
+    with the walls -- against the oracle evaluated from the GPU's own state."""
+    need_gpu()
+    import torch
+    from lattice_boltzmann_cfd_d3q19_amd import Lattice
+    nx, ny, nz, tau = 768, 192, 96, 0.56
+    u_in = (0.05, 0.0, 0.0)
+    faces = {"-x": (1.0, u_in), "+x": (1.0, (0.0, 0.0, 0.0), "zou_he_pressure")}
+    mask = li.cylinder_mask(nx, ny, nz, 2 * 160, 2 * 96 + 1, 20)
+    n = nx * ny * nz
+    u = np.tile(np.array(u_in, np.float32)[:, None], (1, n))
+    say("full-size open channel", layout, scheme)
+    lat = Lattice(nx, ny, nz, precision="f32", layout=layout, scheme=scheme, tau=tau)
+    lat.set_geometry(torch.from_numpy(mask), (0, 0, 1))
+    lat.set_open_faces(faces)
+    lat.init(None, torch.from_numpy(u))
+    box = oracle.Box(nx, ny, nz, periodic=(0, 0, 1), tau=tau, open_faces=faces)
+    rng = np.random.default_rng(7)
+    cells = [_sample_cells(mask, n, 4096, seed=11)]
+    for x in (0, nx - 1):
+        y = np.concatenate([rng.integers(0, ny, 600), [0, ny - 1] * 20])
+        z = rng.integers(0, nz, y.size)
+        cells.append(x + nx * (y + ny * z))
+    cells = np.unique(np.concatenate(cells)).astype(np.int64)
+    lat.step(5)
+    prev = host_f(lat)
+    for _ in range(2):
+        lat.step(1)
+        cur = host_f(lat)
+        want = oracle.step_cells(box, prev, cells, mask)
+        err = np.max(np.abs(cur[:, cells].T - want))
+        say("  one-step max-abs", err, "t =", lat.t, "cells", cells.size)
+        assert err <= 1e-6
+        prev = cur
+    del prev, cur
