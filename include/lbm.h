@@ -213,7 +213,8 @@ lbm_status lbm_set_open_faces(lbm_sim *sim, const int32_t open[6], const double 
  * the fluid-cell count: the only call that blocks the host. */
 lbm_status lbm_init_equilibrium(lbm_sim *sim, const void *rho, const void *u);
 
-/* Advance n >= 0 time steps (one fused kernel launch each); t += n. */
+/* Advance n >= 0 time steps (one fused kernel launch each, plus one small
+ * launch per open face of a NEUMANN or ZOU_HE kind); t += n. */
 lbm_status lbm_step(lbm_sim *sim, int64_t n);
 
 /* Advance n >= 1 time steps like lbm_step; the last step also writes the
@@ -263,7 +264,8 @@ lbm_status lbm_load_state(lbm_sim *sim, const void *s);
  * state of x (collision and forcing exactly as in lbm_step).  Writes
  *   force   device double[6]: the sum over links that end in a solid cell of
  *           the mask (x, y, z), then over links that leave the box through a
- *           non-periodic face (x, y, z).  8-byte aligned.
+ *           wall, i.e. a non-periodic face that is not open (x, y, z).
+ *           8-byte aligned.
  *   scratch device, 256-byte aligned, at least
  *           lbm_momentum_exchange_scratch_bytes() bytes (per-workgroup
  *           partial sums); reused by the caller freely once the call's work
