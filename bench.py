@@ -43,6 +43,11 @@ def workload(name):
         mask, ns = li.porous_mask(512)
         return dict(shape=(512, 512, 512), periodic=(1, 1, 1), tau=0.65, force=(1e-6, 0.0, 0.0), mask=mask,
                     rho=None, u=None, precision="f32", extra={"n_spheres": ns})
+    if name == "random32":
+        # the small seeded case: 32^3 periodic, tau 0.8, random fields (launch-bound)
+        rho, u = li.random_fields(32, 32, 32, seed=1)
+        return dict(shape=(32, 32, 32), periodic=(1, 1, 1), tau=0.8, force=(0.0, 0.0, 0.0), mask=None,
+                    rho=rho.astype(np.float32), u=u.astype(np.float32), precision="f32", extra={})
     if name == "tgv128":
         rho, u = li.taylor_green(128, u0=0.04)
         return dict(shape=(128, 128, 128), periodic=(1, 1, 1), tau=0.6, force=(0.0, 0.0, 0.0), mask=None,
