@@ -30,7 +30,7 @@
  *                  slots, whose roles swap every step.  Bounce-back links keep
  *                  their value in slots no other link uses (a solid
  *                  neighbour's, the wrapped cell's beyond a face; in the
- *                  compact layout nine extra planes).
+ *                  compact layout a packed region after the 19 planes).
  * Population layouts (PortLBM section 3.2, Fig. 2):
  *   LBM_LAYOUT_STREAM     SoA: all cells of direction 0, then direction 1, ...
  *   LBM_LAYOUT_BUNDLE     SoAoS: directions grouped in bundles of equal
@@ -46,10 +46,11 @@
  *                         tables; in porous media it moves only fluid bytes.
  *                         Limits (else LBM_ERR_UNSUPPORTED): 4 (nx+2)(ny+2)
  *                         (nz+2) < 2^32 and 2 * 64-rounded N * sizeof(T) <
- *                         2^32 (32-bit byte offsets inside the kernels; 3 *
- *                         instead of 2 * for ESOPULL, which keeps each pair in
- *                         three planes 3q, 3q + 1 and 3q + 2 (bounce-back),
- *                         and the rest population in plane 27).
+ *                         2^32 (32-bit byte offsets inside the kernels).
+ *                         ESOPULL keeps the bounce-back values of its
+ *                         neighbour-side links after the 19 planes, one slot
+ *                         per link packed in cell order (9 more planes of
+ *                         room, 4 workspace bytes more per cell).
  *
  * Conventions shared by every entry point:
  *  - Cell index: cell = x + nx * (y + ny * z), N = nx * ny * nz.

@@ -83,11 +83,8 @@ lbm_status validate_desc(const lbm_desc* d)
     // block of populations with 32-bit byte offsets
     if (compact(*d) && 4.0 * (double)(d->nx + 2) * (double)(d->ny + 2) * (double)(d->nz + 2) >= 4294967296.0)
         return LBM_ERR_UNSUPPORTED;
-    // (three-plane blocks for the esoteric pull)
-    const double block_planes = d->scheme == LBM_SCHEME_ESOPULL ? 3.0 : 2.0;
-    if (compact(*d) &&
-        block_planes * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)((ncells_of(*d) + 63) / 64 * 64) >=
-            4294967296.0)
+    if (compact(*d) && 2.0 * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)((ncells_of(*d) + 63) / 64 * 64) >=
+                           4294967296.0)
         return LBM_ERR_UNSUPPORTED;
     return LBM_OK;
 }
@@ -97,7 +94,7 @@ size_t elem_size(const lbm_desc& d) { return d.precision == LBM_F64 ? 8 : 4; }
 uint64_t ncells(const lbm_desc& d) { return (uint64_t)d.nx * (uint64_t)d.ny * (uint64_t)d.nz; }
 
 // Population buffer size; the compact layout reserves room for an all-fluid
-// box, and its esoteric pull nine more planes (the bounce-back slots).
+// box, and its esoteric pull nine more planes' worth of bounce-back slots.
 size_t buffer_bytes(const lbm_desc& d)
 {
     const uint64_t cells = compact(d) ? (ncells(d) + 63) / 64 * 64 : ncells(d);
@@ -208,7 +205,8 @@ lbm_status apply_face_rules(lbm_sim* s)
 lbm_status build_compact(lbm_sim* s)
 {
     if (s->ws == nullptr) return LBM_ERR_BAD_STATE;
-    const lbm::CompactLayoutBytes lay = lbm::compact_workspace_layout(s->d.nx, s->d.ny, s->d.nz);
+    const bool eso = s->d.scheme == LBM_SCHEME_ESOPULL;
+    const lbm::CompactLayoutBytes lay = lbm::compact_workspace_layout(s->d.nx, s->d.ny, s->d.nz, eso);
     char* base = (char*)s->ws;
     lbm::CompactTables& t = s->tables;
     t.header = (uint32_t*)(base + lay.header);
@@ -216,6 +214,7 @@ lbm_status build_compact(lbm_sim* s)
     t.idxp = (uint32_t*)(base + lay.idxp);
     t.cellp = (uint32_t*)(base + lay.cellp);
     t.cellid = (uint32_t*)(base + lay.cellid);
+    t.bbase = eso ? (uint32_t*)(base + lay.bbase) : nullptr;
     t.nf = 0;
     t.stride = 0;
     hipError_t e = lbm::launch_compact_build(geom_of(s), t, s->stream);
@@ -226,7 +225,7 @@ lbm_status build_compact(lbm_sim* s)
     if (e != hipSuccess) return hip_status(s, e);
     t.nf = nf;
     t.stride = ((uint64_t)nf + 63) / 64 * 64;
-    return LBM_OK;
+    return hip_status(s, lbm::launch_compact_bounce(geom_of(s), t, s->stream));
 }
 
 }  // namespace
@@ -248,7 +247,10 @@ lbm_status lbm_workspace_bytes(const lbm_desc* desc, size_t* bytes)
     const lbm_status v = validate_desc(desc);
     if (v != LBM_OK) return v;
     if (bytes == nullptr) return LBM_ERR_INVALID_ARGUMENT;
-    *bytes = compact(*desc) ? lbm::compact_workspace_layout(desc->nx, desc->ny, desc->nz).total : 0;
+    *bytes = compact(*desc) ? lbm::compact_workspace_layout(desc->nx, desc->ny, desc->nz,
+                                                             desc->scheme == LBM_SCHEME_ESOPULL)
+                                  .total
+                            : 0;
     return LBM_OK;
 }
 

@@ -138,7 +138,26 @@ __global__ void __launch_bounds__(kBlockThreads) compact_fill_halo(uint32_t nx, 
 }
 
 
-CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz)
+// Bounce-back links of each fluid cell on the neighbour side of the
+// esoteric pull: x + c_k, k < 9, not fluid.
+__global__ void __launch_bounds__(kBlockThreads) compact_bounce_counts(const uint32_t* __restrict__ idxp,
+                                                                       const uint32_t* __restrict__ cellp,
+                                                                       uint32_t nf, uint32_t px, uint32_t pxy,
+                                                                       uint32_t* __restrict__ count)
+{
+    const uint32_t i = blockIdx.x * kBlockThreads + threadIdx.x;
+    if (i >= nf) return;
+    const uint32_t p = cellp[i];
+    uint32_t n = 0;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        const int32_t off = kCx[k] + (int32_t)px * kCy[k] + (int32_t)pxy * kCz[k];
+        n += no_fluid(idxp[(uint32_t)((int32_t)p + off)]) ? 1u : 0u;
+    }
+    count[i] = n;
+}
+
+CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz, bool bounce)
 {
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     CompactLayoutBytes b{};
@@ -150,7 +169,8 @@ CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz)
     b.idxp = b.rows + up(4 * nrows);
     b.cellp = b.idxp + up(4 * npad);
     b.cellid = b.cellp + up(4 * n64);
-    b.total = b.cellid + up(4 * n64);
+    b.bbase = b.cellid + up(4 * n64);
+    b.total = b.bbase + (bounce ? up(4 * n64) : 0);
     return b;
 }
 
@@ -168,6 +188,17 @@ hipError_t launch_compact_build(const LaunchGeom& lg, const CompactTables& t, hi
                        dim3(kBlockThreads), 0, st, nx, ny, nz, (uint32_t)(lg.periodic[0] != 0),
                        (uint32_t)(lg.periodic[1] != 0), (uint32_t)(lg.periodic[2] != 0), lg.open, px, pxy, npad,
                        t.idxp);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact_bounce(const LaunchGeom& lg, const CompactTables& t, hipStream_t st)
+{
+    if (t.bbase == nullptr || t.nf == 0) return hipSuccess;
+    const uint32_t px = (uint32_t)lg.nx + 2, pxy = (uint32_t)((lg.nx + 2) * (lg.ny + 2));
+    hipLaunchKernelGGL(compact_bounce_counts, dim3((t.nf + kBlockThreads - 1) / kBlockThreads), dim3(kBlockThreads),
+                       0, st, (const uint32_t*)t.idxp, (const uint32_t*)t.cellp, t.nf, px, pxy, t.bbase);
+    // total bounce-back links into header[1]
+    hipLaunchKernelGGL(compact_scan_rows, dim3(1), dim3(1024), 0, st, t.bbase, t.nf, t.header + 1);
     return hipGetLastError();
 }
 

@@ -83,6 +83,7 @@ struct CompactGeom {
     const uint32_t* idxp;
     const uint32_t* cellp;
     const uint32_t* cellid;  // cell index x + nx (y + ny z) of the i-th fluid cell
+    const uint32_t* bbase;   // esoteric pull: first bounce-back slot of the i-th fluid cell
     uint32_t nf;   // fluid cells
     uint32_t px;   // nx + 2
     uint32_t pxy;  // (nx + 2)(ny + 2)
@@ -158,29 +159,49 @@ constexpr int pair_of(int q) { return q < 9 ? q : q > 9 ? kQ - 1 - q : 9; }
 constexpr int sub_of(int q) { return q > 9 ? 1 : 0; }
 constexpr int plane_of(int q) { return 2 * pair_of(q) + sub_of(q); }
 
-// Esoteric pull on the compact store: pair k < 9 has three planes, 3k (S0),
-// 3k + 1 (S1) and 3k + 2 (B); the rest population is plane 27 (28 planes in
-// all).  At a step of parity P the own side of pair k is (S_P, i), or (S0, i)
-// if x - c_k is not fluid; the neighbour side is (S_{1-P}, nb[k]) for a fluid
-// neighbour, else the own cell's B plane: a slot only this link uses, since
-// solid cells and the halo have no storage here.
-constexpr int kEsoPlanes = 28;
-__device__ __forceinline__ constexpr int eso_plane(int k, int sub) { return 3 * k + sub; }
-constexpr int kEsoRestPlane = 27;
+// Esoteric pull on the compact store: pair k < 9 keeps its two slots in the
+// planes of the other schemes, S0 = P(k) and S1 = P(18 - k), and the rest
+// population is in plane P(9) = 18.  At a step of parity P the own side of
+// pair k is (S_P, i), or (S0, i) if x - c_k is not fluid; the neighbour side
+// is (S_{1-P}, nb[k]) for a fluid neighbour.  Solid cells and the halo have
+// no storage here, so a neighbour-side bounce-back link keeps its value in a
+// region after the 19 planes, at element 19 S + bbase[i] + (the cell's
+// bounce-back links of the pairs before k): one slot per such link, packed in
+// cell order, so that a wave's bounced links share one or two lines.
+constexpr int kEsoPlanes = 28;     // 19 planes and up to 9 S bounce-back slots
+constexpr int kEsoBouncePlane = 19;
+
+// Bit k (k < 9): the neighbour side x + c_k of pair k is not fluid.
+__device__ __forceinline__ uint32_t eso_bounce_mask(const uint32_t (&nb)[kQ])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) m |= (no_fluid(nb[k]) ? 1u : 0u) << k;
+    return m;
+}
+
+// Bounce-back slot of pair k of fluid cell i (relative to plane 19).
+__device__ __forceinline__ uint32_t eso_bounce_slot(uint32_t base, uint32_t mask, int k)
+{
+    return base + (uint32_t)__popc(mask & ((1u << k) - 1u));
+}
 
 // Element offset (from the start of the buffer) of canonical f_q(x, t) of
 // fluid cell i for stored state kind S (same maps as the dense layouts;
 // x - c_q = x + c_opp(q)); used by the state transfers.
 template <int S>
-__device__ __forceinline__ uint64_t compact_state_off(uint64_t s, uint32_t i, const uint32_t (&nb)[kQ], int q)
+__device__ __forceinline__ uint64_t compact_state_off(const CompactGeom& g, uint32_t i, const uint32_t (&nb)[kQ],
+                                                      int q)
 {
+    const uint64_t s = g.s;
     const uint32_t up = nb[opp(q)];
     if constexpr (is_eso(S)) {
-        constexpr int P = S == kEsoOdd ? 1 : 0;
-        if (q == 9) return (uint64_t)kEsoRestPlane * s + i;
-        if (q < 9) return (uint64_t)eso_plane(q, no_fluid(up) ? 0 : P) * s + i;
+        constexpr bool odd = S == kEsoOdd;
+        if (q == 9) return (uint64_t)plane_of(9) * s + i;
+        if (q < 9) return (uint64_t)plane_of((no_fluid(up) || !odd) ? q : opp(q)) * s + i;
         const int k = opp(q);  // neighbour side: x + c_k = x - c_q
-        return no_fluid(up) ? (uint64_t)eso_plane(k, 2) * s + i : (uint64_t)eso_plane(k, 1 - P) * s + up;
+        if (!no_fluid(up)) return (uint64_t)plane_of(odd ? k : q) * s + up;
+        return (uint64_t)kEsoBouncePlane * s + eso_bounce_slot(g.bbase[i], eso_bounce_mask(nb), k);
     } else if constexpr (S == kAB) {
         return no_fluid(up) ? (uint64_t)plane_of(opp(q)) * s + i : (uint64_t)plane_of(q) * s + up;
     } else if constexpr (S == kAAEven) {
@@ -191,9 +212,10 @@ __device__ __forceinline__ uint64_t compact_state_off(uint64_t s, uint32_t i, co
 }
 
 template <int S, typename T>
-__device__ __forceinline__ T* compact_state_slot(T* buf, uint64_t s, uint32_t i, const uint32_t (&nb)[kQ], int q)
+__device__ __forceinline__ T* compact_state_slot(T* buf, const CompactGeom& g, uint32_t i, const uint32_t (&nb)[kQ],
+                                                 int q)
 {
-    return buf + compact_state_off<S>(s, i, nb, q);
+    return buf + compact_state_off<S>(g, i, nb, q);
 }
 
 // Loads and stores of the compact step kernels.  Measured on MI355X, 256^3
@@ -321,10 +343,10 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
 }
 
 // Esoteric-pull step on the compact store (K = kEsoEven / kEsoOdd; the
-// plane map is described at compact_state_off).  Every access of pair k lies
-// in its three-plane block: one uniform base plus a 32-bit byte offset
-// (3 s sizeof(T) < 2^32 is checked on the host).  The own side is read and
-// written at the cell's own index, the neighbour side at the index of x + c_k.
+// slot map is described at compact_state_off).  The own side of pair k and
+// a fluid neighbour side lie in the pair's two-plane block (a uniform base
+// plus a 32-bit byte offset, as in the other compact kernels); a bounced
+// neighbour side goes to the packed bounce-back region instead.
 template <typename T, int K, bool FORCE, bool OPEN, bool OUT>
 __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restrict__ a, CompactGeom g, Phys<T> p,
                                                                     MomOut<T> mo)
@@ -339,20 +361,24 @@ __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restri
     char* const A = (char*)a;
     uint32_t nb[kQ];
     neighbours_rows(g, g.cellp[i], nb);
-    uint32_t own_off[9], nb_off[9];
+    const uint32_t bmask = eso_bounce_mask(nb);
+    const uint32_t bbase = bmask != 0u ? g.bbase[i] : 0u;
+    T* const B = (T*)(A + (uint64_t)kEsoBouncePlane * sb);
+    uint32_t own_off[9];
+    T* nb_ptr[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-        own_off[k] = no_fluid(nb[opp(k)]) ? own : own + P * sb;
-        const uint32_t via_nb = (1u - P) * sb + nb[k] * (uint32_t)sizeof(T);
-        nb_off[k] = no_fluid(nb[k]) ? 2u * sb + own : via_nb;
+        own_off[k] = (P == 0u || no_fluid(nb[opp(k)])) ? own : own + sb;
+        char* const blk = pair_block(A, k, sb);
+        T* const via_nb = (T*)(blk + (1u - P) * sb + nb[k] * (uint32_t)sizeof(T));
+        nb_ptr[k] = ((bmask >> k) & 1u) ? B + eso_bounce_slot(bbase, bmask, k) : via_nb;
     }
-    char* const rest = A + (uint64_t)kEsoRestPlane * sb;
+    char* const rest = pair_block(A, 9, sb);
     T f[kQ];
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-        const char* blk = A + (uint64_t)(3 * k) * sb;
-        f[k] = ld_at<T>(blk, own_off[k]);
-        f[opp(k)] = ld_at<T>(blk, nb_off[k]);
+        f[k] = ld_at<T>(pair_block(A, k, sb), own_off[k]);
+        f[opp(k)] = *nb_ptr[k];
     }
     f[9] = ld_at<T>(rest, own);
     if constexpr (OPEN) apply_open_nb(f, nb, p);
@@ -361,9 +387,8 @@ __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restri
     if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-        char* blk = A + (uint64_t)(3 * k) * sb;
-        st_at<false>(blk, nb_off[k], f[k]);         // f*_k streams to x + c_k
-        st_at<false>(blk, own_off[k], f[opp(k)]);   // f*_opp(k) streams to x - c_k
+        *nb_ptr[k] = f[k];                                          // f*_k streams to x + c_k
+        st_at<false>(pair_block(A, k, sb), own_off[k], f[opp(k)]);  // f*_opp(k) streams to x - c_k
     }
     st_at<false>(rest, own, f[9]);
 }
@@ -436,7 +461,7 @@ __global__ void __launch_bounds__(kBlockThreads) io_compact_kernel(T* __restrict
     T f[kQ];
     if constexpr (OP == kReadF || OP == kReadMoments || OP == kReadS) {
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) f[q] = *compact_state_slot<S>(a, s, i, nb, q);
+        for (int q = 0; q < kQ; ++q) f[q] = *compact_state_slot<S>(a, cg, i, nb, q);
         if constexpr (S != kAAEven)
             if (cg.open) apply_open_nb(f, nb, p);
         if constexpr (OP == kReadF) {
@@ -477,7 +502,7 @@ __global__ void __launch_bounds__(kBlockThreads) io_compact_kernel(T* __restrict
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
             if (S != kAAEven && is_res(nb[opp(q)], p.res)) continue;
-            *compact_state_slot<S>(a, s, i, nb, q) = f[q];
+            *compact_state_slot<S>(a, cg, i, nb, q) = f[q];
         }
     }
 }

@@ -214,12 +214,11 @@ __global__ void __launch_bounds__(kBlockThreads) face_compact_kernel(T* __restri
     const uint32_t pp = (x + 1) + cg.px * (y + 1) + cg.pxy * (z + 1);
     const uint32_t i = cg.idxp[pp];
     if (i == kInvalid) return;
-    const uint64_t s = cg.s;
     uint32_t nb[kQ];
     neighbours(cg, pp, nb);
     T f[kQ];
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) f[q] = *compact_state_slot<S>(a, s, i, nb, q);
+    for (int q = 0; q < kQ; ++q) f[q] = *compact_state_slot<S>(a, cg, i, nb, q);
     uint32_t ent = 0;
 #pragma unroll
     for (int q = 0; q < kQ; ++q)
@@ -235,7 +234,7 @@ __global__ void __launch_bounds__(kBlockThreads) face_compact_kernel(T* __restri
             uint32_t nb1[kQ];
             neighbours(cg, pp1, nb1);
 #pragma unroll
-            for (int q = 0; q < kQ; ++q) f1[q] = *compact_state_slot<S>(a, s, i1, nb1, q);
+            for (int q = 0; q < kQ; ++q) f1[q] = *compact_state_slot<S>(a, cg, i1, nb1, q);
         }
         neumann_values(e, f1, solid1, r, p);
 #pragma unroll
@@ -245,7 +244,7 @@ __global__ void __launch_bounds__(kBlockThreads) face_compact_kernel(T* __restri
     }
 #pragma unroll
     for (int q = 0; q < kQ; ++q)
-        if ((ent >> q) & 1u) *compact_state_slot<S>(a, s, i, nb, q) = f[q];
+        if ((ent >> q) & 1u) *compact_state_slot<S>(a, cg, i, nb, q) = f[q];
 }
 
 }  // namespace lbm

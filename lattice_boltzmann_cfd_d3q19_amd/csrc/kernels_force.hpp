@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restric
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
             if constexpr (is_eso(S)) {
-                f[q] = a[compact_state_off<S>(g.s, i, nb, q)];
+                f[q] = a[compact_state_off<S>(g, i, nb, q)];
                 continue;
             }
             uint32_t off;

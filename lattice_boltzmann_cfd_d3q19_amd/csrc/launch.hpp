@@ -44,18 +44,24 @@ struct CompactTables {
     uint32_t* idxp;    // halo-padded cell -> compact index (kInvalid: solid / wall)
     uint32_t* cellp;   // compact index -> padded cell
     uint32_t* cellid;  // compact index -> cell index
+    uint32_t* bbase;   // esoteric pull: first bounce-back slot of each fluid cell (else null)
     uint32_t nf;       // fluid cells (known on the host after the build)
     uint64_t stride;   // population stride, nf rounded up to 64
 };
 
 // Byte offsets of the tables inside a workspace, and its size.
 struct CompactLayoutBytes {
-    size_t header, rows, idxp, cellp, cellid, total;
+    size_t header, rows, idxp, cellp, cellid, bbase, total;
 };
-CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz);
+// bounce: also the esoteric pull's bounce-back slot table (4 bytes per cell)
+CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz, bool bounce);
 
 // Build the compact tables from the mask and the periodic flags.
 hipError_t launch_compact_build(const LaunchGeom& g, const CompactTables& t, hipStream_t s);
+
+// Esoteric pull: bbase[i] = number of bounce-back links (x + c_k not fluid,
+// k < 9) of the fluid cells before i (an exclusive scan); needs t.nf.
+hipError_t launch_compact_bounce(const LaunchGeom& g, const CompactTables& t, hipStream_t s);
 
 template <typename T>
 hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& g, const CompactTables& t,

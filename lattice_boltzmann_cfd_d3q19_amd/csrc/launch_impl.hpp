@@ -211,6 +211,7 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     g.idxp = t.idxp;
     g.cellp = t.cellp;
     g.cellid = t.cellid;
+    g.bbase = t.bbase;
     g.nf = t.nf;
     g.px = (uint32_t)lg.nx + 2;
     g.pxy = (uint32_t)((lg.nx + 2) * (lg.ny + 2));

@@ -107,9 +107,13 @@ def test_esoteric_pull_buffers():
         assert st == capi.LBM_OK
         capi.lbm_destroy(h)
     big = dict(layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_ESOPULL)
-    # 3 * roundup(N, 64) * 4 < 2^32 <=> N < 2^28 / 0.75
-    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 341, capi.LBM_F32, **big))[0] == capi.LBM_OK
-    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 342, capi.LBM_F32, **big))[0] == capi.LBM_ERR_UNSUPPORTED
+    # the same two-plane offset limit as the other compact schemes
+    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F32, **big))[0] == capi.LBM_OK
+    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F64, **big))[0] == capi.LBM_ERR_UNSUPPORTED
+    # its workspace holds one more 4-byte table per cell (the bounce-back slots)
+    aa = capi.make_desc(16, 8, 5, capi.LBM_F32, layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_AA)
+    eso = capi.make_desc(16, 8, 5, capi.LBM_F32, layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_ESOPULL)
+    assert capi.lbm_workspace_bytes(eso)[1] == capi.lbm_workspace_bytes(aa)[1] + 2560
 
 
 def test_buffer_rules():
