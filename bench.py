@@ -106,6 +106,23 @@ def read_traffic(name, scheme, layout, kernel):
     return float(vals[key]) if key in vals else None
 
 
+def state_check(rho, u, mask=None):
+    """(finite, bounded) for moments rho[N], u[3][N] (numpy or torch): every
+    fluid value finite, and every fluid cell with rho > 0 and |u| below the
+    lattice speed 1 (a run past that bound has gone unstable)."""
+    import numpy as np
+    rho = rho.detach().cpu().numpy() if hasattr(rho, "detach") else np.asarray(rho)
+    u = u.detach().cpu().numpy() if hasattr(u, "detach") else np.asarray(u)
+    rho, u = rho.reshape(-1).astype(np.float64), u.reshape(3, -1).astype(np.float64)
+    if mask is not None:
+        fluid = np.asarray(mask).reshape(-1) == 0
+        rho, u = rho[fluid], u[:, fluid]
+    finite = bool(np.isfinite(rho).all() and np.isfinite(u).all())
+    with np.errstate(invalid="ignore", over="ignore"):
+        bounded = finite and bool((rho > 0).all() and (np.sqrt((u * u).sum(axis=0)) < 1.0).all())
+    return finite, bounded
+
+
 def cpu_baseline(wl, steps=3):
     """Time the single-threaded fp64 oracle on a few steps of the same box."""
     import numpy as np
@@ -215,10 +232,11 @@ def main():
 
     traffic = read_traffic(args.workload, args.scheme, args.layout, dominant)
 
-    # state sanity: finite moments after the run
-    rho, _ = lat.moments()
-    finite = bool(torch.isfinite(rho).all().item())
+    # state sanity after the run: finite, and below the lattice speed
+    rho, u = lat.moments()
     torch.cuda.synchronize()
+    finite, bounded = state_check(rho, u, mask)
+    del rho, u
 
     # plain copy reference (torch copy kernel, 2 GiB moved)
     src = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
@@ -265,6 +283,7 @@ def main():
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
         "copy_GBps": round(copy_gbps, 1),
         "state_finite": finite,
+        "state_bounded": bounded,
         "kernel_source": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
