@@ -117,6 +117,24 @@ __device__ __forceinline__ T ld_pop(const T* p)
 #endif
 }
 
+// The even step of the in-place pattern reads only its own cells' slots.
+// Nontemporal loads there (NT) measured faster on periodic boxes without a
+// mask in the SoA and bundle layouts (256^3: stream even + odd 0.471 + 0.491
+// -> 0.436 + 0.450 ms, bundle 0.475 + 0.546 -> 0.459 + 0.515 ms) and slower
+// with a mask (porous 256^3 stream: 0.555 + 0.583 -> 0.699 + 0.528 ms; the
+// 128^3 sphere also lost) and in the AoS layout (even step 0.550 -> 1.253 ms:
+// the 19 loads of a record share its lines), so the step kernel uses them
+// only in the no-mask instance of those two layouts.
+template <bool NT, typename T>
+__device__ __forceinline__ T ld_pop_own(const T* p)
+{
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(p);
+    } else {
+        return ld_pop(p);
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ void st_pop(T* p, T v)
 {
@@ -685,7 +703,7 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
         if constexpr (K == kAB) {
             f[q] = ld_pop(state_slot<kAB, L>(a, n, c, bits, q));
         } else if constexpr (K == kAAEven) {
-            f[q] = ld_pop(slot<L>(a, n, q, c.id));
+            f[q] = ld_pop_own<BND == 0 && L != kCollision>(slot<L>(a, n, q, c.id));
         } else if constexpr (K == kAAOdd) {
             f[q] = ld_pop(state_slot<kAAOdd, L>(a, n, c, bits, q));
         } else {
