@@ -403,3 +403,62 @@ def test_degenerate_boxes(name, precision):
     ref = results[("stream", "ab")]
     for k, v in results.items():
         assert np.array_equal(v, ref), f"{k} differs from stream/ab"
+
+
+_MASK512 = {}
+
+
+def _porous512():
+    if "m" not in _MASK512:
+        _MASK512["m"] = li.porous_mask(512)[0]
+    return _MASK512["m"]
+
+
+def _neighbourhood(cells, shape):
+    """The cells and their 18 neighbours (periodic wrap)."""
+    nx, ny, nz = shape
+    c, _, _ = oracle.lattice()
+    x, y, z = cells % nx, (cells // nx) % ny, cells // (nx * ny)
+    out = [cells]
+    for q in range(19):
+        out.append(((x + c[q][0]) % nx) + nx * (((y + c[q][1]) % ny) + ny * ((z + c[q][2]) % nz)))
+    return np.unique(np.concatenate(out))
+
+
+@pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "aa"), ("stream", "ab")])
+def test_full_size_512_sampled_steps(layout, scheme):
+    """The 512^3 porous medium (19,200 spheres, the large-footprint run): the
+    dense layouts address up to 19 x 2^27 elements here, past 2^31, and the
+    compact one 83 M fluid cells.  Two consecutive steps at sampled cells
+    against the oracle, evaluated from the GPU's own state: the state is
+    gathered on the GPU at the cells and their neighbours only, into an
+    otherwise untouched (lazily allocated) host array."""
+    need_gpu()
+    import torch
+    shape = (512, 512, 512)
+    n = 512 ** 3
+    mask = _porous512()
+    tau, F = 0.65, (1e-6, 0.0, 0.0)
+    say("full-size 512", layout, scheme)
+    lat = make(shape, "f32", layout, scheme, tau=tau, force=F, mask=mask)
+    box = oracle.Box(*shape, periodic=(1, 1, 1), tau=tau, force=F)
+    cells = _sample_cells(mask, n, 3000, seed=512)
+    near = _neighbourhood(cells, shape)
+    near_t = torch.from_numpy(near).cuda()
+    cells_t = torch.from_numpy(cells).cuda()
+    lat.step(5)
+    for _ in range(2):
+        prev = lat.read_populations()
+        f = np.zeros((19, n), np.float64)           # pages are touched only where filled
+        f[:, near] = prev.index_select(1, near_t).double().cpu().numpy()
+        del prev
+        lat.step(1)
+        cur = lat.read_populations().index_select(1, cells_t).double().cpu().numpy()
+        torch.cuda.synchronize()
+        want = oracle.step_cells(box, f, cells, mask)
+        err = np.max(np.abs(cur.T - want))
+        say("  one-step max-abs", err, "t =", lat.t, "cells", cells.size)
+        assert err <= 1e-6
+        del f
+    del lat
+    torch.cuda.empty_cache()
