@@ -279,6 +279,17 @@ lbm_status lbm_load_state(lbm_sim *sim, const void *s);
 lbm_status lbm_momentum_exchange_scratch_bytes(const lbm_desc *desc, size_t *bytes);
 lbm_status lbm_momentum_exchange(lbm_sim *sim, void *force, void *scratch, size_t scratch_bytes);
 
+/* n >= 1 steps as lbm_step, the last of which also sums its own momentum
+ * exchange into force (device double[6], as lbm_momentum_exchange): the same
+ * links, values and order of summation as lbm_momentum_exchange called just
+ * before that last step, taken from that step's own gathers and collision
+ * instead of a separate pass over the lattice (fieldcraft page, first
+ * section: the force is read back from the step that bounces the
+ * populations).  The state after the call equals that of lbm_step(sim, n)
+ * bit for bit.  scratch as for lbm_momentum_exchange (the same size).
+ * Errors as lbm_momentum_exchange, and LBM_ERR_INVALID_ARGUMENT for n < 1. */
+lbm_status lbm_step_momentum_exchange(lbm_sim *sim, int64_t n, void *force, void *scratch, size_t scratch_bytes);
+
 /* Release the handle (host memory only); NULL is a no-op. */
 lbm_status lbm_destroy(lbm_sim *sim);
 

@@ -380,8 +380,10 @@ lbm_status lbm_init_equilibrium(lbm_sim* sim, const void* rho, const void* u)
 namespace {
 
 // n steps; the last one also writes the density and velocity its collision
-// used into rho / u when they are given.
-lbm_status run_steps(lbm_sim* sim, int64_t n, void* rho, void* u)
+// used into rho / u when they are given, or sums its momentum exchange into
+// force (partial: the scratch rows) when that is given.
+lbm_status run_steps(lbm_sim* sim, int64_t n, void* rho, void* u, double* force = nullptr,
+                     double* partial = nullptr)
 {
     const lbm::LaunchGeom g = geom_of(sim);
     const lbm::LaunchPhys p = phys_of(sim);
@@ -399,7 +401,15 @@ lbm_status run_steps(lbm_sim* sim, int64_t n, void* rho, void* u)
         void* ro = i + 1 == n ? rho : nullptr;
         void* uo = i + 1 == n ? u : nullptr;
         hipError_t e;
-        if (compact(sim->d)) {
+        const lbm::CompactTables* t = compact(sim->d) ? &sim->tables : nullptr;
+        if (force != nullptr && i + 1 == n) {
+            if (sim->d.precision == LBM_F32)
+                e = lbm::launch_step_mex<float>(sim->d.layout, kind, (float*)a, (float*)b, g, t, p, partial, force,
+                                                sim->stream);
+            else
+                e = lbm::launch_step_mex<double>(sim->d.layout, kind, (double*)a, (double*)b, g, t, p, partial,
+                                                 force, sim->stream);
+        } else if (t != nullptr) {
             if (sim->d.precision == LBM_F32)
                 e = lbm::launch_step_compact<float>(kind, (float*)a, (float*)b, g, sim->tables, p, (float*)ro,
                                                     (float*)uo, sim->stream);
@@ -438,6 +448,17 @@ lbm_status lbm_step_moments(lbm_sim* sim, int64_t n, void* rho, void* u)
     if (sim == nullptr || n < 1 || rho == nullptr || u == nullptr) return LBM_ERR_INVALID_ARGUMENT;
     if (!sim->initialized) return LBM_ERR_BAD_STATE;
     return run_steps(sim, n, rho, u);
+}
+
+lbm_status lbm_step_momentum_exchange(lbm_sim* sim, int64_t n, void* force, void* scratch, size_t scratch_bytes)
+{
+    if (sim == nullptr || n < 1 || force == nullptr || scratch == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    size_t need = 0;
+    lbm_momentum_exchange_scratch_bytes(&sim->d, &need);
+    if (scratch_bytes < need) return LBM_ERR_INVALID_ARGUMENT;
+    if ((uintptr_t)scratch % kAlign != 0 || (uintptr_t)force % sizeof(double) != 0) return LBM_ERR_MISALIGNED;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    return run_steps(sim, n, nullptr, nullptr, (double*)force, (double*)scratch);
 }
 
 lbm_status lbm_moments(lbm_sim* sim, void* rho, void* u)

@@ -569,6 +569,7 @@ struct MomOut {
     T* rho;
     T* u;
     uint64_t n;
+    double* partial;  // fused momentum exchange: six sums per workgroup (MEX instances)
 };
 
 template <typename T>
@@ -606,6 +607,70 @@ __device__ __forceinline__ void shifted_equilibrium(T rho, T ux, T uy, T uz, T (
     LBM_SEQ_PAIR(8)
 #undef LBM_SEQ_PAIR
     s[9] = wq<T>(9) * (drho - rho * k15);
+}
+
+// ------------------------------------------------- momentum exchange sums
+//
+// During a step every population f*_q that leaves a fluid cell toward a solid
+// cell or through a wall comes back along -c_q (halfway bounce-back), so the
+// solid takes 2 f*_q c_q (fieldcraft page, first section: the momentum
+// exchange over the wall links of a step).  Sums are in double, per
+// workgroup in a fixed order, then over the workgroups in a fixed order.
+
+// v[0..5] summed over the workgroup (at most NT work-items, 2-D blocks
+// flattened x-fastest, which is how the hardware forms its waves); thread 0
+// writes the six sums to out.  Every work-item of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ void block_sum6(double (&v)[6], double* __restrict__ out)
+{
+    __shared__ double part[NT / 64][6];
+    const uint32_t tid = threadIdx.x + blockDim.x * threadIdx.y;
+#pragma unroll
+    for (int k = 0; k < 6; ++k)
+        for (int o = 32; o > 0; o >>= 1) v[k] += __shfl_down(v[k], o, 64);
+    if ((tid & 63u) == 0)
+#pragma unroll
+        for (int k = 0; k < 6; ++k) part[tid / 64][k] = v[k];
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+            double s = part[0][k];
+            for (uint32_t w = 1; w < (blockDim.x * blockDim.y + 63) / 64; ++w) s += part[w][k];
+            out[k] = s;
+        }
+    }
+}
+
+// Add 2 f*_q c_q of the outgoing link q (stored value s*_q = f*_q - w_q, w_q
+// rounded to T as in storage) to the solid (acc[0..2]) or wall (acc[3..5])
+// sums; f* is formed in double, so no rounding of s* + w to T.
+template <int q, typename T>
+__device__ __forceinline__ void add_link(double (&acc)[6], T spost, bool bounced, bool wall)
+{
+    const double v = bounced ? 2.0 * ((double)spost + (double)wq<T>(q)) : 0.0;
+    const double vs = wall ? 0.0 : v, vw = wall ? v : 0.0;
+    if constexpr (kCx[q] != 0) {
+        acc[0] += kCx[q] * vs;
+        acc[3] += kCx[q] * vw;
+    }
+    if constexpr (kCy[q] != 0) {
+        acc[1] += kCy[q] * vs;
+        acc[4] += kCy[q] * vw;
+    }
+    if constexpr (kCz[q] != 0) {
+        acc[2] += kCz[q] * vs;
+        acc[5] += kCz[q] * vw;
+    }
+}
+
+template <int q = 0, typename T, typename Pred>
+__device__ __forceinline__ void add_links(double (&acc)[6], const T (&s)[kQ], const Cell& c, Pred bounced)
+{
+    if constexpr (q < kQ) {
+        if constexpr (q != 9) add_link<q>(acc, s[q], bounced(q), beyond_wall(c, kCx[q], kCy[q], kCz[q]));
+        add_links<q + 1>(acc, s, c, bounced);
+    }
 }
 
 // ------------------------------------------------------ stored-state maps
@@ -676,23 +741,11 @@ __device__ __forceinline__ T* state_slot(T* buf, uint64_t n, const Cell& c, uint
 
 constexpr int kBlockThreads = 256;
 
-// One fused time step.  K: kAB (a = source, b = destination), kAAEven,
-// kAAOdd, kEsoEven or kEsoOdd (a = the single lattice).  BND: 0 = fully periodic, no mask;
-// 1 = a mask or a wall exists; 2 = also open faces (a separate instance, so
-// the reservoir selects cost the other kernels no registers).  OUT: also
-// write the density and velocity the collision used (0 on solid cells).
-template <typename T, int L, int K, int BND, bool FORCE, bool OUT>
-__global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, T* __restrict__ b,
-                                                             Geom g, Phys<T> p, MomOut<T> mo)
+// The update of one fluid cell by step_kernel.
+template <typename T, int L, int K, int BND, bool FORCE, bool OUT, bool MEX>
+__device__ __forceinline__ void step_cell(T* __restrict__ a, T* __restrict__ b, const Geom& g, const Phys<T>& p,
+                                          const MomOut<T>& mo, const Cell& c, double (&acc)[6])
 {
-    Cell c;
-    if (!locate(g, c)) return;
-    if constexpr (BND) {
-        if (g.mask != nullptr && g.mask[c.id] != 0) {  // solid cells are never updated
-            if constexpr (OUT) write_moments(mo, c.id, T(0), T(0), T(0), T(0));
-            return;
-        }
-    }
     const uint32_t bits = link_bits<BND != 0>(g, c);
     const uint32_t obits = BND == 2 ? open_bits(g, c) : 0u;  // populations entering through open faces
     const uint64_t n = g.n;
@@ -717,6 +770,13 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
     T rho, ux, uy, uz;
     collide<T, FORCE>(f, p, rho, ux, uy, uz);
     if constexpr (OUT) write_moments(mo, c.id, rho, ux, uy, uz);
+    if constexpr (MEX) {
+        // x + c_q is solid or beyond a wall iff the upstream bit of opp(q) is
+        // set; a face with a face rule sets it too, but its links carry flux
+        add_links(acc, f, c, [&](int q) {
+            return ((bits >> opp(q)) & 1u) != 0 && !beyond_rule_face(g, c, kCx[q], kCy[q], kCz[q]);
+        });
+    }
     if constexpr (BND == 2 && K == kAAOdd) open_outflow(f, obits, p, c);
 
 #pragma unroll
@@ -739,6 +799,39 @@ __global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, 
             const uint64_t far = slot_off<L>(n, q, nbr(c, kCx[q], kCy[q], kCz[q]));
             st_pop(a + (own_slot ? own : far), f[q]);
         }
+    }
+}
+
+// One fused time step.  K: kAB (a = source, b = destination), kAAEven,
+// kAAOdd, kEsoEven or kEsoOdd (a = the single lattice).  BND: 0 = fully
+// periodic, no mask; 1 = a mask or a wall exists; 2 = also open faces (a
+// separate instance, so the reservoir selects cost the other kernels no
+// registers).  OUT: also write the density and velocity the collision used
+// (0 on solid cells).  MEX: also sum the momentum exchange of the step over
+// the workgroup into mo.partial (row = the workgroup's tile).
+template <typename T, int L, int K, int BND, bool FORCE, bool OUT, bool MEX = false>
+__global__ void __launch_bounds__(kBlockThreads) step_kernel(T* __restrict__ a, T* __restrict__ b,
+                                                             Geom g, Phys<T> p, MomOut<T> mo)
+{
+    static_assert(!MEX || BND != 0, "a periodic box without mask has no bounce-back links");
+    Cell c;
+    bool active = locate(g, c);
+    if constexpr (BND) {
+        if (active && g.mask != nullptr && g.mask[c.id] != 0) {  // solid cells are never updated
+            if constexpr (OUT) write_moments(mo, c.id, T(0), T(0), T(0), T(0));
+            active = false;
+        }
+    }
+    if constexpr (!MEX) {
+        if (!active) return;
+    }
+    // MEX: also the momentum exchange of this step (the workgroup's sums go
+    // to mo.partial; every work-item reaches the reduction)
+    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    if (active) step_cell<T, L, K, BND, FORCE, OUT, MEX>(a, b, g, p, mo, c, acc);
+    if constexpr (MEX) {
+        const uint32_t tile = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
+        if (tile < g.ntiles) block_sum6<kBlockThreads>(acc, mo.partial + 6 * (size_t)tile);
     }
 }
 

@@ -149,6 +149,18 @@ __device__ __forceinline__ void neighbours_rows(const CompactGeom& g, uint32_t p
     }
 }
 
+// Momentum exchange on the compact store: the index table marks wall links
+// (kWall) apart from solid ones (kInvalid) and from open faces (kOpen + k,
+// which carry no force).
+template <int q = 0, typename T>
+__device__ __forceinline__ void add_links_nb(double (&acc)[6], const T (&s)[kQ], const uint32_t (&nb)[kQ])
+{
+    if constexpr (q < kQ) {
+        if constexpr (q != 9) add_link<q>(acc, s[q], bounced(nb[q]), nb[q] == kWall);
+        add_links_nb<q + 1>(acc, s, nb);
+    }
+}
+
 // Storage order of the populations: opposite directions side by side.  Pair
 // k = 0..8 holds directions k and 18 - k in planes 2k and 2k + 1 (sub-planes
 // 0 and 1); the rest population is plane 18.  Every access of a step kernel
@@ -290,14 +302,11 @@ __device__ __forceinline__ char* pair_block(char* base, int k, uint32_t plane_by
 // step of the in-place pattern (K = kAAOdd, a = the lattice).  OPEN: some
 // faces are open (a separate instance: the reservoir selects would cost the
 // other cases registers).
-template <typename T, int K, bool FORCE, bool OPEN, bool OUT>
-__global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restrict__ a, T* __restrict__ b,
-                                                                     CompactGeom g, Phys<T> p, MomOut<T> mo)
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
+__device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restrict__ b, const CompactGeom& g,
+                                                  const Phys<T>& p, const MomOut<T>& mo, uint32_t i,
+                                                  double (&acc)[6])
 {
-    static_assert(K == kAB || K == kAAOdd, "the even step has its own kernel");
-    const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
-    const uint32_t i = wg * kGatherThreads + threadIdx.x;
-    if (i >= g.nf) return;
     const uint32_t sb = g.s * (uint32_t)sizeof(T);  // bytes per plane; 2 sb < 2^32 (host check)
     const uint32_t own0 = i * (uint32_t)sizeof(T);  // own slot in sub-plane 0 / 1 of a block
     const uint32_t own1 = own0 + sb;
@@ -319,6 +328,7 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
         T rho, ux, uy, uz;
         collide<T, FORCE>(f, p, rho, ux, uy, uz);
         if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
+        if constexpr (MEX) add_links_nb(acc, f, nb);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(B, pair_of(q), sb), sub_of(q) ? own1 : own0, f[q]);
     } else {
@@ -334,6 +344,7 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
         T rho, ux, uy, uz;
         collide<T, FORCE>(f, p, rho, ux, uy, uz);
         if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
+        if constexpr (MEX) add_links_nb(acc, f, nb);
         // beyond an open face, f*_d leaves the box and the own slot (opp d, x)
         // takes the reservoir's population entering along -c_d
         if constexpr (OPEN) open_outflow(f, nb, p);
@@ -342,20 +353,37 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
     }
 }
 
+// Gather step over the fluid cells, one work-item per fluid cell (see
+// step_compact_cell).  MEX: also sum the momentum exchange of the step over
+// the workgroup into mo.partial (row = the logical workgroup).
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false>
+__global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restrict__ a, T* __restrict__ b,
+                                                                     CompactGeom g, Phys<T> p, MomOut<T> mo)
+{
+    static_assert(K == kAB || K == kAAOdd, "the even step has its own kernel");
+    const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
+    const uint32_t i = wg * kGatherThreads + threadIdx.x;
+    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    if constexpr (!MEX) {
+        if (i >= g.nf) return;
+        step_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, b, g, p, mo, i, acc);
+    } else {
+        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, b, g, p, mo, i, acc);
+        if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
+            block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
+    }
+}
+
 // Esoteric-pull step on the compact store (K = kEsoEven / kEsoOdd; the
 // slot map is described at compact_state_off).  The own side of pair k and
 // a fluid neighbour side lie in the pair's two-plane block (a uniform base
 // plus a 32-bit byte offset, as in the other compact kernels); a bounced
 // neighbour side goes to the packed bounce-back region instead.
-template <typename T, int K, bool FORCE, bool OPEN, bool OUT>
-__global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restrict__ a, CompactGeom g, Phys<T> p,
-                                                                    MomOut<T> mo)
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
+__device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const CompactGeom& g, const Phys<T>& p,
+                                                 const MomOut<T>& mo, uint32_t i, double (&acc)[6])
 {
-    static_assert(is_eso(K), "esoteric-pull step");
     constexpr uint32_t P = K == kEsoOdd ? 1u : 0u;
-    const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
-    const uint32_t i = wg * kGatherThreads + threadIdx.x;
-    if (i >= g.nf) return;
     const uint32_t sb = g.s * (uint32_t)sizeof(T);
     const uint32_t own = i * (uint32_t)sizeof(T);
     char* const A = (char*)a;
@@ -385,12 +413,31 @@ __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restri
     T rho, ux, uy, uz;
     collide<T, FORCE>(f, p, rho, ux, uy, uz);
     if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
+    if constexpr (MEX) add_links_nb(acc, f, nb);
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
         *nb_ptr[k] = f[k];                                          // f*_k streams to x + c_k
         st_at<false>(pair_block(A, k, sb), own_off[k], f[opp(k)]);  // f*_opp(k) streams to x - c_k
     }
     st_at<false>(rest, own, f[9]);
+}
+
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false>
+__global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restrict__ a, CompactGeom g, Phys<T> p,
+                                                                    MomOut<T> mo)
+{
+    static_assert(is_eso(K), "esoteric-pull step");
+    const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
+    const uint32_t i = wg * kGatherThreads + threadIdx.x;
+    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    if constexpr (!MEX) {
+        if (i >= g.nf) return;
+        eso_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, mo, i, acc);
+    } else {
+        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, g, p, mo, i, acc);
+        if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
+            block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
+    }
 }
 
 // Even step of the in-place pattern: purely local, read (q, i), write
@@ -419,6 +466,34 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_kernel(T* __restric
         if (i < nf) write_moments(mo, cellid[i], rho, ux, uy, uz);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(A, pair_of(q), sb), sub_of(opp(q)) ? own1 : own0, f[q]);
+}
+
+// The even step with the momentum exchange of that step: the same purely
+// local update (fluid cells only), plus the neighbour table to know which
+// links are bounced back; the workgroup's sums go to mo.partial.
+template <typename T, bool FORCE>
+__global__ void __launch_bounds__(kEvenThreads) even_compact_mex_kernel(T* __restrict__ a, CompactGeom g,
+                                                                        Phys<T> p, MomOut<T> mo)
+{
+    const uint32_t i = blockIdx.x * kEvenThreads + threadIdx.x;
+    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    if (i < g.nf) {
+        const uint32_t sb = g.s * (uint32_t)sizeof(T);
+        const uint32_t own0 = i * (uint32_t)sizeof(T);
+        const uint32_t own1 = own0 + sb;
+        char* const A = (char*)a;
+        uint32_t nb[kQ];
+        neighbours_rows(g, g.cellp[i], nb);
+        T f[kQ];
+#pragma unroll
+        for (int q = 0; q < kQ; ++q)
+            f[q] = __builtin_nontemporal_load((const T*)(pair_block(A, pair_of(q), sb) + (sub_of(q) ? own1 : own0)));
+        collide<T, FORCE>(f, p);
+        add_links_nb(acc, f, nb);
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(A, pair_of(q), sb), sub_of(opp(q)) ? own1 : own0, f[q]);
+    }
+    block_sum6<kEvenThreads>(acc, mo.partial + 6 * (size_t)blockIdx.x);
 }
 
 // rho and u := 0 on the solid cells (the fields of a compact step; the step
@@ -457,7 +532,6 @@ __global__ void __launch_bounds__(kBlockThreads) io_compact_kernel(T* __restrict
     }
     uint32_t nb[kQ];
     neighbours(cg, cg.cellp[i], nb);
-    const uint64_t s = cg.s;
     T f[kQ];
     if constexpr (OP == kReadF || OP == kReadMoments || OP == kReadS) {
 #pragma unroll

@@ -19,61 +19,6 @@
 
 namespace lbm {
 
-// v[0..5] summed over the workgroup (256 work-items, 2-D blocks flattened
-// x-fastest, which is how the hardware forms its waves); thread 0 writes the
-// six sums to out.
-__device__ __forceinline__ void block_sum6(double (&v)[6], double* __restrict__ out)
-{
-    __shared__ double part[kBlockThreads / 64][6];
-    const uint32_t tid = threadIdx.x + blockDim.x * threadIdx.y;
-#pragma unroll
-    for (int k = 0; k < 6; ++k)
-        for (int o = 32; o > 0; o >>= 1) v[k] += __shfl_down(v[k], o, 64);
-    if ((tid & 63u) == 0)
-#pragma unroll
-        for (int k = 0; k < 6; ++k) part[tid / 64][k] = v[k];
-    __syncthreads();
-    if (tid == 0) {
-#pragma unroll
-        for (int k = 0; k < 6; ++k) {
-            double s = part[0][k];
-            for (uint32_t w = 1; w < (blockDim.x * blockDim.y + 63) / 64; ++w) s += part[w][k];
-            out[k] = s;
-        }
-    }
-}
-
-// Add 2 f*_q c_q of the outgoing link q (stored value s*_q = f*_q - w_q, w_q
-// rounded to T as in storage) to the solid (acc[0..2]) or wall (acc[3..5])
-// sums; f* is formed in double, so no rounding of s* + w to T.
-template <int q, typename T>
-__device__ __forceinline__ void add_link(double (&acc)[6], T spost, bool bounced, bool wall)
-{
-    const double v = bounced ? 2.0 * ((double)spost + (double)wq<T>(q)) : 0.0;
-    const double vs = wall ? 0.0 : v, vw = wall ? v : 0.0;
-    if constexpr (kCx[q] != 0) {
-        acc[0] += kCx[q] * vs;
-        acc[3] += kCx[q] * vw;
-    }
-    if constexpr (kCy[q] != 0) {
-        acc[1] += kCy[q] * vs;
-        acc[4] += kCy[q] * vw;
-    }
-    if constexpr (kCz[q] != 0) {
-        acc[2] += kCz[q] * vs;
-        acc[5] += kCz[q] * vw;
-    }
-}
-
-template <int q = 0, typename T, typename Pred>
-__device__ __forceinline__ void add_links(double (&acc)[6], const T (&s)[kQ], const Cell& c, Pred bounced)
-{
-    if constexpr (q < kQ) {
-        if constexpr (q != 9) add_link<q>(acc, s[q], bounced(q), beyond_wall(c, kCx[q], kCy[q], kCz[q]));
-        add_links<q + 1>(acc, s, c, bounced);
-    }
-}
-
 // Dense layouts: one work-item per cell (tile mapping of the step kernels),
 // one partial row of six doubles per workgroup.
 template <typename T, int L, int S>
@@ -96,17 +41,9 @@ __global__ void __launch_bounds__(kBlockThreads) mex_kernel(T* __restrict__ a, G
             return ((bits >> opp(q)) & 1u) != 0 && !beyond_rule_face(g, c, kCx[q], kCy[q], kCz[q]);
         });
     }
-    block_sum6(acc, partial + 6 * (size_t)blockIdx.x);
+    block_sum6<kBlockThreads>(acc, partial + 6 * (size_t)blockIdx.x);
 }
 
-template <int q = 0, typename T>
-__device__ __forceinline__ void add_links_nb(double (&acc)[6], const T (&s)[kQ], const uint32_t (&nb)[kQ])
-{
-    if constexpr (q < kQ) {
-        if constexpr (q != 9) add_link<q>(acc, s[q], bounced(nb[q]), nb[q] == kWall);
-        add_links_nb<q + 1>(acc, s, nb);
-    }
-}
 
 // Compact layout: one work-item per fluid cell, the gathers of the step
 // kernels (row-wise neighbour reads, the same slot maps), one partial row per
@@ -147,7 +84,7 @@ __global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restric
         collide<T, true>(f, p);
         add_links_nb(acc, f, nb);
     }
-    block_sum6(acc, partial + 6 * (size_t)blockIdx.x);
+    block_sum6<kBlockThreads>(acc, partial + 6 * (size_t)blockIdx.x);
 }
 
 // out[0..5] = sum of the n partial rows, in row order per work-item, then the
@@ -159,7 +96,7 @@ static __global__ void __launch_bounds__(kBlockThreads) mex_sum_kernel(const dou
     for (uint32_t r = threadIdx.x; r < n; r += kBlockThreads)
 #pragma unroll
         for (int k = 0; k < 6; ++k) acc[k] += partial[6 * (size_t)r + k];
-    block_sum6(acc, out);
+    block_sum6<kBlockThreads>(acc, out);
 }
 
 }  // namespace lbm

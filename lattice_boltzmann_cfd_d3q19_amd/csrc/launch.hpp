@@ -87,4 +87,12 @@ template <typename T>
 hipError_t launch_momentum_exchange(int layout, int state, T* a, const LaunchGeom& g, const CompactTables* t,
                                     const LaunchPhys& p, double* partial, double* force, hipStream_t s);
 
+// One step of kind `kind` (as launch_step / launch_step_compact; t null for a
+// dense layout) that also sums the momentum exchange of its own bounce-back
+// links into force[0..5] (as launch_momentum_exchange for the state the step
+// starts from).  partial: device double[6 * mex_partial_rows(g)].
+template <typename T>
+hipError_t launch_step_mex(int layout, int kind, T* a, T* b, const LaunchGeom& g, const CompactTables* t,
+                           const LaunchPhys& p, double* partial, double* force, hipStream_t s);
+
 }  // namespace lbm

@@ -14,6 +14,8 @@ template hipError_t launch_face_rules<float>(int, int, float*, const LaunchGeom&
                                             hipStream_t);
 template hipError_t launch_momentum_exchange<float>(int, int, float*, const LaunchGeom&, const CompactTables*,
                                                     const LaunchPhys&, double*, double*, hipStream_t);
+template hipError_t launch_step_mex<float>(int, int, float*, float*, const LaunchGeom&, const CompactTables*,
+                                          const LaunchPhys&, double*, double*, hipStream_t);
 
 // workgroups of the momentum-exchange pass (precision-independent)
 size_t mex_partial_rows(const LaunchGeom& g) { return make_shape(g).grid.x; }

@@ -14,4 +14,6 @@ template hipError_t launch_face_rules<double>(int, int, double*, const LaunchGeo
                                             hipStream_t);
 template hipError_t launch_momentum_exchange<double>(int, int, double*, const LaunchGeom&, const CompactTables*,
                                                     const LaunchPhys&, double*, double*, hipStream_t);
+template hipError_t launch_step_mex<double>(int, int, double*, double*, const LaunchGeom&, const CompactTables*,
+                                          const LaunchPhys&, double*, double*, hipStream_t);
 }  // namespace lbm

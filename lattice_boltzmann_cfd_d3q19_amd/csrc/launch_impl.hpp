@@ -98,8 +98,17 @@ hipError_t launch_step_t(T* a, T* b, const Shape& s, const Phys<T>& p, const Mom
     MomOut<T> m = mo;
     void* args[] = {&a, &b, &g, &ph, &m};
     // hipLaunchKernel reports the status of this launch only (no stale errors)
-    const void* k = mo.rho != nullptr ? (const void*)&step_kernel<T, L, K, BND, FORCE, true>
-                                      : (const void*)&step_kernel<T, L, K, BND, FORCE, false>;
+    const void* k;
+    if constexpr (BND != 0) {
+        // the fused momentum exchange (no field output in the same step)
+        if (mo.partial != nullptr) {
+            if (mo.rho != nullptr) return hipErrorInvalidValue;
+            return hipLaunchKernel((const void*)&step_kernel<T, L, K, BND, FORCE, false, true>, s.grid, s.block, args,
+                                   0, st);
+        }
+    }
+    k = mo.rho != nullptr ? (const void*)&step_kernel<T, L, K, BND, FORCE, true>
+                          : (const void*)&step_kernel<T, L, K, BND, FORCE, false>;
     return hipLaunchKernel(k, s.grid, s.block, args, 0, st);
 }
 
@@ -131,23 +140,35 @@ hipError_t launch_step_l(int kind, T* a, T* b, const Shape& s, const Phys<T>& p,
     }
 }
 
+inline int boundary_instance(const LaunchGeom& lg)
+{
+    return lg.res != 0 ? 2 : (lg.mask != nullptr || !lg.periodic[0] || !lg.periodic[1] || !lg.periodic[2]);
+}
+
 template <typename T>
-hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp, T* rho_out,
-                       T* u_out, hipStream_t st)
+hipError_t launch_step_mo(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp,
+                          const MomOut<T>& mo, hipStream_t st)
 {
     // XCD-chunked tile order for the AoS layout only.  Measured, 256^3 porous
     // box, hardware order -> chunked: collision AA odd 2.06 -> 1.22 ms, AB
     // 0.92 -> 0.78 ms; stream AA +8% / +2% and AB +7%, bundle within 2%.
     const Shape s = make_shape(lg, layout == kCollision);
     const Phys<T> p = make_phys<T>(lp);
-    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz};
-    const int bnd = lg.res != 0 ? 2 : (lg.mask != nullptr || !lg.periodic[0] || !lg.periodic[1] || !lg.periodic[2]);
+    const int bnd = boundary_instance(lg);
     switch (layout) {
     case kStream: return launch_step_l<T, kStream>(kind, a, b, s, p, mo, bnd, lp.has_force, st);
     case kBundle: return launch_step_l<T, kBundle>(kind, a, b, s, p, mo, bnd, lp.has_force, st);
     case kCollision: return launch_step_l<T, kCollision>(kind, a, b, s, p, mo, bnd, lp.has_force, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <typename T>
+hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp, T* rho_out,
+                       T* u_out, hipStream_t st)
+{
+    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz, nullptr};
+    return launch_step_mo<T>(layout, kind, a, b, lg, lp, mo, st);
 }
 
 template <typename T, int L, int S, int OP>
@@ -238,6 +259,12 @@ hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, MomOut<T>
     if (g.xk > 1) nwg = (nwg + 8 * g.xk - 1) / (8 * g.xk) * (8 * g.xk);
     const dim3 grid(nwg), block(kGatherThreads);
     const bool out = mo.rho != nullptr;
+    if (mo.partial != nullptr) {
+        if (out) return hipErrorInvalidValue;
+        const void* k = g.open ? (const void*)&step_compact_kernel<T, K, FORCE, true, false, true>
+                               : (const void*)&step_compact_kernel<T, K, FORCE, false, false, true>;
+        return hipLaunchKernel(k, grid, block, args, 0, st);
+    }
     const void* k = g.open ? (out ? (const void*)&step_compact_kernel<T, K, FORCE, true, true>
                                   : (const void*)&step_compact_kernel<T, K, FORCE, true, false>)
                            : (out ? (const void*)&step_compact_kernel<T, K, FORCE, false, true>
@@ -249,6 +276,12 @@ template <typename T, bool FORCE>
 hipError_t launch_even_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, hipStream_t st)
 {
     if (g.nf == 0) return hipSuccess;
+    if (mo.partial != nullptr) {
+        if (mo.rho != nullptr) return hipErrorInvalidValue;
+        void* args[] = {&a, &g, &p, &mo};
+        const dim3 grid((g.s + kEvenThreads - 1) / kEvenThreads), block(kEvenThreads);
+        return hipLaunchKernel((const void*)&even_compact_mex_kernel<T, FORCE>, grid, block, args, 0, st);
+    }
     uint32_t s = g.s, nf = g.nf;
     const uint32_t* cellid = g.cellid;
     void* args[] = {&a, &s, &p, &mo, &cellid, &nf};
@@ -267,6 +300,12 @@ hipError_t launch_eso_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, hi
     if (g.xk > 1) nwg = (nwg + 8 * g.xk - 1) / (8 * g.xk) * (8 * g.xk);
     const dim3 grid(nwg), block(kGatherThreads);
     const bool out = mo.rho != nullptr;
+    if (mo.partial != nullptr) {
+        if (out) return hipErrorInvalidValue;
+        const void* k = g.open ? (const void*)&eso_compact_kernel<T, K, FORCE, true, false, true>
+                               : (const void*)&eso_compact_kernel<T, K, FORCE, false, false, true>;
+        return hipLaunchKernel(k, grid, block, args, 0, st);
+    }
     const void* k = g.open ? (out ? (const void*)&eso_compact_kernel<T, K, FORCE, true, true>
                                   : (const void*)&eso_compact_kernel<T, K, FORCE, true, false>)
                            : (out ? (const void*)&eso_compact_kernel<T, K, FORCE, false, true>
@@ -288,13 +327,12 @@ hipError_t launch_step_compact_k(T* a, T* b, CompactGeom g, Phys<T> p, MomOut<T>
 }
 
 template <typename T>
-hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& lg, const CompactTables& t,
-                               const LaunchPhys& lp, T* rho_out, T* u_out, hipStream_t st)
+hipError_t launch_step_compact_mo(int kind, T* a, T* b, const LaunchGeom& lg, const CompactTables& t,
+                                  const LaunchPhys& lp, const MomOut<T>& mo, hipStream_t st)
 {
     const CompactGeom g = compact_geom(lg, t);
     const Phys<T> p = make_phys<T>(lp);
-    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz};
-    if (rho_out != nullptr && lg.mask != nullptr) {
+    if (mo.rho != nullptr && lg.mask != nullptr) {
         // solid cells get zeros here; the step writes the fluid cells
         const uint64_t blocks = (mo.n + kBlockThreads - 1) / kBlockThreads;
         MomOut<T> m = mo;
@@ -312,6 +350,14 @@ hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& lg, const
     case kEsoOdd: return launch_step_compact_k<T, kEsoOdd>(a, b, g, p, mo, lp.has_force, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <typename T>
+hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& lg, const CompactTables& t,
+                               const LaunchPhys& lp, T* rho_out, T* u_out, hipStream_t st)
+{
+    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz, nullptr};
+    return launch_step_compact_mo<T>(kind, a, b, lg, t, lp, mo, st);
 }
 
 template <typename T, int S, int OP>
@@ -450,6 +496,14 @@ hipError_t launch_face_rules(int layout, int state, T* a, const LaunchGeom& lg, 
 
 // ------------------------------------------------------ momentum exchange
 
+// force[0..5] = the sum of partial rows 0 .. rows - 1 (zeros if rows = 0)
+inline hipError_t launch_mex_sum(double* partial, uint32_t rows, double* force, hipStream_t st)
+{
+    const double* part = partial;
+    void* args[] = {&part, &rows, &force};
+    return hipLaunchKernel((const void*)&mex_sum_kernel, dim3(1), dim3(kBlockThreads), args, 0, st);
+}
+
 template <typename T, int L, int S>
 hipError_t launch_mex_t(T* a, const Shape& sh, const Phys<T>& p, double* partial, hipStream_t st)
 {
@@ -513,9 +567,40 @@ hipError_t launch_momentum_exchange(int layout, int state, T* a, const LaunchGeo
         }
     }
     if (e != hipSuccess) return e;
-    const double* part = partial;
-    void* args[] = {&part, &rows, &force};
-    return hipLaunchKernel((const void*)&mex_sum_kernel, dim3(1), dim3(kBlockThreads), args, 0, st);
+    return launch_mex_sum(partial, rows, force, st);
+}
+
+// Fused variant: the step's own gathers and collision give the exchanged
+// momentum, so the separate pass (a second read of the lattice) is not needed.
+// Partial rows: the dense tiles (the fully periodic box without mask has no
+// bounce-back link and writes none), the compact step's workgroups (fewer:
+// at least 256 work-items each).
+static_assert(kGatherThreads >= kBlockThreads && kEvenThreads >= kBlockThreads,
+              "the compact steps' partial rows must fit in the dense layouts' scratch");
+
+template <typename T>
+hipError_t launch_step_mex(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const CompactTables* t,
+                           const LaunchPhys& lp, double* partial, double* force, hipStream_t st)
+{
+    const MomOut<T> mo{nullptr, nullptr, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz, partial};
+    uint32_t rows;
+    hipError_t e;
+    if (t != nullptr) {
+        const uint32_t nf = t->nf;
+        const uint32_t s = (uint32_t)t->stride;
+        rows = nf == 0 ? 0u
+               : kind == kAAEven ? (s + kEvenThreads - 1) / kEvenThreads
+                                 : (nf + kGatherThreads - 1) / kGatherThreads;
+        e = launch_step_compact_mo<T>(kind, a, b, lg, *t, lp, mo, st);
+    } else if (boundary_instance(lg) == 0) {
+        rows = 0;
+        e = launch_step<T>(layout, kind, a, b, lg, lp, nullptr, nullptr, st);
+    } else {
+        rows = make_shape(lg).g.ntiles;
+        e = launch_step_mo<T>(layout, kind, a, b, lg, lp, mo, st);
+    }
+    if (e != hipSuccess) return e;
+    return launch_mex_sum(partial, rows, force, st);
 }
 
 }  // namespace lbm

@@ -126,16 +126,29 @@ class Lattice:
         capi.check(capi.lbm_write_populations(self.handle, ff.data_ptr()), "lbm_write_populations", self.handle)
         self._keep = (ff,)
 
-    def momentum_exchange(self):
-        """Force on the solids during the step that starts from the current
-        state: (solid, wall), each a float64 tensor of 3 on the device."""
+    def _mex_buffer(self):
         if getattr(self, "_mex_scratch", None) is None:
             st, nb = capi.lbm_momentum_exchange_scratch_bytes(self.desc)
             capi.check(st, "lbm_momentum_exchange_scratch_bytes")
             self._mex_scratch = torch.empty(nb, dtype=torch.uint8, device=self.device)
+        return self._mex_scratch
+
+    def momentum_exchange(self):
+        """Force on the solids during the step that starts from the current
+        state: (solid, wall), each a float64 tensor of 3 on the device."""
+        scratch = self._mex_buffer()
         out = torch.empty(6, dtype=torch.float64, device=self.device)
-        capi.check(capi.lbm_momentum_exchange(self.handle, out.data_ptr(), self._mex_scratch.data_ptr(),
-                                              self._mex_scratch.numel()), "lbm_momentum_exchange", self.handle)
+        capi.check(capi.lbm_momentum_exchange(self.handle, out.data_ptr(), scratch.data_ptr(), scratch.numel()),
+                   "lbm_momentum_exchange", self.handle)
+        return out[0:3], out[3:6]
+
+    def step_momentum_exchange(self, n=1):
+        """n steps; the force on the solids during the last one, taken inside
+        that step: (solid, wall) as momentum_exchange() just before it."""
+        scratch = self._mex_buffer()
+        out = torch.empty(6, dtype=torch.float64, device=self.device)
+        capi.check(capi.lbm_step_momentum_exchange(self.handle, n, out.data_ptr(), scratch.data_ptr(),
+                                                   scratch.numel()), "lbm_step_momentum_exchange", self.handle)
         return out[0:3], out[3:6]
 
     def save_state(self):
