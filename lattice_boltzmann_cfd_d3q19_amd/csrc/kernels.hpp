@@ -310,6 +310,16 @@ struct Entering {
     static constexpr int f1 = a1 < 0 ? -1 : 2 * a1 + (c1 > 0 ? 0 : 1);
 };
 
+// v, pinned in a register.  "Loaded value or reservoir constant" is
+// otherwise turned into one load through a selected pointer (a flat load,
+// and the constant copied to private memory for it to point at).
+template <typename T>
+__device__ __forceinline__ T in_register(T v)
+{
+    asm("" : "+v"(v));
+    return v;
+}
+
 // The reservoir value of population q entering c (stored, shifted form).
 template <int q, typename T>
 __device__ __forceinline__ T entering_value(const Phys<T>& p, const Cell& c)
@@ -339,7 +349,7 @@ template <int q = 0, typename T>
 __device__ __forceinline__ void apply_open(T (&f)[kQ], uint32_t obits, const Phys<T>& p, const Cell& c)
 {
     if constexpr (q < kQ) {
-        if constexpr (q != 9) f[q] = ((obits >> q) & 1u) ? entering_value<q>(p, c) : f[q];
+        if constexpr (q != 9) f[q] = ((obits >> q) & 1u) ? entering_value<q>(p, c) : in_register(f[q]);
         apply_open<q + 1>(f, obits, p, c);
     }
 }
@@ -770,13 +780,14 @@ __device__ __forceinline__ void step_cell(T* __restrict__ a, T* __restrict__ b, 
     T rho, ux, uy, uz;
     collide<T, FORCE>(f, p, rho, ux, uy, uz);
     if constexpr (OUT) write_moments(mo, c.id, rho, ux, uy, uz);
-    if constexpr (MEX) {
-        // x + c_q is solid or beyond a wall iff the upstream bit of opp(q) is
-        // set; a face with a face rule sets it too, but its links carry flux
-        add_links(acc, f, c, [&](int q) {
-            return ((bits >> opp(q)) & 1u) != 0 && !beyond_rule_face(g, c, kCx[q], kCy[q], kCz[q]);
-        });
-    }
+    // MEX: x + c_q is solid or beyond a wall iff the upstream bit of opp(q)
+    // is set; a face with a face rule sets it too, but its links carry flux.
+    // Summed after the stores (f is still f*), unless open_outflow changes f.
+    constexpr bool kMexEarly = BND == 2 && K == kAAOdd;
+    const auto link_bounced = [&](int q) {
+        return ((bits >> opp(q)) & 1u) != 0 && !beyond_rule_face(g, c, kCx[q], kCy[q], kCz[q]);
+    };
+    if constexpr (MEX && kMexEarly) add_links(acc, f, c, link_bounced);
     if constexpr (BND == 2 && K == kAAOdd) open_outflow(f, obits, p, c);
 
 #pragma unroll
@@ -800,6 +811,7 @@ __device__ __forceinline__ void step_cell(T* __restrict__ a, T* __restrict__ b, 
             st_pop(a + (own_slot ? own : far), f[q]);
         }
     }
+    if constexpr (MEX && !kMexEarly) add_links(acc, f, c, link_bounced);
 }
 
 // One fused time step.  K: kAB (a = source, b = destination), kAAEven,

@@ -62,7 +62,7 @@ template <int q = 0, typename T>
 __device__ __forceinline__ void apply_open_nb(T (&f)[kQ], const uint32_t (&nb)[kQ], const Phys<T>& p)
 {
     if constexpr (q < kQ) {
-        if constexpr (q != 9) f[q] = is_res(nb[opp(q)], p.res) ? entering_value_nb<q>(p, nb[opp(q)]) : f[q];
+        if constexpr (q != 9) f[q] = is_res(nb[opp(q)], p.res) ? entering_value_nb<q>(p, nb[opp(q)]) : in_register(f[q]);
         apply_open_nb<q + 1>(f, nb, p);
     }
 }
@@ -146,6 +146,30 @@ __device__ __forceinline__ void neighbours_rows(const CompactGeom& g, uint32_t p
             const u32x3_a4& v = r[kCz[d] + 1][kCy[d] + 1];
             nb[d] = kCx[d] < 0 ? v.x : kCx[d] == 0 ? v.y : v.z;
         }
+    }
+}
+
+// Bit q of bm: link q is bounced back (x + c_q solid or beyond a wall); of
+// wm: it leaves through a wall.  Taken right after the table reads, so the
+// fused momentum exchange does not keep the 18 indices alive.
+__device__ __forceinline__ void link_masks(const uint32_t (&nb)[kQ], uint32_t& bm, uint32_t& wm)
+{
+    bm = 0u;
+    wm = 0u;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        if (q == 9) continue;
+        bm |= (bounced(nb[q]) ? 1u : 0u) << q;
+        wm |= (nb[q] == kWall ? 1u : 0u) << q;
+    }
+}
+
+template <int q = 0, typename T>
+__device__ __forceinline__ void add_links_mask(double (&acc)[6], const T (&s)[kQ], uint32_t bm, uint32_t wm)
+{
+    if constexpr (q < kQ) {
+        if constexpr (q != 9) add_link<q>(acc, s[q], ((bm >> q) & 1u) != 0, ((wm >> q) & 1u) != 0);
+        add_links_mask<q + 1>(acc, s, bm, wm);
     }
 }
 
@@ -314,6 +338,8 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
     char* const B = (char*)b;
     uint32_t nb[kQ];
     neighbours_rows(g, g.cellp[i], nb);
+    uint32_t bm = 0u, wm = 0u;
+    if constexpr (MEX) link_masks(nb, bm, wm);
     T f[kQ];
     if constexpr (K == kAB) {
         // f_q = src[q][x - c_q], or src[opp q][x] if x - c_q is solid, or the
@@ -328,9 +354,9 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
         T rho, ux, uy, uz;
         collide<T, FORCE>(f, p, rho, ux, uy, uz);
         if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
-        if constexpr (MEX) add_links_nb(acc, f, nb);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(B, pair_of(q), sb), sub_of(q) ? own1 : own0, f[q]);
+        if constexpr (MEX) add_links_mask(acc, f, bm, wm);
     } else {
         // slot of direction d: (d, x + c_d), or (opp d, x) if x + c_d is solid.
         // The odd step reads f_{opp d} from it and writes f*_d into it.
@@ -344,12 +370,14 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
         T rho, ux, uy, uz;
         collide<T, FORCE>(f, p, rho, ux, uy, uz);
         if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
-        if constexpr (MEX) add_links_nb(acc, f, nb);
+        // (with open faces f changes before the stores: sum the links first)
+        if constexpr (MEX && OPEN) add_links_mask(acc, f, bm, wm);
         // beyond an open face, f*_d leaves the box and the own slot (opp d, x)
         // takes the reservoir's population entering along -c_d
         if constexpr (OPEN) open_outflow(f, nb, p);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<false>(pair_block(A, pair_of(q), sb), off[q], f[q]);
+        if constexpr (MEX && !OPEN) add_links_mask(acc, f, bm, wm);
     }
 }
 
@@ -389,6 +417,8 @@ __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const Compac
     char* const A = (char*)a;
     uint32_t nb[kQ];
     neighbours_rows(g, g.cellp[i], nb);
+    uint32_t bm = 0u, wm = 0u;
+    if constexpr (MEX) link_masks(nb, bm, wm);
     const uint32_t bmask = eso_bounce_mask(nb);
     const uint32_t bbase = bmask != 0u ? g.bbase[i] : 0u;
     T* const B = (T*)(A + (uint64_t)kEsoBouncePlane * sb);
@@ -413,13 +443,13 @@ __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const Compac
     T rho, ux, uy, uz;
     collide<T, FORCE>(f, p, rho, ux, uy, uz);
     if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
-    if constexpr (MEX) add_links_nb(acc, f, nb);
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
         *nb_ptr[k] = f[k];                                          // f*_k streams to x + c_k
         st_at<false>(pair_block(A, k, sb), own_off[k], f[opp(k)]);  // f*_opp(k) streams to x - c_k
     }
     st_at<false>(rest, own, f[9]);
+    if constexpr (MEX) add_links_mask(acc, f, bm, wm);
 }
 
 template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false>
@@ -484,14 +514,16 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_mex_kernel(T* __res
         char* const A = (char*)a;
         uint32_t nb[kQ];
         neighbours_rows(g, g.cellp[i], nb);
+        uint32_t bm, wm;
+        link_masks(nb, bm, wm);
         T f[kQ];
 #pragma unroll
         for (int q = 0; q < kQ; ++q)
             f[q] = __builtin_nontemporal_load((const T*)(pair_block(A, pair_of(q), sb) + (sub_of(q) ? own1 : own0)));
         collide<T, FORCE>(f, p);
-        add_links_nb(acc, f, nb);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(A, pair_of(q), sb), sub_of(opp(q)) ? own1 : own0, f[q]);
+        add_links_mask(acc, f, bm, wm);
     }
     block_sum6<kEvenThreads>(acc, mo.partial + 6 * (size_t)blockIdx.x);
 }
