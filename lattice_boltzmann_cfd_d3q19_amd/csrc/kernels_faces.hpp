@@ -132,19 +132,18 @@ __device__ __forceinline__ void zou_he(T (&s)[kQ], uint32_t ent, const FaceRule<
 }
 
 // Neumann: e := shifted equilibrium of the inward cell's moments (s1), or the
-// face's own values when that cell is solid.
+// face's own values when that cell is solid (s1 is then all zeros, so the
+// unused equilibrium stays finite).  Both are formed and one is selected: a
+// branch here leaves part of e in private memory.
 template <typename T>
 __device__ __forceinline__ void neumann_values(T (&e)[kQ], const T (&s1)[kQ], bool solid1, const FaceRule<T>& r,
                                                const Phys<T>& p)
 {
-    if (solid1) {
+    T drho, rho, ux, uy, uz;
+    moments<T, true>(s1, p, drho, rho, ux, uy, uz);
+    shifted_equilibrium(rho, ux, uy, uz, e);
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) e[q] = r.seq[q];
-    } else {
-        T drho, rho, ux, uy, uz;
-        moments<T, true>(s1, p, drho, rho, ux, uy, uz);
-        shifted_equilibrium(rho, ux, uy, uz, e);
-    }
+    for (int q = 0; q < kQ; ++q) e[q] = solid1 ? r.seq[q] : e[q];
 }
 
 // Dense layouts: one work-item per cell of the face, the state maps of the
@@ -187,6 +186,9 @@ __global__ void __launch_bounds__(kBlockThreads) face_kernel(T* __restrict__ a, 
             const uint32_t bits1 = link_bits<true>(g, c1), obits1 = open_bits(g, c1);
 #pragma unroll
             for (int q = 0; q < kQ; ++q) s1[q] = *state_slot<S, L>(a, g.n, c1, bits1, q, obits1);
+        } else {
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) s1[q] = T(0);
         }
         neumann_values(e, s1, solid1, r, p);
 #pragma unroll
@@ -235,6 +237,9 @@ __global__ void __launch_bounds__(kBlockThreads) face_compact_kernel(T* __restri
             neighbours(cg, pp1, nb1);
 #pragma unroll
             for (int q = 0; q < kQ; ++q) f1[q] = *compact_state_slot<S>(a, cg, i1, nb1, q);
+        } else {
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) f1[q] = T(0);
         }
         neumann_values(e, f1, solid1, r, p);
 #pragma unroll
