@@ -58,7 +58,7 @@ constexpr uintptr_t kAlign = 256;
 
 bool compact(const lbm_desc& d) { return d.layout == LBM_LAYOUT_COMPACT; }
 
-uint64_t ncells_of(const lbm_desc& d) { return (uint64_t)d.nx * (uint64_t)d.ny * (uint64_t)d.nz; }
+uint64_t ncells(const lbm_desc& d) { return (uint64_t)d.nx * (uint64_t)d.ny * (uint64_t)d.nz; }
 
 lbm_status validate_desc(const lbm_desc* d)
 {
@@ -83,15 +83,13 @@ lbm_status validate_desc(const lbm_desc* d)
     // block of populations with 32-bit byte offsets
     if (compact(*d) && 4.0 * (double)(d->nx + 2) * (double)(d->ny + 2) * (double)(d->nz + 2) >= 4294967296.0)
         return LBM_ERR_UNSUPPORTED;
-    if (compact(*d) && 2.0 * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)((ncells_of(*d) + 63) / 64 * 64) >=
+    if (compact(*d) && 2.0 * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)((ncells(*d) + 63) / 64 * 64) >=
                            4294967296.0)
         return LBM_ERR_UNSUPPORTED;
     return LBM_OK;
 }
 
 size_t elem_size(const lbm_desc& d) { return d.precision == LBM_F64 ? 8 : 4; }
-
-uint64_t ncells(const lbm_desc& d) { return (uint64_t)d.nx * (uint64_t)d.ny * (uint64_t)d.nz; }
 
 // Population buffer size; the compact layout reserves room for an all-fluid
 // box, and its esoteric pull nine more planes' worth of bounce-back slots.

@@ -579,7 +579,8 @@ struct MomOut {
     T* rho;
     T* u;
     uint64_t n;
-    double* partial;  // fused momentum exchange: six sums per workgroup (MEX instances)
+    double* partial;      // fused momentum exchange: six sums per workgroup (MEX instances)
+    const uint8_t* mask;  // compact layout with output: the solid cells the waves zero (null: none)
 };
 
 template <typename T>

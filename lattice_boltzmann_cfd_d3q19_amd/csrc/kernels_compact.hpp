@@ -321,6 +321,27 @@ __device__ __forceinline__ char* pair_block(char* base, int k, uint32_t plane_by
     return base + (uint64_t)(2 * k) * plane_bytes;
 }
 
+// Fields output of a compact step: the solid cells get zeros from the wave
+// whose fluid cells surround them.  The wave of fluid cells i0 .. i0 + 63
+// covers the cell range [r0, r1): r0 = its first cell (0 for the first
+// wave), r1 = the next wave's first cell (N after the last fluid cell); the
+// cells of the range that are not the wave's own are solid.  Writing them
+// right after the fluid cells completes each line of the fields within one
+// wave, so L2 merges it before write-back (a separate pass leaves every line
+// that mixes fluid and solid cells to be written in two parts).  Called by
+// every work-item of a wave with i0 < nf, blocks one-dimensional.
+template <typename T>
+__device__ __forceinline__ void zero_solid_range(const MomOut<T>& mo, const uint32_t* __restrict__ cellid,
+                                                 uint32_t nf, uint32_t i0)
+{
+    if (mo.mask == nullptr) return;
+    const uint64_t lane = threadIdx.x & 63u;
+    const uint64_t r0 = i0 == 0 ? 0 : cellid[i0];
+    const uint64_t r1 = i0 + 64u < nf ? cellid[i0 + 64u] : mo.n;
+    for (uint64_t c = r0 + lane; c < r1; c += 64)
+        if (mo.mask[c] != 0) write_moments(mo, c, T(0), T(0), T(0), T(0));
+}
+
 // Gather step over the fluid cells, one work-item per fluid cell: the
 // two-lattice fused pull (K = kAB, a = source, b = destination) or the odd
 // step of the in-place pattern (K = kAAOdd, a = the lattice).  OPEN: some
@@ -392,7 +413,12 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
     const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
     const uint32_t i = wg * kGatherThreads + threadIdx.x;
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    if constexpr (!MEX) {
+    if constexpr (OUT) {
+        static_assert(!MEX, "no fields output in a momentum-exchange step");
+        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, true, false>(a, b, g, p, mo, i, acc);
+        const uint32_t i0 = i - (threadIdx.x & 63u);
+        if (i0 < g.nf) zero_solid_range(mo, g.cellid, g.nf, i0);
+    } else if constexpr (!MEX) {
         if (i >= g.nf) return;
         step_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, b, g, p, mo, i, acc);
     } else {
@@ -460,7 +486,12 @@ __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restri
     const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
     const uint32_t i = wg * kGatherThreads + threadIdx.x;
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    if constexpr (!MEX) {
+    if constexpr (OUT) {
+        static_assert(!MEX, "no fields output in a momentum-exchange step");
+        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, true, false>(a, g, p, mo, i, acc);
+        const uint32_t i0 = i - (threadIdx.x & 63u);
+        if (i0 < g.nf) zero_solid_range(mo, g.cellid, g.nf, i0);
+    } else if constexpr (!MEX) {
         if (i >= g.nf) return;
         eso_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, mo, i, acc);
     } else {
@@ -496,6 +527,11 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_kernel(T* __restric
         if (i < nf) write_moments(mo, cellid[i], rho, ux, uy, uz);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(A, pair_of(q), sb), sub_of(opp(q)) ? own1 : own0, f[q]);
+    if constexpr (OUT) {
+        // s is a multiple of 64: the whole wave is still here
+        const uint32_t i0 = i - (threadIdx.x & 63u);
+        if (i0 < nf) zero_solid_range(mo, cellid, nf, i0);
+    }
 }
 
 // The even step with the momentum exchange of that step: the same purely
@@ -528,13 +564,13 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_mex_kernel(T* __res
     block_sum6<kEvenThreads>(acc, mo.partial + 6 * (size_t)blockIdx.x);
 }
 
-// rho and u := 0 on the solid cells (the fields of a compact step; the step
-// itself writes the fluid cells).
+// rho and u := 0 on every cell: the fields of a step on a box without fluid
+// cells (no step kernel runs there).
 template <typename T>
-__global__ void __launch_bounds__(kBlockThreads) zero_moments_kernel(MomOut<T> mo, const uint8_t* __restrict__ mask)
+__global__ void __launch_bounds__(kBlockThreads) zero_fields_kernel(MomOut<T> mo)
 {
     const uint64_t id = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
-    if (id < mo.n && mask[id] != 0) write_moments(mo, id, T(0), T(0), T(0), T(0));
+    if (id < mo.n) write_moments(mo, id, T(0), T(0), T(0), T(0));
 }
 
 // State transfers between canonical dense arrays ([19][N], [N], [3][N]) and

@@ -167,7 +167,7 @@ template <typename T>
 hipError_t launch_step(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp, T* rho_out,
                        T* u_out, hipStream_t st)
 {
-    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz, nullptr};
+    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz, nullptr, nullptr};
     return launch_step_mo<T>(layout, kind, a, b, lg, lp, mo, st);
 }
 
@@ -332,22 +332,24 @@ hipError_t launch_step_compact_mo(int kind, T* a, T* b, const LaunchGeom& lg, co
 {
     const CompactGeom g = compact_geom(lg, t);
     const Phys<T> p = make_phys<T>(lp);
-    if (mo.rho != nullptr && lg.mask != nullptr) {
-        // solid cells get zeros here; the step writes the fluid cells
-        const uint64_t blocks = (mo.n + kBlockThreads - 1) / kBlockThreads;
-        MomOut<T> m = mo;
-        const uint8_t* mask = lg.mask;
-        void* args[] = {&m, &mask};
-        const hipError_t e = hipLaunchKernel((const void*)&zero_moments_kernel<T>, dim3((uint32_t)blocks),
-                                             dim3(kBlockThreads), args, 0, st);
-        if (e != hipSuccess) return e;
+    MomOut<T> m = mo;
+    if (m.rho != nullptr) {
+        // the step's waves write the solid cells between their fluid cells;
+        // a box without fluid cells runs no step, only this fill
+        m.mask = lg.mask;
+        if (g.nf == 0) {
+            const uint64_t blocks = (m.n + kBlockThreads - 1) / kBlockThreads;
+            void* args[] = {&m};
+            return hipLaunchKernel((const void*)&zero_fields_kernel<T>, dim3((uint32_t)blocks), dim3(kBlockThreads),
+                                   args, 0, st);
+        }
     }
     switch (kind) {
-    case kAB: return launch_step_compact_k<T, kAB>(a, b, g, p, mo, lp.has_force, st);
-    case kAAEven: return launch_step_compact_k<T, kAAEven>(a, b, g, p, mo, lp.has_force, st);
-    case kAAOdd: return launch_step_compact_k<T, kAAOdd>(a, b, g, p, mo, lp.has_force, st);
-    case kEsoEven: return launch_step_compact_k<T, kEsoEven>(a, b, g, p, mo, lp.has_force, st);
-    case kEsoOdd: return launch_step_compact_k<T, kEsoOdd>(a, b, g, p, mo, lp.has_force, st);
+    case kAB: return launch_step_compact_k<T, kAB>(a, b, g, p, m, lp.has_force, st);
+    case kAAEven: return launch_step_compact_k<T, kAAEven>(a, b, g, p, m, lp.has_force, st);
+    case kAAOdd: return launch_step_compact_k<T, kAAOdd>(a, b, g, p, m, lp.has_force, st);
+    case kEsoEven: return launch_step_compact_k<T, kEsoEven>(a, b, g, p, m, lp.has_force, st);
+    case kEsoOdd: return launch_step_compact_k<T, kEsoOdd>(a, b, g, p, m, lp.has_force, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -356,7 +358,7 @@ template <typename T>
 hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& lg, const CompactTables& t,
                                const LaunchPhys& lp, T* rho_out, T* u_out, hipStream_t st)
 {
-    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz, nullptr};
+    const MomOut<T> mo{rho_out, u_out, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz, nullptr, nullptr};
     return launch_step_compact_mo<T>(kind, a, b, lg, t, lp, mo, st);
 }
 
@@ -582,7 +584,7 @@ template <typename T>
 hipError_t launch_step_mex(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const CompactTables* t,
                            const LaunchPhys& lp, double* partial, double* force, hipStream_t st)
 {
-    const MomOut<T> mo{nullptr, nullptr, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz, partial};
+    const MomOut<T> mo{nullptr, nullptr, (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz, partial, nullptr};
     uint32_t rows;
     hipError_t e;
     if (t != nullptr) {
