@@ -374,10 +374,10 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
         if constexpr (OPEN) apply_open_nb(f, nb, p);
         T rho, ux, uy, uz;
         collide<T, FORCE>(f, p, rho, ux, uy, uz);
-        if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(B, pair_of(q), sb), sub_of(q) ? own1 : own0, f[q]);
         if constexpr (MEX) add_links_mask(acc, f, bm, wm);
+        if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
     } else {
         // slot of direction d: (d, x + c_d), or (opp d, x) if x + c_d is solid.
         // The odd step reads f_{opp d} from it and writes f*_d into it.
@@ -468,13 +468,13 @@ __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const Compac
     if constexpr (OPEN) apply_open_nb(f, nb, p);
     T rho, ux, uy, uz;
     collide<T, FORCE>(f, p, rho, ux, uy, uz);
-    if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
         *nb_ptr[k] = f[k];                                          // f*_k streams to x + c_k
         st_at<false>(pair_block(A, k, sb), own_off[k], f[opp(k)]);  // f*_opp(k) streams to x - c_k
     }
     st_at<false>(rest, own, f[9]);
+    if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
     if constexpr (MEX) add_links_mask(acc, f, bm, wm);
 }
 
@@ -523,11 +523,10 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_kernel(T* __restric
         f[q] = __builtin_nontemporal_load((const T*)(pair_block(A, pair_of(q), sb) + (sub_of(q) ? own1 : own0)));
     T rho, ux, uy, uz;
     collide<T, FORCE>(f, p, rho, ux, uy, uz);
-    if constexpr (OUT)
-        if (i < nf) write_moments(mo, cellid[i], rho, ux, uy, uz);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(A, pair_of(q), sb), sub_of(opp(q)) ? own1 : own0, f[q]);
     if constexpr (OUT) {
+        if (i < nf) write_moments(mo, cellid[i], rho, ux, uy, uz);
         // s is a multiple of 64: the whole wave is still here
         const uint32_t i0 = i - (threadIdx.x & 63u);
         if (i0 < nf) zero_solid_range(mo, cellid, nf, i0);
