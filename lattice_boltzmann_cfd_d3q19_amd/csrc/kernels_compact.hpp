@@ -523,10 +523,13 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_kernel(T* __restric
         f[q] = __builtin_nontemporal_load((const T*)(pair_block(A, pair_of(q), sb) + (sub_of(q) ? own1 : own0)));
     T rho, ux, uy, uz;
     collide<T, FORCE>(f, p, rho, ux, uy, uz);
+    // (the fields before the populations: 4% faster than after them, though
+    // that holds more registers)
+    if constexpr (OUT)
+        if (i < nf) write_moments(mo, cellid[i], rho, ux, uy, uz);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(A, pair_of(q), sb), sub_of(opp(q)) ? own1 : own0, f[q]);
     if constexpr (OUT) {
-        if (i < nf) write_moments(mo, cellid[i], rho, ux, uy, uz);
         // s is a multiple of 64: the whole wave is still here
         const uint32_t i0 = i - (threadIdx.x & 63u);
         if (i0 < nf) zero_solid_range(mo, cellid, nf, i0);
