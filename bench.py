@@ -157,7 +157,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="porous256")
-    ap.add_argument("--scheme", default="aa", choices=["aa", "ab", "eso"])
+    ap.add_argument("--scheme", default="aa", choices=["aa", "ab", "eso", "twist"])
     ap.add_argument("--layout", default="compact", choices=["stream", "bundle", "collision", "compact"])
     ap.add_argument("--per-kernel-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -212,6 +212,8 @@ def main():
         names = ["aa_even", "aa_odd"]
     elif args.scheme == "eso":
         names = ["eso_even", "eso_odd"]
+    elif args.scheme == "twist":
+        names = ["twist_even", "twist_odd"]
     else:
         names = ["ab", "ab"]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

@@ -31,6 +31,21 @@
  *                  their value in slots no other link uses (a solid
  *                  neighbour's, the wrapped cell's beyond a face; in the
  *                  compact layout a packed region after the 19 planes).
+ *   LBM_SCHEME_ESOTWIST  one lattice, in place, the esoteric twist that
+ *                  PortLBM (section 3.3) names with AA and the esoteric pull
+ *                  (Geier and Schoenherr, Computation 5, 19, 2017): with
+ *                  c+ = max(c_q, 0) per axis, f_q(x) lives at x - c+ (the cell
+ *                  or one of the six behind it along -x, -y, -z and their face
+ *                  diagonals) in plane q at even t, opposite(q) at odd t; a step
+ *                  writes the collided f_q where it read f_opposite(q), or into
+ *                  the other plane there when the link bounces back.  Dense
+ *                  layouts keep one halo layer below each low face for the
+ *                  values behind a wall: their buffers hold (nx+1)(ny+1)(nz+1)
+ *                  cells per plane (lbm_buffer_bytes).  The compact layout
+ *                  gives each solid or halo cell behind a fluid cell a ghost
+ *                  slot after the fluid cells (its buffer has room for the
+ *                  same (nx+1)(ny+1)(nz+1) cells; its workspace also holds
+ *                  the stored index of every padded cell).
  * Population layouts (PortLBM section 3.2, Fig. 2):
  *   LBM_LAYOUT_STREAM     SoA: all cells of direction 0, then direction 1, ...
  *   LBM_LAYOUT_BUNDLE     SoAoS: directions grouped in bundles of equal
@@ -101,6 +116,7 @@ typedef int32_t lbm_status;
 #define LBM_SCHEME_AB 0
 #define LBM_SCHEME_AA 1
 #define LBM_SCHEME_ESOPULL 2
+#define LBM_SCHEME_ESOTWIST 3
 
 typedef struct lbm_desc {
     int64_t nx, ny, nz;  /* box size in cells, each >= 1 */

@@ -21,7 +21,7 @@ LBM_ERR_HIP = -5
 
 LBM_F32, LBM_F64 = 0, 1
 LBM_LAYOUT_STREAM, LBM_LAYOUT_BUNDLE, LBM_LAYOUT_COLLISION, LBM_LAYOUT_COMPACT = 0, 1, 2, 3
-LBM_SCHEME_AB, LBM_SCHEME_AA, LBM_SCHEME_ESOPULL = 0, 1, 2
+LBM_SCHEME_AB, LBM_SCHEME_AA, LBM_SCHEME_ESOPULL, LBM_SCHEME_ESOTWIST = 0, 1, 2, 3
 
 EXPORTED = ["lbm_buffer_bytes", "lbm_workspace_bytes", "lbm_create", "lbm_set_workspace", "lbm_set_geometry", "lbm_init_equilibrium", "lbm_step",
             "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_save_state",

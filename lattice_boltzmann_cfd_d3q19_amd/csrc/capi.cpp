@@ -60,6 +60,17 @@ bool compact(const lbm_desc& d) { return d.layout == LBM_LAYOUT_COMPACT; }
 
 uint64_t ncells(const lbm_desc& d) { return (uint64_t)d.nx * (uint64_t)d.ny * (uint64_t)d.nz; }
 
+// Stored cells a compact buffer has room for: every cell of the box, and for
+// the esoteric twist also the halo below the low faces (its ghost cells lie
+// among the box's solid cells and in that halo); rounded up to 64.
+uint64_t compact_capacity(const lbm_desc& d)
+{
+    const uint64_t cells = d.scheme == LBM_SCHEME_ESOTWIST
+                               ? (uint64_t)(d.nx + 1) * (uint64_t)(d.ny + 1) * (uint64_t)(d.nz + 1)
+                               : ncells(d);
+    return (cells + 63) / 64 * 64;
+}
+
 lbm_status validate_desc(const lbm_desc* d)
 {
     if (d == nullptr) return LBM_ERR_INVALID_ARGUMENT;
@@ -68,7 +79,8 @@ lbm_status validate_desc(const lbm_desc* d)
     if (d->layout != LBM_LAYOUT_STREAM && d->layout != LBM_LAYOUT_BUNDLE && d->layout != LBM_LAYOUT_COLLISION &&
         d->layout != LBM_LAYOUT_COMPACT)
         return LBM_ERR_INVALID_ARGUMENT;
-    if (d->scheme != LBM_SCHEME_AB && d->scheme != LBM_SCHEME_AA && d->scheme != LBM_SCHEME_ESOPULL)
+    if (d->scheme != LBM_SCHEME_AB && d->scheme != LBM_SCHEME_AA && d->scheme != LBM_SCHEME_ESOPULL &&
+        d->scheme != LBM_SCHEME_ESOTWIST)
         return LBM_ERR_INVALID_ARGUMENT;
     if (d->reserved != 0) return LBM_ERR_INVALID_ARGUMENT;
     if (std::isnan(d->tau) || !(d->tau > 0.5)) return LBM_ERR_INVALID_ARGUMENT;
@@ -79,12 +91,16 @@ lbm_status validate_desc(const lbm_desc* d)
     const double n = (double)d->nx * (double)d->ny * (double)d->nz;
     if (d->nx > INT32_MAX || d->ny > INT32_MAX || d->nz > INT32_MAX || n >= 2147483648.0)
         return LBM_ERR_UNSUPPORTED;
+    // the dense esoteric twist stores a halo layer below each low face and
+    // addresses its (nx+1)(ny+1)(nz+1) cells with 32-bit indices
+    if (!compact(*d) && d->scheme == LBM_SCHEME_ESOTWIST &&
+        (double)(d->nx + 1) * (double)(d->ny + 1) * (double)(d->nz + 1) >= 2147483648.0)
+        return LBM_ERR_UNSUPPORTED;
     // the compact kernels address the padded index table and each two-plane
     // block of populations with 32-bit byte offsets
     if (compact(*d) && 4.0 * (double)(d->nx + 2) * (double)(d->ny + 2) * (double)(d->nz + 2) >= 4294967296.0)
         return LBM_ERR_UNSUPPORTED;
-    if (compact(*d) && 2.0 * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)((ncells(*d) + 63) / 64 * 64) >=
-                           4294967296.0)
+    if (compact(*d) && 2.0 * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)compact_capacity(*d) >= 4294967296.0)
         return LBM_ERR_UNSUPPORTED;
     return LBM_OK;
 }
@@ -95,7 +111,9 @@ size_t elem_size(const lbm_desc& d) { return d.precision == LBM_F64 ? 8 : 4; }
 // box, and its esoteric pull nine more planes' worth of bounce-back slots.
 size_t buffer_bytes(const lbm_desc& d)
 {
-    const uint64_t cells = compact(d) ? (ncells(d) + 63) / 64 * 64 : ncells(d);
+    uint64_t cells = compact(d) ? compact_capacity(d) : ncells(d);
+    if (!compact(d) && d.scheme == LBM_SCHEME_ESOTWIST)
+        cells = (uint64_t)(d.nx + 1) * (uint64_t)(d.ny + 1) * (uint64_t)(d.nz + 1);
     const uint64_t planes = compact(d) && d.scheme == LBM_SCHEME_ESOPULL ? lbm::kEsoPlanes : lbm::kQ;
     return (size_t)planes * cells * elem_size(d);
 }
@@ -145,6 +163,7 @@ int state_kind(const lbm_sim* s)
 {
     if (s->d.scheme == LBM_SCHEME_AB) return lbm::kAB;
     if (s->d.scheme == LBM_SCHEME_ESOPULL) return (s->t % 2 == 0) ? lbm::kEsoEven : lbm::kEsoOdd;
+    if (s->d.scheme == LBM_SCHEME_ESOTWIST) return (s->t % 2 == 0) ? lbm::kTwEven : lbm::kTwOdd;
     return (s->t % 2 == 0) ? lbm::kAAEven : lbm::kAAOdd;
 }
 
@@ -203,8 +222,8 @@ lbm_status apply_face_rules(lbm_sim* s)
 lbm_status build_compact(lbm_sim* s)
 {
     if (s->ws == nullptr) return LBM_ERR_BAD_STATE;
-    const bool eso = s->d.scheme == LBM_SCHEME_ESOPULL;
-    const lbm::CompactLayoutBytes lay = lbm::compact_workspace_layout(s->d.nx, s->d.ny, s->d.nz, eso);
+    const bool eso = s->d.scheme == LBM_SCHEME_ESOPULL, twist = s->d.scheme == LBM_SCHEME_ESOTWIST;
+    const lbm::CompactLayoutBytes lay = lbm::compact_workspace_layout(s->d.nx, s->d.ny, s->d.nz, eso, twist);
     char* base = (char*)s->ws;
     lbm::CompactTables& t = s->tables;
     t.header = (uint32_t*)(base + lay.header);
@@ -213,6 +232,8 @@ lbm_status build_compact(lbm_sim* s)
     t.cellp = (uint32_t*)(base + lay.cellp);
     t.cellid = (uint32_t*)(base + lay.cellid);
     t.bbase = eso ? (uint32_t*)(base + lay.bbase) : nullptr;
+    t.tidx = twist ? (uint32_t*)(base + lay.tidx) : nullptr;
+    t.grows = twist ? (uint32_t*)(base + lay.grows) : nullptr;
     t.nf = 0;
     t.stride = 0;
     hipError_t e = lbm::launch_compact_build(geom_of(s), t, s->stream);
@@ -223,6 +244,15 @@ lbm_status build_compact(lbm_sim* s)
     if (e != hipSuccess) return hip_status(s, e);
     t.nf = nf;
     t.stride = ((uint64_t)nf + 63) / 64 * 64;
+    if (twist) {
+        // ghost cells after the fluid ones: the stride covers both
+        e = lbm::launch_compact_twist(geom_of(s), t, s->stream);
+        uint32_t ng = 0;
+        if (e == hipSuccess) e = hipMemcpyAsync(&ng, t.header + 2, sizeof(ng), hipMemcpyDeviceToHost, s->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(s->stream);
+        if (e != hipSuccess) return hip_status(s, e);
+        t.stride = ((uint64_t)nf + ng + 63) / 64 * 64;
+    }
     return hip_status(s, lbm::launch_compact_bounce(geom_of(s), t, s->stream));
 }
 
@@ -246,7 +276,8 @@ lbm_status lbm_workspace_bytes(const lbm_desc* desc, size_t* bytes)
     if (v != LBM_OK) return v;
     if (bytes == nullptr) return LBM_ERR_INVALID_ARGUMENT;
     *bytes = compact(*desc) ? lbm::compact_workspace_layout(desc->nx, desc->ny, desc->nz,
-                                                             desc->scheme == LBM_SCHEME_ESOPULL)
+                                                             desc->scheme == LBM_SCHEME_ESOPULL,
+                                                             desc->scheme == LBM_SCHEME_ESOTWIST)
                                   .total
                             : 0;
     return LBM_OK;

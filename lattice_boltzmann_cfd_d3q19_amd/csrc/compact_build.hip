@@ -157,7 +157,116 @@ __global__ void __launch_bounds__(kBlockThreads) compact_bounce_counts(const uin
     count[i] = n;
 }
 
-CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz, bool bounce)
+// ---------------------------------------------- esoteric-twist ghosts
+//
+// The twist reads and writes x - o for the six offsets o of the directions
+// with a positive component (x, y, z, and the face diagonals xy, xz, yz).
+// A padded cell that is not fluid gets storage ("ghost") if one of those
+// offsets leads from it to a fluid cell; candidates are the interior cells
+// and the halo below a low face that is not periodic (a periodic low halo is
+// the image of a cell on the other side, which is a candidate itself).
+
+// padded coordinate v of an axis with n cells is a candidate location
+__device__ __forceinline__ bool twist_candidate(uint32_t v, uint32_t n, uint32_t per)
+{
+    return (v >= 1u && v <= n) || (v == 0u && per == 0u);
+}
+
+__device__ __forceinline__ bool twist_ghost(const uint32_t* __restrict__ idxp, uint32_t p, uint32_t px, uint32_t pxy)
+{
+    if (!no_fluid(idxp[p])) return false;
+    const uint32_t offs[6] = {1u, px, pxy, 1u + px, 1u + pxy, px + pxy};
+    bool g = false;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) g = g || !no_fluid(idxp[p + offs[k]]);
+    return g;
+}
+
+// Ghost cells per padded row r = py + (ny + 2) pz; one workgroup per row.
+__global__ void __launch_bounds__(kBlockThreads) twist_count_rows(const uint32_t* __restrict__ idxp, uint32_t nx,
+                                                                  uint32_t ny, uint32_t nz, uint32_t per_x,
+                                                                  uint32_t per_y, uint32_t per_z,
+                                                                  uint32_t* __restrict__ row_count)
+{
+    __shared__ uint32_t part[kBlockThreads / 64];
+    const uint32_t r = blockIdx.x;
+    const uint32_t py = r % (ny + 2u), pz = r / (ny + 2u);
+    const uint32_t px = nx + 2u, pxy = px * (ny + 2u);
+    const bool row_ok = twist_candidate(py, ny, per_y) && twist_candidate(pz, nz, per_z);
+    uint32_t cnt = 0;
+    if (row_ok)
+        for (uint32_t x = threadIdx.x; x < px; x += kBlockThreads)
+            cnt += (twist_candidate(x, nx, per_x) && twist_ghost(idxp, x + px * py + pxy * pz, px, pxy)) ? 1u : 0u;
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_down(cnt, o, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x / 64] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < kBlockThreads / 64; ++w) t += part[w];
+        row_count[r] = t;
+    }
+}
+
+// tidx of every cell of padded row r: the fluid index, nf + the ghost's rank
+// (in cell order), or kInvalid.  Periodic halos are filled afterwards.
+__global__ void __launch_bounds__(kBlockThreads) twist_fill_rows(const uint32_t* __restrict__ idxp, uint32_t nx,
+                                                                 uint32_t ny, uint32_t nz, uint32_t per_x,
+                                                                 uint32_t per_y, uint32_t per_z, uint32_t nf,
+                                                                 const uint32_t* __restrict__ row_start,
+                                                                 uint32_t* __restrict__ tidx)
+{
+    __shared__ uint32_t wave_tot[kBlockThreads / 64];
+    const uint32_t r = blockIdx.x;
+    const uint32_t py = r % (ny + 2u), pz = r / (ny + 2u);
+    const uint32_t px = nx + 2u, pxy = px * (ny + 2u);
+    const bool row_ok = twist_candidate(py, ny, per_y) && twist_candidate(pz, nz, per_z);
+    const bool row_in = py >= 1u && py <= ny && pz >= 1u && pz <= nz;
+    uint32_t base = nf + row_start[r];
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x / 64;
+    for (uint32_t x0 = 0; x0 < px; x0 += kBlockThreads) {
+        const uint32_t x = x0 + threadIdx.x;
+        const bool inside = x < px;
+        const uint32_t p = x + px * py + pxy * pz;
+        const bool ghost = inside && row_ok && twist_candidate(x, nx, per_x) && twist_ghost(idxp, p, px, pxy);
+        const uint64_t bal = __ballot(ghost);
+        const uint32_t below = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wave_tot[wave] = __popcll(bal);
+        __syncthreads();
+        uint32_t before = 0, all = 0;
+        for (uint32_t w = 0; w < kBlockThreads / 64; ++w) {
+            before += w < wave ? wave_tot[w] : 0u;
+            all += wave_tot[w];
+        }
+        if (inside) {
+            const bool fluid = row_in && x >= 1u && x <= nx && !no_fluid(idxp[p]);
+            tidx[p] = ghost ? base + before + below : fluid ? idxp[p] : kInvalid;
+        }
+        base += all;
+        __syncthreads();
+    }
+}
+
+// Periodic halos of tidx: the entry of the cell with every periodic halo
+// coordinate wrapped (the others kept), which is never such a halo itself.
+__global__ void __launch_bounds__(kBlockThreads) twist_fill_halo(uint32_t nx, uint32_t ny, uint32_t nz, uint32_t per_x,
+                                                                 uint32_t per_y, uint32_t per_z, uint64_t npad,
+                                                                 uint32_t* __restrict__ tidx)
+{
+    const uint64_t pp = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+    if (pp >= npad) return;
+    const uint32_t px = nx + 2u, pxy = px * (ny + 2u);
+    const uint32_t p = (uint32_t)pp;
+    uint32_t x = p % px, y = (p / px) % (ny + 2u), z = p / pxy;
+    const bool hx = per_x && (x == 0u || x == nx + 1u), hy = per_y && (y == 0u || y == ny + 1u),
+               hz = per_z && (z == 0u || z == nz + 1u);
+    if (!hx && !hy && !hz) return;
+    if (hx) x = x == 0u ? nx : 1u;
+    if (hy) y = y == 0u ? ny : 1u;
+    if (hz) z = z == 0u ? nz : 1u;
+    tidx[p] = tidx[x + px * y + pxy * z];
+}
+
+CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz, bool bounce, bool twist)
 {
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     CompactLayoutBytes b{};
@@ -170,7 +279,9 @@ CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz, 
     b.cellp = b.idxp + up(4 * npad);
     b.cellid = b.cellp + up(4 * n64);
     b.bbase = b.cellid + up(4 * n64);
-    b.total = b.bbase + (bounce ? up(4 * n64) : 0);
+    b.tidx = b.bbase + (bounce ? up(4 * n64) : 0);
+    b.grows = b.tidx + (twist ? up(4 * npad) : 0);
+    b.total = b.grows + (twist ? up(4 * (size_t)(ny + 2) * (size_t)(nz + 2)) : 0);
     return b;
 }
 
@@ -188,6 +299,24 @@ hipError_t launch_compact_build(const LaunchGeom& lg, const CompactTables& t, hi
                        dim3(kBlockThreads), 0, st, nx, ny, nz, (uint32_t)(lg.periodic[0] != 0),
                        (uint32_t)(lg.periodic[1] != 0), (uint32_t)(lg.periodic[2] != 0), lg.open, px, pxy, npad,
                        t.idxp);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact_twist(const LaunchGeom& lg, const CompactTables& t, hipStream_t st)
+{
+    if (t.tidx == nullptr) return hipSuccess;
+    const uint32_t nx = (uint32_t)lg.nx, ny = (uint32_t)lg.ny, nz = (uint32_t)lg.nz;
+    const uint32_t prow = (ny + 2) * (nz + 2);
+    const uint64_t npad = (uint64_t)(nx + 2) * (ny + 2) * (nz + 2);
+    const uint32_t per_x = lg.periodic[0] != 0, per_y = lg.periodic[1] != 0, per_z = lg.periodic[2] != 0;
+    hipLaunchKernelGGL(twist_count_rows, dim3(prow), dim3(kBlockThreads), 0, st, (const uint32_t*)t.idxp, nx, ny, nz,
+                       per_x, per_y, per_z, t.grows);
+    // ghost count into header[2]
+    hipLaunchKernelGGL(compact_scan_rows, dim3(1), dim3(1024), 0, st, t.grows, prow, t.header + 2);
+    hipLaunchKernelGGL(twist_fill_rows, dim3(prow), dim3(kBlockThreads), 0, st, (const uint32_t*)t.idxp, nx, ny, nz,
+                       per_x, per_y, per_z, t.nf, (const uint32_t*)t.grows, t.tidx);
+    hipLaunchKernelGGL(twist_fill_halo, dim3((uint32_t)((npad + kBlockThreads - 1) / kBlockThreads)),
+                       dim3(kBlockThreads), 0, st, nx, ny, nz, per_x, per_y, per_z, npad, t.tidx);
     return hipGetLastError();
 }
 

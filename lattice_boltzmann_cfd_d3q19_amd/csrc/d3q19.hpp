@@ -59,8 +59,16 @@ enum Layout : int { kStream = 0, kBundle = 1, kCollision = 2 };
 //            directions is read from the own cell and from the neighbour along
 //            one of them and written back to the same two slots, whose roles
 //            swap from one step to the next (even / odd step).
-enum Kind : int { kAB = 0, kAAEven = 1, kAAOdd = 2, kEsoEven = 3, kEsoOdd = 4 };
+//   kTwEven, kTwOdd  one lattice, esoteric twist: each population is read
+//            from the cell itself or one of the six cells behind it along
+//            -x, -y, -z and the face diagonals between them, and written to
+//            the slot its opposite was read from, with the planes of a pair
+//            swapping roles from one step to the next.
+enum Kind : int { kAB = 0, kAAEven = 1, kAAOdd = 2, kEsoEven = 3, kEsoOdd = 4, kTwEven = 5, kTwOdd = 6 };
 
 constexpr bool is_eso(int k) { return k == kEsoEven || k == kEsoOdd; }
+constexpr bool is_twist(int k) { return k == kTwEven || k == kTwOdd; }
+// the stored state uses slots of solid (and, for the twist, halo) cells
+constexpr bool solid_slots_live(int k) { return is_eso(k) || is_twist(k); }
 
 }  // namespace lbm

@@ -730,10 +730,52 @@ __device__ __forceinline__ uint64_t eso_off(uint64_t n, const Cell& c, uint32_t 
     }
 }
 
+// Esoteric twist (kTwEven / kTwOdd, parity P).  With c+ = max(c_q, 0) per
+// axis, f_q(x) lives at the location x - c+ (the cell itself or one of the
+// six cells behind it along -x, -y, -z and the face diagonals between them)
+// in plane q (P = 0) or opp(q) (P = 1).  A step reads every f_q there and
+// writes f*_q where it read f_opp(q), i.e. at x + c- (c- = min(c_q, 0)) in
+// plane opp(q) (P = 0) or q (P = 1): the next step finds it there as the
+// population that reached x + c_q.  A bounced-back f*_q goes to the other
+// plane of that location instead, where x itself finds f_opp(q) next.  The
+// dense storage of this scheme has one extra layer of cells below the low
+// face of each axis, (nx+1)(ny+1)(nz+1) cells per plane, padded coordinate =
+// coordinate + 1: behind a low face that is not periodic the location is
+// such a halo cell (it holds a bounced or reservoir value of the cell next
+// to it), on a periodic axis it wraps.
+__device__ __forceinline__ uint64_t twist_cells(const Geom& g)
+{
+    return (uint64_t)(g.nx + 1) * (uint64_t)(g.ny + 1) * (uint64_t)(g.nz + 1);
+}
+
+// padded index of x - (ox, oy, oz), o in {0, 1}^3
+__device__ __forceinline__ uint32_t twist_loc(const Geom& g, const Cell& c, int ox, int oy, int oz)
+{
+    auto back = [](uint32_t v, int o, bool face, uint32_t n) -> uint32_t {
+        // padded coordinate of v - o: v + 1 - o, or behind the low face the
+        // halo (0) if that face is not periodic, else the wrapped cell (n)
+        return o == 0 ? v + 1u : v > 0u ? v : face ? 0u : n;
+    };
+    const uint32_t px = back(c.x, ox, c.wall[0][0] || c.open[0][0], g.nx);
+    const uint32_t py = back(c.y, oy, c.wall[1][0] || c.open[1][0], g.ny);
+    const uint32_t pz = back(c.z, oz, c.wall[2][0] || c.open[2][0], g.nz);
+    return px + (g.nx + 1u) * (py + (g.ny + 1u) * pz);
+}
+
+// element offset of f_q(x) in a twist state of parity P
+template <int P, int L>
+__device__ __forceinline__ uint64_t twist_off(const Geom& g, const Cell& c, int q)
+{
+    const int pl = P == 0 ? q : opp(q);
+    return slot_off<L>(twist_cells(g), pl, twist_loc(g, c, kCx[q] > 0, kCy[q] > 0, kCz[q] > 0));
+}
+
 template <int S, int L, typename T>
-__device__ __forceinline__ T* state_slot(T* buf, uint64_t n, const Cell& c, uint32_t bits, int q,
+__device__ __forceinline__ T* state_slot(T* buf, const Geom& g, const Cell& c, uint32_t bits, int q,
                                          uint32_t obits = 0u)
 {
+    const uint64_t n = g.n;
+    if constexpr (is_twist(S)) return buf + twist_off<S == kTwOdd ? 1 : 0, L>(g, c, q);
     if constexpr (is_eso(S)) return buf + eso_off<S, L>(n, c, bits, obits, q);
     const bool bb = (bits >> q) & 1u;
     const uint32_t up = nbr(c, -kCx[q], -kCy[q], -kCz[q]);
@@ -765,11 +807,13 @@ __device__ __forceinline__ void step_cell(T* __restrict__ a, T* __restrict__ b, 
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
         if constexpr (K == kAB) {
-            f[q] = ld_pop(state_slot<kAB, L>(a, n, c, bits, q));
+            f[q] = ld_pop(state_slot<kAB, L>(a, g, c, bits, q));
         } else if constexpr (K == kAAEven) {
             f[q] = ld_pop_own<BND == 0 && L != kCollision>(slot<L>(a, n, q, c.id));
         } else if constexpr (K == kAAOdd) {
-            f[q] = ld_pop(state_slot<kAAOdd, L>(a, n, c, bits, q));
+            f[q] = ld_pop(state_slot<kAAOdd, L>(a, g, c, bits, q));
+        } else if constexpr (is_twist(K)) {
+            f[q] = ld_pop(a + twist_off<K == kTwOdd ? 1 : 0, L>(g, c, q));
         } else {
             f[q] = ld_pop(a + eso_off<K, L>(n, c, bits, obits, q));
         }
@@ -800,6 +844,12 @@ __device__ __forceinline__ void step_cell(T* __restrict__ a, T* __restrict__ b, 
         } else if constexpr (is_eso(K)) {
             // into the slot f_opp(q) was read from
             st_pop(a + eso_off<K, L>(n, c, bits, obits, opp(q)), f[q]);
+        } else if constexpr (is_twist(K)) {
+            // where f_opp(q) was read from; bounced back (x + c_q solid or
+            // beyond a wall: the upstream bit of opp q), the other plane there
+            constexpr int P = K == kTwOdd ? 1 : 0;
+            const uint64_t normal = twist_off<P, L>(g, c, opp(q)), back = twist_off<1 - P, L>(g, c, opp(q));
+            st_pop(a + (((bits >> opp(q)) & 1u) ? back : normal), f[q]);
         } else {
             // toward x + c_q, or straight back into (opp q, x) if that cell is
             // solid or beyond a wall (its upstream bit for opp q is set); if
@@ -870,9 +920,9 @@ __global__ void __launch_bounds__(kBlockThreads) io_kernel(T* __restrict__ a, T*
             out0[c.id] = T(0);
 #pragma unroll
             for (int d = 0; d < 3; ++d) out1[(uint64_t)d * n + c.id] = T(0);
-        } else if constexpr (!is_eso(S)) {
-            // (in the esoteric pull a solid cell's slots hold the bounce-back
-            // values of its fluid neighbours' links: not cleared here)
+        } else if constexpr (!solid_slots_live(S)) {
+            // (in the esoteric schemes a solid cell's slots hold the
+            // bounce-back values of its fluid neighbours' links: not cleared)
 #pragma unroll
             for (int q = 0; q < kQ; ++q) {
                 *slot<L>(a, n, q, c.id) = T(0);
@@ -886,7 +936,7 @@ __global__ void __launch_bounds__(kBlockThreads) io_kernel(T* __restrict__ a, T*
     T f[kQ];
     if constexpr (OP == kReadF || OP == kReadMoments || OP == kReadS) {
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) f[q] = *state_slot<S, L>(a, n, c, bits, q, obits);
+        for (int q = 0; q < kQ; ++q) f[q] = *state_slot<S, L>(a, g, c, bits, q, obits);
         if constexpr (S != kAAEven) apply_open(f, obits, p, c);
         if constexpr (OP == kReadF) {
 #pragma unroll
@@ -926,7 +976,7 @@ __global__ void __launch_bounds__(kBlockThreads) io_kernel(T* __restrict__ a, T*
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
             if (S != kAAEven && ((obits >> q) & 1u)) continue;
-            *state_slot<S, L>(a, n, c, bits, q, obits) = f[q];
+            *state_slot<S, L>(a, g, c, bits, q, obits) = f[q];
         }
     }
 }

@@ -84,6 +84,7 @@ struct CompactGeom {
     const uint32_t* cellp;
     const uint32_t* cellid;  // cell index x + nx (y + ny z) of the i-th fluid cell
     const uint32_t* bbase;   // esoteric pull: first bounce-back slot of the i-th fluid cell
+    const uint32_t* tidx;    // esoteric twist: stored index of every padded cell (fluid, ghost) or kInvalid
     uint32_t nf;   // fluid cells
     uint32_t px;   // nx + 2
     uint32_t pxy;  // (nx + 2)(ny + 2)
@@ -225,13 +226,38 @@ __device__ __forceinline__ uint32_t eso_bounce_slot(uint32_t base, uint32_t mask
 // Element offset (from the start of the buffer) of canonical f_q(x, t) of
 // fluid cell i for stored state kind S (same maps as the dense layouts;
 // x - c_q = x + c_opp(q)); used by the state transfers.
+// Esoteric twist on the compact store (the map of the dense layouts, see
+// twist_off): the fluid cells keep their indices 0 .. nf - 1; a location
+// x - o (o one of the six offsets c+ of the directions with a positive
+// component) that is not a fluid cell has a ghost cell of its own, numbered
+// after the fluid cells in cell order (a solid cell behind a fluid one, or
+// the halo below a low face that is not periodic).  tidx gives the stored
+// index of every padded cell, the periodic image in a periodic halo.
+// Every location x - o of a fluid cell is fluid or a ghost; the clamp keeps
+// the index inside the buffer all the same (a table error then shows as a
+// wrong value, not as an access beyond the allocation).
+__device__ __forceinline__ uint32_t twist_ghost_index(const CompactGeom& g, uint32_t v)
+{
+    return min(v, g.s - 1u);
+}
+
+__device__ __forceinline__ uint32_t twist_compact_loc(const CompactGeom& g, uint32_t i, int ox, int oy, int oz)
+{
+    if (ox == 0 && oy == 0 && oz == 0) return i;
+    const uint32_t off = (uint32_t)ox + (uint32_t)oy * g.px + (uint32_t)oz * g.pxy;
+    return twist_ghost_index(g, g.tidx[g.cellp[i] - off]);
+}
+
 template <int S>
 __device__ __forceinline__ uint64_t compact_state_off(const CompactGeom& g, uint32_t i, const uint32_t (&nb)[kQ],
                                                       int q)
 {
     const uint64_t s = g.s;
     const uint32_t up = nb[opp(q)];
-    if constexpr (is_eso(S)) {
+    if constexpr (is_twist(S)) {
+        const int pl = S == kTwOdd ? opp(q) : q;
+        return (uint64_t)plane_of(pl) * s + twist_compact_loc(g, i, kCx[q] > 0, kCy[q] > 0, kCz[q] > 0);
+    } else if constexpr (is_eso(S)) {
         constexpr bool odd = S == kEsoOdd;
         if (q == 9) return (uint64_t)plane_of(9) * s + i;
         if (q < 9) return (uint64_t)plane_of((no_fluid(up) || !odd) ? q : opp(q)) * s + i;
@@ -496,6 +522,80 @@ __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restri
         eso_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, mo, i, acc);
     } else {
         if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, g, p, mo, i, acc);
+        if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
+            block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
+    }
+}
+
+// Esoteric-twist step on the compact store (K = kTwEven / kTwOdd; the map is
+// described at twist_compact_loc and twist_off).  Every population of the
+// pair (q, opp q) stays in the pair's two-plane block: reads and both
+// candidate writes are a uniform base plus a 32-bit offset, and a bounced
+// link only selects the other sub-plane at the same location.
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
+__device__ __forceinline__ void twist_compact_cell(T* __restrict__ a, const CompactGeom& g, const Phys<T>& p,
+                                                   const MomOut<T>& mo, uint32_t i, double (&acc)[6])
+{
+    constexpr int P = K == kTwOdd ? 1 : 0;
+    const uint32_t sb = g.s * (uint32_t)sizeof(T);
+    char* const A = (char*)a;
+    const uint32_t pc = g.cellp[i];
+    uint32_t nb[kQ];
+    neighbours_rows(g, pc, nb);
+    uint32_t bm = 0u, wm = 0u;
+    if constexpr (MEX) link_masks(nb, bm, wm);
+    // stored indices of x - o, o = (ox, oy, oz) in {0, 1}^3, at [ox + 2 oy + 4 oz]
+    uint32_t loc[7];
+    loc[0] = i;
+    loc[1] = twist_ghost_index(g, g.tidx[pc - 1u]);
+    loc[2] = twist_ghost_index(g, g.tidx[pc - g.px]);
+    loc[3] = twist_ghost_index(g, g.tidx[pc - 1u - g.px]);
+    loc[4] = twist_ghost_index(g, g.tidx[pc - g.pxy]);
+    loc[5] = twist_ghost_index(g, g.tidx[pc - 1u - g.pxy]);
+    loc[6] = twist_ghost_index(g, g.tidx[pc - g.px - g.pxy]);
+    T f[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        const int o = (kCx[q] > 0 ? 1 : 0) + (kCy[q] > 0 ? 2 : 0) + (kCz[q] > 0 ? 4 : 0);
+        const int pl = P == 0 ? q : opp(q);
+        f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), (sub_of(pl) ? sb : 0u) + loc[o] * (uint32_t)sizeof(T));
+    }
+    if constexpr (OPEN) apply_open_nb(f, nb, p);
+    T rho, ux, uy, uz;
+    collide<T, FORCE>(f, p, rho, ux, uy, uz);
+    if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        // where f_opp(q) was read (x + c-_q, plane opp q at P = 0, q at P = 1),
+        // or the other plane there if the link bounces back (x + c_q solid,
+        // beyond a wall or a face with a face rule; a reservoir's link leaves)
+        const int o = (kCx[q] < 0 ? 1 : 0) + (kCy[q] < 0 ? 2 : 0) + (kCz[q] < 0 ? 4 : 0);
+        const bool back = no_fluid(nb[q]) && !is_res(nb[q], g.open);
+        const int pn = P == 0 ? opp(q) : q, pb = P == 0 ? q : opp(q);
+        const uint32_t sub = back ? (sub_of(pb) ? sb : 0u) : (sub_of(pn) ? sb : 0u);
+        st_at<false>(pair_block(A, pair_of(q), sb), sub + loc[o] * (uint32_t)sizeof(T), f[q]);
+    }
+    if constexpr (MEX) add_links_mask(acc, f, bm, wm);
+}
+
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false>
+__global__ void __launch_bounds__(kGatherThreads) twist_compact_kernel(T* __restrict__ a, CompactGeom g, Phys<T> p,
+                                                                      MomOut<T> mo)
+{
+    static_assert(is_twist(K), "esoteric-twist step");
+    const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
+    const uint32_t i = wg * kGatherThreads + threadIdx.x;
+    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    if constexpr (OUT) {
+        static_assert(!MEX, "no fields output in a momentum-exchange step");
+        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, true, false>(a, g, p, mo, i, acc);
+        const uint32_t i0 = i - (threadIdx.x & 63u);
+        if (i0 < g.nf) zero_solid_range(mo, g.cellid, g.nf, i0);
+    } else if constexpr (!MEX) {
+        if (i >= g.nf) return;
+        twist_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, mo, i, acc);
+    } else {
+        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, g, p, mo, i, acc);
         if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
             block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
     }

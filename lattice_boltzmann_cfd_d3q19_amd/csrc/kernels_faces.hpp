@@ -163,7 +163,7 @@ __global__ void __launch_bounds__(kBlockThreads) face_kernel(T* __restrict__ a, 
     const uint32_t obits = open_bits(g, c);
     T s[kQ];
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g.n, c, bits, q, obits);
+    for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g, c, bits, q, obits);
     // entering through this face: c_q[ax] = sigma, unless the upstream cell
     // also lies beyond a wall of another axis (an edge: the wall wins)
     uint32_t ent = 0;
@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(kBlockThreads) face_kernel(T* __restrict__ a, 
         if (!solid1) {
             const uint32_t bits1 = link_bits<true>(g, c1), obits1 = open_bits(g, c1);
 #pragma unroll
-            for (int q = 0; q < kQ; ++q) s1[q] = *state_slot<S, L>(a, g.n, c1, bits1, q, obits1);
+            for (int q = 0; q < kQ; ++q) s1[q] = *state_slot<S, L>(a, g, c1, bits1, q, obits1);
         } else {
 #pragma unroll
             for (int q = 0; q < kQ; ++q) s1[q] = T(0);
@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(kBlockThreads) face_kernel(T* __restrict__ a, 
     // a wall to the steps), so these are the own bounce slots
 #pragma unroll
     for (int q = 0; q < kQ; ++q)
-        if ((ent >> q) & 1u) *state_slot<S, L>(a, g.n, c, bits, q, obits) = s[q];
+        if ((ent >> q) & 1u) *state_slot<S, L>(a, g, c, bits, q, obits) = s[q];
 }
 
 // Compact layout: the same on the fluid-compacted store; the index table

@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(kBlockThreads) mex_kernel(T* __restrict__ a, G
         const uint32_t obits = open_bits(g, c);
         T s[kQ];
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g.n, c, bits, q, obits);
+        for (int q = 0; q < kQ; ++q) s[q] = *state_slot<S, L>(a, g, c, bits, q, obits);
         if constexpr (S != kAAEven) apply_open(s, obits, p, c);
         collide<T, true>(s, p);
         // x + c_q is solid or beyond a wall iff the upstream bit of opp(q) is
@@ -65,7 +65,7 @@ __global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restric
         T f[kQ];
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            if constexpr (is_eso(S)) {
+            if constexpr (solid_slots_live(S)) {
                 f[q] = a[compact_state_off<S>(g, i, nb, q)];
                 continue;
             }

@@ -45,16 +45,19 @@ struct CompactTables {
     uint32_t* cellp;   // compact index -> padded cell
     uint32_t* cellid;  // compact index -> cell index
     uint32_t* bbase;   // esoteric pull: first bounce-back slot of each fluid cell (else null)
+    uint32_t* tidx;    // esoteric twist: stored index of each padded cell (else null)
+    uint32_t* grows;   // esoteric twist: ghost cells per padded row, then their exclusive scan
     uint32_t nf;       // fluid cells (known on the host after the build)
     uint64_t stride;   // population stride, nf rounded up to 64
 };
 
 // Byte offsets of the tables inside a workspace, and its size.
 struct CompactLayoutBytes {
-    size_t header, rows, idxp, cellp, cellid, bbase, total;
+    size_t header, rows, idxp, cellp, cellid, bbase, tidx, grows, total;
 };
-// bounce: also the esoteric pull's bounce-back slot table (4 bytes per cell)
-CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz, bool bounce);
+// bounce: also the esoteric pull's bounce-back slot table (4 bytes per cell);
+// twist: also the esoteric twist's stored-index table and ghost row counts
+CompactLayoutBytes compact_workspace_layout(int64_t nx, int64_t ny, int64_t nz, bool bounce, bool twist);
 
 // Build the compact tables from the mask and the periodic flags.
 hipError_t launch_compact_build(const LaunchGeom& g, const CompactTables& t, hipStream_t s);
@@ -62,6 +65,11 @@ hipError_t launch_compact_build(const LaunchGeom& g, const CompactTables& t, hip
 // Esoteric pull: bbase[i] = number of bounce-back links (x + c_k not fluid,
 // k < 9) of the fluid cells before i (an exclusive scan); needs t.nf.
 hipError_t launch_compact_bounce(const LaunchGeom& g, const CompactTables& t, hipStream_t s);
+
+// Esoteric twist: ghost cells and the stored-index table tidx (fluid cells
+// keep their indices, ghosts follow from nf in cell order); header[2] = the
+// ghost count.  Needs t.nf; no-op if t.tidx is null.
+hipError_t launch_compact_twist(const LaunchGeom& g, const CompactTables& t, hipStream_t s);
 
 template <typename T>
 hipError_t launch_step_compact(int kind, T* a, T* b, const LaunchGeom& g, const CompactTables& t,

@@ -136,6 +136,8 @@ hipError_t launch_step_l(int kind, T* a, T* b, const Shape& s, const Phys<T>& p,
     case kAAOdd: return launch_step_k<T, L, kAAOdd>(a, b, s, p, mo, bnd, force, st);
     case kEsoEven: return launch_step_k<T, L, kEsoEven>(a, b, s, p, mo, bnd, force, st);
     case kEsoOdd: return launch_step_k<T, L, kEsoOdd>(a, b, s, p, mo, bnd, force, st);
+    case kTwEven: return launch_step_k<T, L, kTwEven>(a, b, s, p, mo, bnd, force, st);
+    case kTwOdd: return launch_step_k<T, L, kTwOdd>(a, b, s, p, mo, bnd, force, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -206,6 +208,8 @@ hipError_t launch_io_l(int state, int op, T* a, T* b, const Shape& s, const Phys
     case kAAOdd: return launch_io_s<T, L, kAAOdd>(op, a, b, s, p, o0, o1, i0, i1, st);
     case kEsoEven: return launch_io_s<T, L, kEsoEven>(op, a, b, s, p, o0, o1, i0, i1, st);
     case kEsoOdd: return launch_io_s<T, L, kEsoOdd>(op, a, b, s, p, o0, o1, i0, i1, st);
+    case kTwEven: return launch_io_s<T, L, kTwEven>(op, a, b, s, p, o0, o1, i0, i1, st);
+    case kTwOdd: return launch_io_s<T, L, kTwOdd>(op, a, b, s, p, o0, o1, i0, i1, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -233,6 +237,7 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     g.cellp = t.cellp;
     g.cellid = t.cellid;
     g.bbase = t.bbase;
+    g.tidx = t.tidx;
     g.nf = t.nf;
     g.px = (uint32_t)lg.nx + 2;
     g.pxy = (uint32_t)((lg.nx + 2) * (lg.ny + 2));
@@ -313,11 +318,36 @@ hipError_t launch_eso_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, hi
     return hipLaunchKernel(k, grid, block, args, 0, st);
 }
 
+template <typename T, int K, bool FORCE>
+hipError_t launch_twist_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, hipStream_t st)
+{
+    if (g.nf == 0) return hipSuccess;
+    void* args[] = {&a, &g, &p, &mo};
+    uint32_t nwg = (g.nf + kGatherThreads - 1) / kGatherThreads;
+    if (g.xk > 1) nwg = (nwg + 8 * g.xk - 1) / (8 * g.xk) * (8 * g.xk);
+    const dim3 grid(nwg), block(kGatherThreads);
+    const bool out = mo.rho != nullptr;
+    if (mo.partial != nullptr) {
+        if (out) return hipErrorInvalidValue;
+        const void* k = g.open ? (const void*)&twist_compact_kernel<T, K, FORCE, true, false, true>
+                               : (const void*)&twist_compact_kernel<T, K, FORCE, false, false, true>;
+        return hipLaunchKernel(k, grid, block, args, 0, st);
+    }
+    const void* k = g.open ? (out ? (const void*)&twist_compact_kernel<T, K, FORCE, true, true>
+                                  : (const void*)&twist_compact_kernel<T, K, FORCE, true, false>)
+                           : (out ? (const void*)&twist_compact_kernel<T, K, FORCE, false, true>
+                                  : (const void*)&twist_compact_kernel<T, K, FORCE, false, false>);
+    return hipLaunchKernel(k, grid, block, args, 0, st);
+}
+
 template <typename T, int K>
 hipError_t launch_step_compact_k(T* a, T* b, CompactGeom g, Phys<T> p, MomOut<T> mo, bool force, hipStream_t st)
 {
     if constexpr (is_eso(K)) {
         return force ? launch_eso_compact_t<T, K, true>(a, g, p, mo, st) : launch_eso_compact_t<T, K, false>(a, g, p, mo, st);
+    } else if constexpr (is_twist(K)) {
+        return force ? launch_twist_compact_t<T, K, true>(a, g, p, mo, st)
+                     : launch_twist_compact_t<T, K, false>(a, g, p, mo, st);
     } else if constexpr (K == kAAEven) {
         return force ? launch_even_compact_t<T, true>(a, g, p, mo, st) : launch_even_compact_t<T, false>(a, g, p, mo, st);
     } else {
@@ -350,6 +380,8 @@ hipError_t launch_step_compact_mo(int kind, T* a, T* b, const LaunchGeom& lg, co
     case kAAOdd: return launch_step_compact_k<T, kAAOdd>(a, b, g, p, m, lp.has_force, st);
     case kEsoEven: return launch_step_compact_k<T, kEsoEven>(a, b, g, p, m, lp.has_force, st);
     case kEsoOdd: return launch_step_compact_k<T, kEsoOdd>(a, b, g, p, m, lp.has_force, st);
+    case kTwEven: return launch_step_compact_k<T, kTwEven>(a, b, g, p, m, lp.has_force, st);
+    case kTwOdd: return launch_step_compact_k<T, kTwOdd>(a, b, g, p, m, lp.has_force, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -399,6 +431,8 @@ hipError_t launch_io_compact(int state, int op, T* a, const LaunchGeom& lg, cons
     case kAAOdd: return launch_io_compact_s<T, kAAOdd>(op, a, cg, s, p, o0, o1, i0, i1, st);
     case kEsoEven: return launch_io_compact_s<T, kEsoEven>(op, a, cg, s, p, o0, o1, i0, i1, st);
     case kEsoOdd: return launch_io_compact_s<T, kEsoOdd>(op, a, cg, s, p, o0, o1, i0, i1, st);
+    case kTwEven: return launch_io_compact_s<T, kTwEven>(op, a, cg, s, p, o0, o1, i0, i1, st);
+    case kTwOdd: return launch_io_compact_s<T, kTwOdd>(op, a, cg, s, p, o0, o1, i0, i1, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -445,6 +479,8 @@ hipError_t launch_face_l(int state, T* a, const Geom& g, const Phys<T>& p, const
     case kAAOdd: return hipLaunchKernel((const void*)&face_kernel<T, L, kAAOdd>, grid, block, args, 0, st);
     case kEsoEven: return hipLaunchKernel((const void*)&face_kernel<T, L, kEsoEven>, grid, block, args, 0, st);
     case kEsoOdd: return hipLaunchKernel((const void*)&face_kernel<T, L, kEsoOdd>, grid, block, args, 0, st);
+    case kTwEven: return hipLaunchKernel((const void*)&face_kernel<T, L, kTwEven>, grid, block, args, 0, st);
+    case kTwOdd: return hipLaunchKernel((const void*)&face_kernel<T, L, kTwOdd>, grid, block, args, 0, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -464,6 +500,8 @@ hipError_t launch_face_compact(int state, T* a, const CompactGeom& cg, const Phy
     case kAAOdd: return hipLaunchKernel((const void*)&face_compact_kernel<T, kAAOdd>, grid, block, args, 0, st);
     case kEsoEven: return hipLaunchKernel((const void*)&face_compact_kernel<T, kEsoEven>, grid, block, args, 0, st);
     case kEsoOdd: return hipLaunchKernel((const void*)&face_compact_kernel<T, kEsoOdd>, grid, block, args, 0, st);
+    case kTwEven: return hipLaunchKernel((const void*)&face_compact_kernel<T, kTwEven>, grid, block, args, 0, st);
+    case kTwOdd: return hipLaunchKernel((const void*)&face_compact_kernel<T, kTwOdd>, grid, block, args, 0, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -533,6 +571,8 @@ hipError_t launch_mex_l(int state, T* a, const Shape& sh, const Phys<T>& p, doub
     case kAAOdd: return launch_mex_t<T, L, kAAOdd>(a, sh, p, partial, st);
     case kEsoEven: return launch_mex_t<T, L, kEsoEven>(a, sh, p, partial, st);
     case kEsoOdd: return launch_mex_t<T, L, kEsoOdd>(a, sh, p, partial, st);
+    case kTwEven: return launch_mex_t<T, L, kTwEven>(a, sh, p, partial, st);
+    case kTwOdd: return launch_mex_t<T, L, kTwOdd>(a, sh, p, partial, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -557,6 +597,8 @@ hipError_t launch_momentum_exchange(int layout, int state, T* a, const LaunchGeo
             case kAAOdd: e = launch_mex_compact_t<T, kAAOdd>(a, cg, p, partial, st); break;
             case kEsoEven: e = launch_mex_compact_t<T, kEsoEven>(a, cg, p, partial, st); break;
             case kEsoOdd: e = launch_mex_compact_t<T, kEsoOdd>(a, cg, p, partial, st); break;
+            case kTwEven: e = launch_mex_compact_t<T, kTwEven>(a, cg, p, partial, st); break;
+            case kTwOdd: e = launch_mex_compact_t<T, kTwOdd>(a, cg, p, partial, st); break;
             default: return hipErrorInvalidValue;
             }
         }

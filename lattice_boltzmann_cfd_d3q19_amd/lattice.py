@@ -10,7 +10,8 @@ from . import capi
 _PREC = {"f32": (capi.LBM_F32, torch.float32), "f64": (capi.LBM_F64, torch.float64)}
 _LAYOUT = {"stream": capi.LBM_LAYOUT_STREAM, "bundle": capi.LBM_LAYOUT_BUNDLE,
            "collision": capi.LBM_LAYOUT_COLLISION, "compact": capi.LBM_LAYOUT_COMPACT}
-_SCHEME = {"ab": capi.LBM_SCHEME_AB, "aa": capi.LBM_SCHEME_AA, "eso": capi.LBM_SCHEME_ESOPULL}
+_SCHEME = {"ab": capi.LBM_SCHEME_AB, "aa": capi.LBM_SCHEME_AA, "eso": capi.LBM_SCHEME_ESOPULL,
+           "twist": capi.LBM_SCHEME_ESOTWIST}
 
 Q = 19
 
@@ -21,7 +22,7 @@ class Lattice:
     precision: "f32" | "f64"; layout: "stream" | "bundle" | "collision" |
     "compact" (SoA over fluid cells only); scheme: "ab" (two lattices, fused
     pull) | "aa" (one lattice, in place) | "eso" (one lattice, in place,
-    esoteric pull).
+    esoteric pull) | "twist" (one lattice, in place, esoteric twist).
     """
 
     def __init__(self, nx, ny, nz, precision="f32", layout="stream", scheme="aa", tau=1.0,

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 LAYOUTS = ("stream", "bundle", "collision", "compact")
-SCHEMES = ("ab", "aa", "eso")
+SCHEMES = ("ab", "aa", "eso", "twist")
 TOL = {"f32": 1e-5, "f64": 1e-12}
 
 

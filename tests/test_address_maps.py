@@ -5,7 +5,8 @@ the kernels' code; the GPU's collision-free bit-exact runs check the code).
 AA (fieldcraft page, first section): even steps read (q, x) and write
 (opp q, x); odd steps read (opp q, x - c_q) and write (q, x + c_q), with the
 halfway bounce-back substitutions (own slots) where the link leaves the fluid.
-Esoteric pull (dense and compact storage), as described in the design notes.
+Esoteric pull (dense and compact storage) and esoteric twist, as described
+in the design notes.
 For every scheme and parity: the read slots of all (cell, direction) pairs
 are distinct, so are the written slots, each cell writes exactly the slots it
 read (no cell can overwrite another's input), and collision-free steps through
@@ -93,11 +94,51 @@ def eso_slots(g, parity, compact):
     return rd, wr
 
 
+def twist_slots(g, parity):
+    """Esoteric twist: f_q of x at parity P lives at x - c+_q (c+ = max(c, 0)
+    per axis) in plane q (P = 0) or opp q (P = 1); below the low face of a
+    non-periodic axis the location is a halo slot, keyed by its coordinate -1.
+    f*_q goes where f_opp(q) was read, or, bounced back, to the other plane
+    at that location: where x finds f_opp(q) at the next step."""
+    def loc(x, d):
+        p = g.coords(x)
+        for a in range(3):
+            p[a] += int(d[a])
+            if p[a] < 0 and g.periodic[a]:
+                p[a] += g.dims[a]
+        return tuple(p)
+
+    def plane(par, q):
+        return q if par == 0 else OPP[q]
+
+    rd, wr = {}, {}
+    for x in g.fluid:
+        for q in range(Q):
+            rd[x, q] = (plane(parity, q), loc(x, -np.maximum(C[q], 0)))
+    for x in g.fluid:
+        for q in range(Q):
+            kind, _ = g.link(x, C[q])
+            o = OPP[q]
+            where = loc(x, np.minimum(C[q], 0))
+            wr[x, q] = (plane(parity, o) if kind in ("fluid", "open") else plane(1 - parity, o), where)
+    return rd, wr
+
+
 def check_maps(g, rd, wr):
     assert len(set(rd.values())) == len(rd), "two links read one slot"
     assert len(set(wr.values())) == len(wr), "two links write one slot"
     for x in g.fluid:
         assert {rd[x, q] for q in range(Q)} == {wr[x, q] for q in range(Q)}, x
+
+
+def check_maps_no_cross(g, rd, wr):
+    """Reads distinct, writes distinct, and no cell writes a slot that another
+    cell reads in the same step (a cell may write a slot no one reads)."""
+    assert len(set(rd.values())) == len(rd), "two links read one slot"
+    assert len(set(wr.values())) == len(wr), "two links write one slot"
+    reader = {s: x for (x, q), s in rd.items()}
+    for (x, q), s in wr.items():
+        assert reader.get(s, x) == x, (x, q, s, reader.get(s))
 
 
 def stream_through(g, box, f0, steps, slots):
@@ -150,3 +191,7 @@ def test_in_place_maps_are_race_free_and_stream(name):
         for parity in (0, 1):
             check_maps(g, *slots(parity))
         stream_through(g, box, f0, 4, slots)
+    slots = lambda p: twist_slots(g, p)  # noqa: E731
+    for parity in (0, 1):
+        check_maps_no_cross(g, *slots(parity))
+    stream_through(g, box, f0, 4, slots)

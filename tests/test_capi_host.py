@@ -116,6 +116,34 @@ def test_esoteric_pull_buffers():
     assert capi.lbm_workspace_bytes(eso)[1] == capi.lbm_workspace_bytes(aa)[1] + 2560
 
 
+def test_esoteric_twist_buffers():
+    # one buffer, 19 planes; the dense layouts store one halo layer below each
+    # low face, (nx+1)(ny+1)(nz+1) cells per plane, and the compact one has
+    # room for as many stored cells (fluid and ghost), rounded up to 64
+    for layout, cells in ((capi.LBM_LAYOUT_STREAM, 17 * 9 * 6), (capi.LBM_LAYOUT_BUNDLE, 17 * 9 * 6),
+                          (capi.LBM_LAYOUT_COLLISION, 17 * 9 * 6), (capi.LBM_LAYOUT_COMPACT, 960)):
+        d = capi.make_desc(16, 8, 5, capi.LBM_F32, layout=layout, scheme=capi.LBM_SCHEME_ESOTWIST)
+        st, nbytes, nbuf = capi.lbm_buffer_bytes(d)
+        assert st == capi.LBM_OK and nbuf == 1 and nbytes == 19 * cells * 4, (layout, nbytes)
+        assert capi.lbm_create(d, FAKE, FAKE + (1 << 20))[0] == capi.LBM_ERR_INVALID_ARGUMENT
+        st, h = capi.lbm_create(d, FAKE)
+        assert st == capi.LBM_OK
+        capi.lbm_destroy(h)
+    # the padded cells are addressed with 32-bit indices: a box whose cells fit
+    # but whose padded cells do not is refused for this scheme only
+    thin = dict(nx=1, ny=1, nz=1 << 30)
+    assert capi.lbm_buffer_bytes(capi.make_desc(thin["nx"], thin["ny"], thin["nz"], capi.LBM_F32,
+                                                scheme=capi.LBM_SCHEME_AA))[0] == capi.LBM_OK
+    assert capi.lbm_buffer_bytes(capi.make_desc(thin["nx"], thin["ny"], thin["nz"], capi.LBM_F32,
+                                                scheme=capi.LBM_SCHEME_ESOTWIST))[0] == capi.LBM_ERR_UNSUPPORTED
+    # its compact workspace also holds the stored index of every padded cell
+    # and the ghost count of every padded row
+    aa = capi.make_desc(16, 8, 5, capi.LBM_F32, layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_AA)
+    tw = capi.make_desc(16, 8, 5, capi.LBM_F32, layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_ESOTWIST)
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert capi.lbm_workspace_bytes(tw)[1] == capi.lbm_workspace_bytes(aa)[1] + up(4 * 18 * 10 * 7) + up(4 * 10 * 7)
+
+
 def test_buffer_rules():
     aa = capi.make_desc(8, 8, 8, scheme=capi.LBM_SCHEME_AA)
     ab = capi.make_desc(8, 8, 8, scheme=capi.LBM_SCHEME_AB)

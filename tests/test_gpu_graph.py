@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("layout,scheme", [("stream", "aa"), ("compact", "aa"), ("bundle", "ab"),
-                                           ("compact", "eso")])
+                                           ("compact", "eso"), ("compact", "twist"), ("collision", "twist")])
 def test_graph_replays_equal_direct_steps(layout, scheme):
     need_gpu()
     from lattice_boltzmann_cfd_d3q19_amd import Lattice

@@ -74,7 +74,7 @@ def test_force_matches_oracle_all_layouts_schemes(name, precision):
 
 
 @pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "ab"), ("bundle", "aa"), ("compact", "eso"),
-                                           ("collision", "eso")])
+                                           ("collision", "eso"), ("compact", "twist"), ("stream", "twist")])
 def test_force_closes_momentum_budget_fp64(layout, scheme):
     # P(t+1) - P(t) = N_fluid F - F_solid - F_wall over the step the force was
     # taken for (P = sum of rho u over fluid cells, u including F/2)

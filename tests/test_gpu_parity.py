@@ -240,7 +240,8 @@ def _full_size(name):
     ("channel_f64", "stream", "aa"), ("channel_f64", "stream", "ab"),
     ("porous256", "stream", "aa"), ("porous256", "stream", "ab"),
     ("porous256", "compact", "eso"), ("porous256", "stream", "eso"), ("sphere128", "collision", "eso"),
-    ("channel_f64", "bundle", "eso")])
+    ("channel_f64", "bundle", "eso"), ("porous256", "compact", "twist"), ("porous256", "stream", "twist"),
+    ("sphere128", "collision", "twist"), ("channel_f64", "bundle", "twist")])
 def test_full_size_sampled_steps(name, layout, scheme):
     """At the benchmark sizes: advance a few steps, then check two consecutive
     steps (odd -> even and even -> odd for AA) at sampled cells against the
@@ -311,7 +312,8 @@ def test_compact_tables_bit_exact(periodic):
     assert np.array_equal(ws[cell_off:cell_off + nf], want_cellp)
 
 
-@pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "ab"), ("compact", "eso")])
+@pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "ab"), ("compact", "eso"),
+                                           ("compact", "twist"), ("stream", "twist")])
 def test_full_size_open_channel_sampled_steps(layout, scheme):
     """The 768 x 192 x 96 open channel at full size: equilibrium inlet on -x,
     Zou-He pressure outlet on +x, walls in y, periodic z, a cylinder of
@@ -425,7 +427,8 @@ def _neighbourhood(cells, shape):
     return np.unique(np.concatenate(out))
 
 
-@pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "aa"), ("stream", "ab")])
+@pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "aa"), ("stream", "ab"),
+                                           ("compact", "twist"), ("stream", "twist")])
 def test_full_size_512_sampled_steps(layout, scheme):
     """The 512^3 porous medium (19,200 spheres, the large-footprint run): the
     dense layouts address up to 19 x 2^27 elements here, past 2^31, and the

@@ -140,7 +140,7 @@ def test_porous_256_schemes_agree_1000_steps():
     mask, _ = li.porous_mask(256)
     out = {}
     for scheme, layout in (("aa", "stream"), ("ab", "stream"), ("aa", "compact"), ("eso", "compact"),
-                           ("eso", "stream")):
+                           ("eso", "stream"), ("twist", "compact"), ("twist", "stream")):
         lat = make((256,) * 3, "f32", layout, scheme, tau=0.65, force=(1e-6, 0.0, 0.0), mask=mask)
         m0 = _mass(lat)
         lat.step(1000)
@@ -155,7 +155,8 @@ def test_porous_256_schemes_agree_1000_steps():
         assert torch.equal(out[("aa", "stream")], out[k]), k
 
 
-@pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "ab"), ("compact", "eso")])
+@pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "ab"), ("compact", "eso"),
+                                           ("compact", "twist")])
 def test_pressure_driven_channel_fp64(layout, scheme):
     """Zou-He pressure faces at both ends of a 96 x 24 x 4 walled channel (fp64,
     tau 0.8, rho 1.0015 -> 0.9985): at steady state the density falls
