@@ -312,6 +312,74 @@ def test_compact_tables_bit_exact(periodic):
     assert np.array_equal(ws[cell_off:cell_off + nf], want_cellp)
 
 
+@pytest.mark.parametrize("periodic", [(1, 1, 1), (0, 1, 0), (1, 0, 1), (0, 0, 0)])
+def test_twist_ghost_table_bit_exact(periodic):
+    """The esoteric twist's stored-index table on the compact layout equals a
+    numpy construction: fluid cells keep their rank; a non-fluid location from
+    which one of the six offsets (x, y, z, xy, xz, yz) leads to a fluid cell,
+    inside the box or below a low face that is not periodic, is a ghost
+    numbered nf + (its rank among ghosts in padded-cell order); a periodic
+    halo holds its image; anything else is 0xFFFFFFFF."""
+    need_gpu()
+    import torch
+    shape = (23, 17, 11)
+    nx, ny, nz = shape
+    mask = li.random_mask(*shape, fraction=0.3, seed=29)
+    lat = make(shape, "f32", "compact", "twist", tau=0.7, mask=mask, periodic=periodic)
+    torch.cuda.synchronize()
+    fluid = (mask == 0).reshape(nz, ny, nx)
+    nf = int(fluid.sum())
+    rank = np.full((nz, ny, nx), 0xFFFFFFFF, np.int64)
+    rank[fluid] = np.arange(nf)
+    dims = (nx, ny, nz)
+
+    def is_fluid(x, y, z):
+        p = [x, y, z]
+        for a in range(3):
+            if periodic[a]:
+                p[a] %= dims[a]
+            elif not 0 <= p[a] < dims[a]:
+                return False
+        return bool(fluid[p[2], p[1], p[0]])
+
+    def candidate(v, a):
+        return 0 <= v < dims[a] or (v == -1 and not periodic[a])
+
+    offs = [(1, 0, 0), (0, 1, 0), (0, 0, 1), (1, 1, 0), (1, 0, 1), (0, 1, 1)]
+    px, py, pz = nx + 2, ny + 2, nz + 2
+    want = np.full((pz, py, px), 0xFFFFFFFF, np.int64)
+    ng = 0
+    for z in range(-1, nz + 1):
+        for y in range(-1, ny + 1):
+            for x in range(-1, nx + 1):
+                if not (candidate(x, 0) and candidate(y, 1) and candidate(z, 2)):
+                    continue
+                if 0 <= x < nx and 0 <= y < ny and 0 <= z < nz and fluid[z, y, x]:
+                    want[z + 1, y + 1, x + 1] = rank[z, y, x]
+                elif not is_fluid(x, y, z) and any(is_fluid(x + a, y + b, z + c) for a, b, c in offs):
+                    want[z + 1, y + 1, x + 1] = nf + ng
+                    ng += 1
+    # periodic halos: the entry of the cell with those coordinates wrapped
+    for z in range(pz):
+        for y in range(py):
+            for x in range(px):
+                q = [x, y, z]
+                halo = False
+                for a, n in enumerate(dims):
+                    if periodic[a] and q[a] in (0, n + 1):
+                        q[a] = n if q[a] == 0 else 1
+                        halo = True
+                if halo:
+                    want[z, y, x] = want[q[2], q[1], q[0]]
+    ws = lat.workspace.cpu().numpy().view(np.uint32)
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    npad, n64 = px * py * pz, (nx * ny * nz + 63) // 64 * 64
+    off = (256 + up(4 * ny * nz) + up(4 * npad) + 2 * up(4 * n64)) // 4
+    got = ws[off:off + npad].astype(np.int64)
+    assert np.array_equal(got, want.reshape(-1)), int(np.sum(got != want.reshape(-1)))
+    say("twist ghosts", periodic, "fluid", nf, "ghosts", ng)
+
+
 @pytest.mark.parametrize("layout,scheme", [("compact", "aa"), ("stream", "ab"), ("compact", "eso"),
                                            ("compact", "twist"), ("stream", "twist")])
 def test_full_size_open_channel_sampled_steps(layout, scheme):
