@@ -194,9 +194,20 @@ def test_momentum_exchange_arguments_before_any_launch():
         assert capi.lbm_momentum_exchange(h, FAKE, FAKE + 8, nb) == capi.LBM_ERR_MISALIGNED
         assert capi.lbm_momentum_exchange(h, FAKE + 4, FAKE, nb) == capi.LBM_ERR_MISALIGNED
         assert capi.lbm_momentum_exchange(h, FAKE, FAKE, nb) == capi.LBM_ERR_BAD_STATE
+        # the same rules for the exchange taken inside the last of n >= 1 steps
+        step_mex = capi.lbm_step_momentum_exchange
+        assert step_mex(h, 0, FAKE, FAKE, nb) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert step_mex(h, 1, None, FAKE, nb) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert step_mex(h, 1, FAKE, None, nb) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert step_mex(h, 1, FAKE, FAKE, nb - 1) == capi.LBM_ERR_INVALID_ARGUMENT
+        assert step_mex(h, 1, FAKE, FAKE + 8, nb) == capi.LBM_ERR_MISALIGNED
+        assert step_mex(h, 1, FAKE + 4, FAKE, nb) == capi.LBM_ERR_MISALIGNED
+        assert step_mex(h, 1, FAKE, FAKE, nb) == capi.LBM_ERR_BAD_STATE
+        assert capi.lbm_time(h) == 0
     finally:
         capi.lbm_destroy(h)
     assert capi.lbm_momentum_exchange(None, FAKE, FAKE, nb) == capi.LBM_ERR_INVALID_ARGUMENT
+    assert capi.lbm_step_momentum_exchange(None, 1, FAKE, FAKE, nb) == capi.LBM_ERR_INVALID_ARGUMENT
 
 
 def test_open_faces_arguments():
