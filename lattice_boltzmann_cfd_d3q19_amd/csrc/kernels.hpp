@@ -737,29 +737,41 @@ __device__ __forceinline__ uint64_t eso_off(uint64_t n, const Cell& c, uint32_t 
 // writes f*_q where it read f_opp(q), i.e. at x + c- (c- = min(c_q, 0)) in
 // plane opp(q) (P = 0) or q (P = 1): the next step finds it there as the
 // population that reached x + c_q.  A bounced-back f*_q goes to the other
-// plane of that location instead, where x itself finds f_opp(q) next.  The
-// dense storage of this scheme has one extra layer of cells below the low
-// face of each axis, (nx+1)(ny+1)(nz+1) cells per plane, padded coordinate =
-// coordinate + 1: behind a low face that is not periodic the location is
-// such a halo cell (it holds a bounced or reservoir value of the cell next
-// to it), on a periodic axis it wraps.
+// plane of that location instead, where x itself finds f_opp(q) next.
+// Behind a low face that is not periodic the location lies below the box
+// (it holds a bounced or reservoir value of the cell next to it); on a
+// periodic axis it wraps.  The dense storage of this scheme keeps the cells
+// of the box at their cell index (rows stay line-aligned) and the cells of
+// the layer below the low faces after them: first those with x = -1
+// ((ny+1)(nz+1), y and z from -1), then y = -1 (nx (nz+1)), then z = -1
+// (nx ny), (nx+1)(ny+1)(nz+1) cells per plane in all.
 __device__ __forceinline__ uint64_t twist_cells(const Geom& g)
 {
     return (uint64_t)(g.nx + 1) * (uint64_t)(g.ny + 1) * (uint64_t)(g.nz + 1);
 }
 
-// padded index of x - (ox, oy, oz), o in {0, 1}^3
+// storage index of x - (ox, oy, oz), o in {0, 1}^3
 __device__ __forceinline__ uint32_t twist_loc(const Geom& g, const Cell& c, int ox, int oy, int oz)
 {
-    auto back = [](uint32_t v, int o, bool face, uint32_t n) -> uint32_t {
-        // padded coordinate of v - o: v + 1 - o, or behind the low face the
-        // halo (0) if that face is not periodic, else the wrapped cell (n)
-        return o == 0 ? v + 1u : v > 0u ? v : face ? 0u : n;
+    // coordinate of v - o: v - o, or behind the low face -1 if that face is
+    // not periodic (then `below`), else the wrapped cell n - 1
+    auto back = [](uint32_t v, int o, bool face, uint32_t n, bool& below) -> uint32_t {
+        if (o == 0 || v > 0u) return v - (uint32_t)o;
+        below = face;
+        return face ? 0u : n - 1u;
     };
-    const uint32_t px = back(c.x, ox, c.wall[0][0] || c.open[0][0], g.nx);
-    const uint32_t py = back(c.y, oy, c.wall[1][0] || c.open[1][0], g.ny);
-    const uint32_t pz = back(c.z, oz, c.wall[2][0] || c.open[2][0], g.nz);
-    return px + (g.nx + 1u) * (py + (g.ny + 1u) * pz);
+    bool bx = false, by = false, bz = false;
+    const uint32_t x = back(c.x, ox, c.wall[0][0] || c.open[0][0], g.nx, bx);
+    const uint32_t y = back(c.y, oy, c.wall[1][0] || c.open[1][0], g.ny, by);
+    const uint32_t z = back(c.z, oz, c.wall[2][0] || c.open[2][0], g.nz, bz);
+    const uint32_t n = (uint32_t)g.n;
+    const uint32_t h1 = (g.ny + 1u) * (g.nz + 1u), h2 = g.nx * (g.nz + 1u);
+    // (a coordinate flagged below is -1: y + 1 and z + 1 are then 0)
+    const uint32_t yb = by ? 0u : y + 1u, zb = bz ? 0u : z + 1u;
+    if (bx) return n + yb + (g.ny + 1u) * zb;
+    if (by) return n + h1 + x + g.nx * zb;
+    if (bz) return n + h1 + h2 + x + g.nx * y;
+    return x + g.nx * (y + g.ny * z);
 }
 
 // element offset of f_q(x) in a twist state of parity P
