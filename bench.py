@@ -39,6 +39,11 @@ def workload(name):
         mask, ns = li.porous_mask(256)
         return dict(shape=(256, 256, 256), periodic=(1, 1, 1), tau=0.65, force=(1e-6, 0.0, 0.0), mask=mask,
                     rho=None, u=None, precision="f32", extra={"n_spheres": ns})
+    if name == "porous256_f64":
+        # the same medium in double precision (304 B per fluid-cell update)
+        mask, ns = li.porous_mask(256)
+        return dict(shape=(256, 256, 256), periodic=(1, 1, 1), tau=0.65, force=(1e-6, 0.0, 0.0), mask=mask,
+                    rho=None, u=None, precision="f64", extra={"n_spheres": ns})
     if name == "porous512":
         mask, ns = li.porous_mask(512)
         return dict(shape=(512, 512, 512), periodic=(1, 1, 1), tau=0.65, force=(1e-6, 0.0, 0.0), mask=mask,
