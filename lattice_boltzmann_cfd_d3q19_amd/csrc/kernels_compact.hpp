@@ -347,25 +347,36 @@ __device__ __forceinline__ char* pair_block(char* base, int k, uint32_t plane_by
     return base + (uint64_t)(2 * k) * plane_bytes;
 }
 
-// Fields output of a compact step: the solid cells get zeros from the wave
-// whose fluid cells surround them.  The wave of fluid cells i0 .. i0 + 63
-// covers the cell range [r0, r1): r0 = its first cell (0 for the first
-// wave), r1 = the next wave's first cell (N after the last fluid cell); the
-// cells of the range that are not the wave's own are solid.  Writing them
-// right after the fluid cells completes each line of the fields within one
-// wave, so L2 merges it before write-back (a separate pass leaves every line
-// that mixes fluid and solid cells to be written in two parts).  Called by
-// every work-item of a wave with i0 < nf, blocks one-dimensional.
+// Fields output of a compact step, written by waves in cell order.  The wave
+// of fluid cells i0 .. i0 + 63 covers the cell range [r0, r1): r0 = its
+// first cell (0 for the first wave), r1 = the next wave's first cell (N
+// after the last fluid cell); the cells of the range that are not the
+// wave's own are solid and get zeros.  The wave writes the range in chunks
+// of 64 consecutive cells: each lane takes one cell and the values of a
+// fluid one come from the lane that computed them (the k-th fluid cell of
+// the range is the wave's k-th), so every store covers whole lines instead
+// of scattering the fluid cells and patching the solid ones around them.
+// fo: the lane's own density and velocity.  Called by every work-item of a
+// wave with i0 < nf, blocks one-dimensional.
 template <typename T>
-__device__ __forceinline__ void zero_solid_range(const MomOut<T>& mo, const uint32_t* __restrict__ cellid,
-                                                 uint32_t nf, uint32_t i0)
+__device__ __forceinline__ void write_fields_range(const MomOut<T>& mo, const uint32_t* __restrict__ cellid,
+                                                   uint32_t nf, uint32_t i0, const T (&fo)[4])
 {
-    if (mo.mask == nullptr) return;
-    const uint64_t lane = threadIdx.x & 63u;
+    const uint32_t lane = threadIdx.x & 63u;
     const uint64_t r0 = i0 == 0 ? 0 : cellid[i0];
     const uint64_t r1 = i0 + 64u < nf ? cellid[i0 + 64u] : mo.n;
-    for (uint64_t c = r0 + lane; c < r1; c += 64)
-        if (mo.mask[c] != 0) write_moments(mo, c, T(0), T(0), T(0), T(0));
+    uint32_t before = 0;  // the wave's fluid cells ahead of this chunk
+    for (uint64_t c0 = r0; c0 < r1; c0 += 64) {
+        const uint64_t c = c0 + lane;
+        const bool in = c < r1;
+        const bool fluid = in && (mo.mask == nullptr || mo.mask[c] == 0);
+        const uint64_t bal = __ballot(fluid);
+        const int src = (int)((before + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull))) & 63u);
+        const T rho = __shfl(fo[0], src, 64), ux = __shfl(fo[1], src, 64);
+        const T uy = __shfl(fo[2], src, 64), uz = __shfl(fo[3], src, 64);
+        if (in) write_moments(mo, c, fluid ? rho : T(0), fluid ? ux : T(0), fluid ? uy : T(0), fluid ? uz : T(0));
+        before += (uint32_t)__popcll(bal);
+    }
 }
 
 // Gather step over the fluid cells, one work-item per fluid cell: the
@@ -375,8 +386,7 @@ __device__ __forceinline__ void zero_solid_range(const MomOut<T>& mo, const uint
 // other cases registers).
 template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
 __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restrict__ b, const CompactGeom& g,
-                                                  const Phys<T>& p, const MomOut<T>& mo, uint32_t i,
-                                                  double (&acc)[6])
+                                                  const Phys<T>& p, uint32_t i, double (&acc)[6], T (&fo)[4])
 {
     const uint32_t sb = g.s * (uint32_t)sizeof(T);  // bytes per plane; 2 sb < 2^32 (host check)
     const uint32_t own0 = i * (uint32_t)sizeof(T);  // own slot in sub-plane 0 / 1 of a block
@@ -403,7 +413,12 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
 #pragma unroll
         for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(B, pair_of(q), sb), sub_of(q) ? own1 : own0, f[q]);
         if constexpr (MEX) add_links_mask(acc, f, bm, wm);
-        if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
+        if constexpr (OUT) {
+            fo[0] = rho;
+            fo[1] = ux;
+            fo[2] = uy;
+            fo[3] = uz;
+        }
     } else {
         // slot of direction d: (d, x + c_d), or (opp d, x) if x + c_d is solid.
         // The odd step reads f_{opp d} from it and writes f*_d into it.
@@ -416,7 +431,12 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
         if constexpr (OPEN) apply_open_nb(f, nb, p);
         T rho, ux, uy, uz;
         collide<T, FORCE>(f, p, rho, ux, uy, uz);
-        if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
+        if constexpr (OUT) {
+            fo[0] = rho;
+            fo[1] = ux;
+            fo[2] = uy;
+            fo[3] = uz;
+        }
         // (with open faces f changes before the stores: sum the links first)
         if constexpr (MEX && OPEN) add_links_mask(acc, f, bm, wm);
         // beyond an open face, f*_d leaves the box and the own slot (opp d, x)
@@ -439,16 +459,18 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
     const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
     const uint32_t i = wg * kGatherThreads + threadIdx.x;
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    T fo[4];  // the fields of the OUT instances
     if constexpr (OUT) {
         static_assert(!MEX, "no fields output in a momentum-exchange step");
-        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, true, false>(a, b, g, p, mo, i, acc);
+        fo[0] = fo[1] = fo[2] = fo[3] = T(0);
+        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, true, false>(a, b, g, p, i, acc, fo);
         const uint32_t i0 = i - (threadIdx.x & 63u);
-        if (i0 < g.nf) zero_solid_range(mo, g.cellid, g.nf, i0);
+        if (i0 < g.nf) write_fields_range(mo, g.cellid, g.nf, i0, fo);
     } else if constexpr (!MEX) {
         if (i >= g.nf) return;
-        step_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, b, g, p, mo, i, acc);
+        step_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, b, g, p, i, acc, fo);
     } else {
-        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, b, g, p, mo, i, acc);
+        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, b, g, p, i, acc, fo);
         if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
             block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
     }
@@ -461,7 +483,7 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
 // neighbour side goes to the packed bounce-back region instead.
 template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
 __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const CompactGeom& g, const Phys<T>& p,
-                                                 const MomOut<T>& mo, uint32_t i, double (&acc)[6])
+                                                 uint32_t i, double (&acc)[6], T (&fo)[4])
 {
     constexpr uint32_t P = K == kEsoOdd ? 1u : 0u;
     const uint32_t sb = g.s * (uint32_t)sizeof(T);
@@ -500,7 +522,12 @@ __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const Compac
         st_at<false>(pair_block(A, k, sb), own_off[k], f[opp(k)]);  // f*_opp(k) streams to x - c_k
     }
     st_at<false>(rest, own, f[9]);
-    if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
+    if constexpr (OUT) {
+            fo[0] = rho;
+            fo[1] = ux;
+            fo[2] = uy;
+            fo[3] = uz;
+        }
     if constexpr (MEX) add_links_mask(acc, f, bm, wm);
 }
 
@@ -512,16 +539,18 @@ __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restri
     const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
     const uint32_t i = wg * kGatherThreads + threadIdx.x;
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    T fo[4];  // the fields of the OUT instances
     if constexpr (OUT) {
         static_assert(!MEX, "no fields output in a momentum-exchange step");
-        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, true, false>(a, g, p, mo, i, acc);
+        fo[0] = fo[1] = fo[2] = fo[3] = T(0);
+        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, true, false>(a, g, p, i, acc, fo);
         const uint32_t i0 = i - (threadIdx.x & 63u);
-        if (i0 < g.nf) zero_solid_range(mo, g.cellid, g.nf, i0);
+        if (i0 < g.nf) write_fields_range(mo, g.cellid, g.nf, i0, fo);
     } else if constexpr (!MEX) {
         if (i >= g.nf) return;
-        eso_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, mo, i, acc);
+        eso_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, i, acc, fo);
     } else {
-        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, g, p, mo, i, acc);
+        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, g, p, i, acc, fo);
         if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
             block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
     }
@@ -534,7 +563,7 @@ __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restri
 // link only selects the other sub-plane at the same location.
 template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
 __device__ __forceinline__ void twist_compact_cell(T* __restrict__ a, const CompactGeom& g, const Phys<T>& p,
-                                                   const MomOut<T>& mo, uint32_t i, double (&acc)[6])
+                                                   uint32_t i, double (&acc)[6], T (&fo)[4])
 {
     constexpr int P = K == kTwOdd ? 1 : 0;
     const uint32_t sb = g.s * (uint32_t)sizeof(T);
@@ -563,7 +592,12 @@ __device__ __forceinline__ void twist_compact_cell(T* __restrict__ a, const Comp
     if constexpr (OPEN) apply_open_nb(f, nb, p);
     T rho, ux, uy, uz;
     collide<T, FORCE>(f, p, rho, ux, uy, uz);
-    if constexpr (OUT) write_moments(mo, g.cellid[i], rho, ux, uy, uz);
+    if constexpr (OUT) {
+            fo[0] = rho;
+            fo[1] = ux;
+            fo[2] = uy;
+            fo[3] = uz;
+        }
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
         // where f_opp(q) was read (x + c-_q, plane opp q at P = 0, q at P = 1),
@@ -586,16 +620,18 @@ __global__ void __launch_bounds__(kGatherThreads) twist_compact_kernel(T* __rest
     const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
     const uint32_t i = wg * kGatherThreads + threadIdx.x;
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    T fo[4];  // the fields of the OUT instances
     if constexpr (OUT) {
         static_assert(!MEX, "no fields output in a momentum-exchange step");
-        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, true, false>(a, g, p, mo, i, acc);
+        fo[0] = fo[1] = fo[2] = fo[3] = T(0);
+        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, true, false>(a, g, p, i, acc, fo);
         const uint32_t i0 = i - (threadIdx.x & 63u);
-        if (i0 < g.nf) zero_solid_range(mo, g.cellid, g.nf, i0);
+        if (i0 < g.nf) write_fields_range(mo, g.cellid, g.nf, i0, fo);
     } else if constexpr (!MEX) {
         if (i >= g.nf) return;
-        twist_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, mo, i, acc);
+        twist_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, i, acc, fo);
     } else {
-        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, g, p, mo, i, acc);
+        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, g, p, i, acc, fo);
         if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
             block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
     }
@@ -623,16 +659,13 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_kernel(T* __restric
         f[q] = __builtin_nontemporal_load((const T*)(pair_block(A, pair_of(q), sb) + (sub_of(q) ? own1 : own0)));
     T rho, ux, uy, uz;
     collide<T, FORCE>(f, p, rho, ux, uy, uz);
-    // (the fields before the populations: 4% faster than after them, though
-    // that holds more registers)
-    if constexpr (OUT)
-        if (i < nf) write_moments(mo, cellid[i], rho, ux, uy, uz);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) st_at<true>(pair_block(A, pair_of(q), sb), sub_of(opp(q)) ? own1 : own0, f[q]);
     if constexpr (OUT) {
         // s is a multiple of 64: the whole wave is still here
+        const T fo[4] = {rho, ux, uy, uz};
         const uint32_t i0 = i - (threadIdx.x & 63u);
-        if (i0 < nf) zero_solid_range(mo, cellid, nf, i0);
+        if (i0 < nf) write_fields_range(mo, cellid, nf, i0, fo);
     }
 }
 
