@@ -39,7 +39,7 @@ def _golden_tgv():
     return {int(t): (float(k), float(m)) for t, k, m in rows}
 
 
-@pytest.mark.parametrize("scheme", ["aa", "ab"])
+@pytest.mark.parametrize("scheme", ["aa", "ab", "eso", "twist"])
 def test_taylor_green_128_decay_and_mass(scheme):
     """128^3 periodic, u0 = 0.04, tau = 0.6, 1000 steps."""
     need_gpu()
@@ -79,7 +79,7 @@ def _channel(scheme, steps):
     return uz, u, exact, nu, g, H, tau
 
 
-@pytest.mark.parametrize("scheme", ["aa", "ab"])
+@pytest.mark.parametrize("scheme", ["aa", "ab", "eso", "twist"])
 def test_poiseuille_channel_fp64(scheme):
     """64 x 64 x 256 fp64 channel, walls beyond y = 0 and y = 63, g = 1e-6 along z."""
     need_gpu()
