@@ -169,7 +169,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if args.steps < 2 or args.steps % 2:
         raise SystemExit("--steps must be even and >= 2 (the in-place scheme alternates two kernels)")
