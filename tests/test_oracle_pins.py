@@ -126,6 +126,67 @@ def test_guo_term_moments():
         np.testing.assert_allclose(c.T.astype(float) @ g, (1 - omega / 2) * F, rtol=1e-13, atol=1e-19)
 
 
+@pytest.mark.parametrize("omega", [0.0, 1.0 / 0.7, 1.0 / 0.55, 1.9])
+@pytest.mark.parametrize("u,F", [((0.03, -0.01, 0.02), (1e-3, -2e-3, 5e-4)),
+                                 ((-0.07, 0.11, 0.05), (2e-4, 3e-4, -7e-4)),
+                                 ((0.2, 0.15, -0.12), (-1e-2, 4e-3, 6e-3))])
+def test_guo_term_higher_moments(omega, u, F):
+    # Guo, Zheng and Shi choose the forcing term so that its velocity moments
+    # are those of the force acting on the Maxwellian up to second order:
+    #   sum_q F_q c_a c_b     = (1 - omega/2) (u_a F_b + u_b F_a),
+    #   sum_q F_q c_a c_b c_c = (1 - omega/2) (F_a d_bc + F_b d_ac + F_c d_ab) / 3.
+    # The second moment is where the velocity-dependent parts -3 u.F and
+    # 9 (c.u)(c.F) act; the simple forcing 3 w c.F, or either velocity part
+    # with a wrong sign or factor, fails it.
+    c, _, _ = oracle.lattice()
+    u, F = np.array(u), np.array(F)
+    g = oracle.guo_term(omega, u, F)
+    cf = c.astype(np.float64)
+    k = 1 - omega / 2
+    scale = max(abs(k), 1e-300) * np.max(np.abs(F))
+    second = np.einsum("qa,qb,q->ab", cf, cf, g)
+    np.testing.assert_allclose(second, k * (np.outer(u, F) + np.outer(F, u)), rtol=0, atol=1e-15 * scale)
+    third = np.einsum("qa,qb,qc,q->abc", cf, cf, cf, g)
+    d = np.eye(3)
+    want = k / 3 * (np.einsum("a,bc->abc", F, d) + np.einsum("b,ac->abc", F, d) + np.einsum("c,ab->abc", F, d))
+    np.testing.assert_allclose(third, want, rtol=0, atol=1e-15 * scale)
+
+
+def test_guo_term_is_second_order_hermite_projection():
+    # the term lies in the span of w_q, w_q c_q and w_q c_q c_q (a polynomial
+    # of degree two in c times the weight); with its moments up to second
+    # order (pinned above) that determines it uniquely.  Solve for the ten
+    # coefficients by least squares on exact integer design rows and demand a
+    # zero residual.
+    c, w, _ = oracle.lattice()
+    cf = c.astype(np.float64)
+    rows = [np.ones(19)] + [cf[:, a] for a in range(3)]
+    rows += [cf[:, a] * cf[:, b] for a in range(3) for b in range(a, 3)]
+    A = np.stack(rows, axis=1) * w[:, None]
+    rng = np.random.default_rng(17)
+    for _ in range(20):
+        u = rng.uniform(-0.15, 0.15, 3)
+        F = rng.uniform(-1e-3, 1e-3, 3)
+        omega = rng.uniform(0.0, 1.95)
+        g = oracle.guo_term(omega, u, F)
+        coef, *_ = np.linalg.lstsq(A, g, rcond=None)
+        assert np.max(np.abs(A @ coef - g)) <= 1e-17
+        # and the coefficients are the Hermite ones: 3 F (degree 1),
+        # 9/2 (u_a F_b + u_b F_a) on (c_a c_b - d_ab / 3) (degree 2)
+        k = 1 - omega / 2
+        want = np.zeros(10)
+        want[1:4] = 3 * k * F
+        i = 4
+        for a in range(3):
+            for b in range(a, 3):
+                s = 9 / 2 * (u[a] * F[b] + u[b] * F[a]) * k
+                want[i] = s if a == b else 2 * s
+                if a == b:
+                    want[0] -= s / 3
+                i += 1
+        np.testing.assert_allclose(coef, want, rtol=0, atol=1e-15)
+
+
 # ------------------------------------------------------ P3 conservation
 
 def _random_state(box, seed=3, mask=None):
@@ -686,14 +747,36 @@ def test_taylor_green_low_amplitude_decay():
 
 # ------------------------------------------------- consistency of helpers
 
-def test_step_cells_equals_run():
-    box = oracle.Box(6, 5, 7, periodic=(1, 0, 1), tau=0.7, force=(2e-5, 0, -1e-5))
+_STEP_CELLS_FACES = [
+    None,
+    {"-y": (1.01, (0.0, 0.02, 0.01)), "+y": (0.99, (0.01, 0.0, -0.02))},
+    {"-y": (1.0, (0.0, 0.03, 0.0), "zou_he_velocity"), "+y": (0.995, (0.0, 0.0, 0.0), "zou_he_pressure")},
+    {"-y": (1.0, (0.01, 0.02, 0.0), "neumann"), "+y": (1.0, (0.0, 0.0, 0.0), "zou_he_pressure")},
+    {"-y": (1.02, (0.0, 0.0, 0.0), "zou_he_pressure"), "+y": (1.0, (0.0, -0.01, 0.01), "zou_he_velocity")},
+    {"+y": (1.0, (0.0, 0.0, 0.0), "neumann")},
+]
+
+
+@pytest.mark.parametrize("faces", _STEP_CELLS_FACES)
+def test_step_cells_equals_run(faces):
+    # one step evaluated cell by cell (the checker of the full-size sampled
+    # GPU steps) equals the whole-box step, with walls, solids, a body force
+    # and open faces of every kind (reservoirs, Zou-He, Neumann); the face
+    # rules read the inward cell's new state, which step_cells recomputes
+    box = oracle.Box(6, 5, 7, periodic=(1, 0, 1), tau=0.7, force=(2e-5, 0, -1e-5), open_faces=faces)
     mask = li.random_mask(6, 5, 7, fraction=0.2, seed=8)
-    f0 = _random_state(box, seed=6, mask=mask)
+    rho, u = li.random_fields(6, 5, 7, seed=6, drho=0.02, du=0.04)
+    f0 = oracle.init_equilibrium(box, mask, rho, u)
+    rng = np.random.default_rng(6)
+    f0 = f0 * (1.0 + 0.05 * rng.standard_normal(f0.shape))
+    f0[:, mask.reshape(-1) != 0] = 0.0
     f1 = oracle.run(box, f0, 1, mask)
     cells = np.arange(box.n)
     got = oracle.step_cells(box, f0, cells, mask)
     assert np.array_equal(got.T, f1)
+    # a random subset, in random order, gives the same rows
+    sub = rng.permutation(box.n)[:57]
+    assert np.array_equal(oracle.step_cells(box, f0, sub, mask), f1[:, sub].T)
 
 
 def test_moments_and_totals_are_plain_sums():
