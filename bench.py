@@ -11,11 +11,18 @@ along +x, fp32, one-lattice AA scheme, fluid-compacted SoA layout (populations o
 fluid cells only).  Inputs are resident in HBM
 before timing starts.  Prints ONE JSON line.
 
-value = MLUPS over all cells (cells x steps / seconds / 1e6).
+value = MLUPS over all cells (cells x steps / seconds / 1e6) over the K timed
+steps.  The timed region is cut into `reps` equal segments (10 by default,
+each an even number of steps) with HIP events between them; `reps_mlups`
+gives the median, minimum and maximum over the segments (the PortLBM page's
+Results section reports the median of 10 runs with their range).
 roofline: the dominant kernel's algorithmic bytes per launch (152 B per fluid
 cell for fp32, 304 B for fp64, + 1 B per cell for the mask) over its mean
-launch time from HIP events on the launch stream, against 8 TB/s.
-cpu_baseline: the fp64 CPU oracle, single-threaded, on three steps of the same box.
+launch time from HIP events on the launch stream, against 8 TB/s; also
+against the measured ceilings of two probe kernels (libprobes.so): a float4
+copy and the 19-plane in-place swap of the AA even step without arithmetic.
+cpu_baseline: the fp64 CPU oracle, single-threaded, on three steps of the same
+box; also the 32^3 seeded case in full (100 steps).
 """
 import argparse
 import hashlib
@@ -88,7 +95,7 @@ def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lattice_boltzmann_cfd_d3q19_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
-        if fn.endswith((".hip", ".hpp", ".cpp")):
+        if fn.endswith((".hip", ".hpp", ".cpp")) and fn != "probes.hip":
             h.update(fn.encode())
             h.update(open(os.path.join(csrc, fn), "rb").read())
     return h.hexdigest()[:16]
@@ -128,9 +135,7 @@ def state_check(rho, u, mask=None):
     return finite, bounded
 
 
-def cpu_baseline(wl, steps=3):
-    """Time the single-threaded fp64 oracle on a few steps of the same box."""
-    import numpy as np
+def _oracle_mlups(wl, steps):
     import oracle
     box = oracle.Box(*wl["shape"], periodic=wl["periodic"], tau=wl["tau"], force=wl["force"],
                      open_faces=wl.get("open_faces"))
@@ -139,21 +144,90 @@ def cpu_baseline(wl, steps=3):
     f = oracle.run(box, f, steps, wl["mask"])
     dt = time.perf_counter() - t0
     del f
-    n = box.n
-    return {"value": round(n * steps / dt / 1e6, 3), "unit": "MLUPS", "cores": 1, "kind": "oracle",
+    return box.n * steps / dt / 1e6, dt
+
+
+def cpu_baseline(wl, steps=3):
+    """Time the single-threaded fp64 oracle on a few steps of the same box,
+    and on the 32^3 seeded case in full."""
+    value, dt = _oracle_mlups(wl, steps)
+    c1, dt1 = _oracle_mlups(workload("random32"), 100)
+    return {"value": round(value, 3), "unit": "MLUPS", "cores": 1, "kind": "oracle",
             "sample": f"{steps} steps of the full {'x'.join(map(str, wl['shape']))} box, fp64, "
                       f"single thread, {dt:.1f} s",
+            "c1_32cubed_100_steps": {"value": round(c1, 3), "unit": "MLUPS", "seconds": round(dt1, 2)},
             "host_cpu": _cpu_model(), "host_threads": os.cpu_count()}
 
 
 def _cpu_model():
+    """Model name as /proc/cpuinfo gives it, with family, model and stepping
+    (a virtualised host may print only the vendor's series name)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                info.setdefault(k.strip(), v.strip())
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    extra = [f"{info['cpu MHz']} MHz"] if "cpu MHz" in info else []
+    extra += [f"cache {info['cache size']}"] if "cache size" in info else []
+    return f"{name} ({', '.join(ids + extra)})" if ids or extra else name
+
+
+def probe_ceilings(n_cells, reps=20):
+    """Bandwidth (GB/s, bytes read + written) of the two probe kernels on the
+    launch stream: a float4 copy of 1 GiB and the 19-plane in-place swap over
+    n_cells cells; the better of plain and nontemporal accesses for each."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "lattice_boltzmann_cfd_d3q19_amd", "libprobes.so"))
+    lib.probe_copy_f4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_swap19.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def timed(fn, nbytes):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed: hip error {rc}")
+
+    out = {}
+    src = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    n4 = src.numel() // 4
+    out["copy_float4_GBps"] = max(
+        timed(lambda nt=nt: check(lib.probe_copy_f4(src.data_ptr(), dst.data_ptr(), n4, nt, sp)), 2 * n4 * 16)
+        for nt in (0, 1))
+    del src, dst
+    stride = (n_cells + 63) // 64 * 64
+    buf = torch.zeros(19 * stride, dtype=torch.float32, device="cuda")
+    out["swap19_inplace_GBps"] = max(
+        timed(lambda nt=nt: check(lib.probe_swap19(buf.data_ptr(), stride, n_cells, nt, sp)), 2 * 19 * 4 * n_cells)
+        for nt in (0, 1))
+    del buf
+    out["swap19_cells"] = n_cells
+    return {k: (round(v, 1) if isinstance(v, float) else v) for k, v in out.items()}
+
+
+def segments(steps, want=10):
+    """Largest r <= want that cuts `steps` into r equal even segments."""
+    for r in range(min(want, steps // 2), 0, -1):
+        if steps % r == 0 and (steps // r) % 2 == 0:
+            return r
+    return 1
 
 
 def main():
@@ -166,6 +240,7 @@ def main():
     ap.add_argument("--layout", default="compact", choices=["stream", "bundle", "collision", "compact"])
     ap.add_argument("--per-kernel-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reps", type=int, default=10, help="segments of the timed region (median, min, max)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -199,17 +274,22 @@ def main():
     lat.step(args.warmup if args.warmup % 2 == 0 else args.warmup + 1)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # timed region: exactly K steps, in `reps` equal segments between HIP
+    # events on the launch stream
+    reps = segments(args.steps, args.reps)
+    seg = args.steps // reps
+    evs_t = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
-    ev0.record(stream)
-    lat.step(args.steps)
-    ev1.record(stream)
+    evs_t[0].record(stream)
+    for r in range(reps):
+        lat.step(seg)
+        evs_t[r + 1].record(stream)
     torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
+    seg_ms = [evs_t[r].elapsed_time(evs_t[r + 1]) for r in range(reps)]
+    ms_total = evs_t[0].elapsed_time(evs_t[reps])
     sec = ms_total / 1e3
     mlups = n * args.steps / sec / 1e6
+    seg_mlups = sorted(n * seg / (m / 1e3) / 1e6 for m in seg_ms)
 
     # per-kernel launch durations (events around single steps on the launch stream)
     per = {}
@@ -244,6 +324,9 @@ def main():
     torch.cuda.synchronize()
     finite, bounded = state_check(rho, u, mask)
     del rho, u
+
+    # measured ceilings: the probe kernels
+    ceilings = probe_ceilings(n_fluid)
 
     # plain copy reference (torch copy kernel, 2 GiB moved)
     src = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
@@ -285,9 +368,17 @@ def main():
                      "traffic": None if traffic is None else int(traffic),
                      "traffic_over_alg": None if traffic is None else round(traffic / alg_bytes, 4),
                      "kernel": dominant, "alg_bytes_per_launch": alg_bytes,
-                     "kernel_ms": {k: round(v, 5) for k, v in per_ms.items()}},
+                     "kernel_ms": {k: round(v, 5) for k, v in per_ms.items()},
+                     "frac_of_copy_float4": round(achieved / ceilings["copy_float4_GBps"], 4),
+                     "frac_of_swap19": round(achieved / ceilings["swap19_inplace_GBps"], 4)},
+        "reps": reps,
+        "steps_per_rep": seg,
+        "reps_mlups": {"median": round(float(np.median(seg_mlups)), 1), "min": round(seg_mlups[0], 1),
+                       "max": round(seg_mlups[-1], 1)},
         "mflups": round(n_fluid * args.steps / sec / 1e6, 1),
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "step_frac_of_copy_float4": round(step_gbps / ceilings["copy_float4_GBps"], 4),
+        **ceilings,
         "copy_GBps": round(copy_gbps, 1),
         "state_finite": finite,
         "state_bounded": bounded,

@@ -133,8 +133,11 @@ typedef struct lbm_sim lbm_sim; /* opaque handle (host memory only) */
 
 /* Size of one population buffer, 19 * N * sizeof(T) bytes (compact layout:
  * 19 * roundup(N, 64) * sizeof(T), room for an all-fluid box; 28 planes
- * instead of 19 for the compact esoteric pull), and how many the scheme
- * needs (2 for AB, 1 for AA and ESOPULL).  Host only; never touches the GPU. */
+ * instead of 19 for the compact esoteric pull; for the esoteric twist
+ * (nx+1)(ny+1)(nz+1) cells per plane instead of N, rounded up to 64 on the
+ * compact layout), and how many the scheme needs (2 for AB; 1 for AA,
+ * ESOPULL and ESOTWIST, the in-place schemes of PortLBM section 3.3).  Host
+ * only; never touches the GPU. */
 lbm_status lbm_buffer_bytes(const lbm_desc *desc, size_t *bytes_per_buffer, int32_t *n_buffers);
 
 /* Device workspace the layout needs for geometry tables: 0 for the dense
@@ -142,7 +145,10 @@ lbm_status lbm_buffer_bytes(const lbm_desc *desc, size_t *bytes_per_buffer, int3
  * one halo layer plus 8 bytes per cell (index tables).  Host only. */
 lbm_status lbm_workspace_bytes(const lbm_desc *desc, size_t *bytes);
 
-/* Create a handle over caller-owned population memory.
+/* Create a handle over caller-owned population memory: one lattice of 19
+ * populations per cell for the in-place schemes, two for the two-lattice
+ * pull (PortLBM section 3.3, Eq. 3, and its four algorithms; fieldcraft
+ * page, first section: one buffer in place against two buffers).
  *   buf0, buf1   device buffers of lbm_buffer_bytes() bytes each, 256-byte
  *                aligned.  AB needs both (distinct, not overlapping); AA
  *                takes buf0 and requires buf1 == NULL.
@@ -220,7 +226,9 @@ typedef enum {
  * their axis.  Host only. */
 lbm_status lbm_set_open_faces(lbm_sim *sim, const int32_t open[6], const double rho[6], const double u[18]);
 
-/* f(0) = equilibrium(rho, u) on fluid cells, 0 on solid cells; t := 0.
+/* f(0) = equilibrium(rho, u) on fluid cells, 0 on solid cells; t := 0.  The
+ * equilibrium is PortLBM section 3.1, Eq. 2 in its compressible form
+ * w_q rho (1 + 3 c_q.u + 9/2 (c_q.u)^2 - 3/2 u^2) with the D3Q19 weights.
  *   rho   device T[N] or NULL (rho = 1).
  *   u     device T[3][N] (component-major) or NULL (u = 0).
  * AB stores the streaming pre-image of f(0) in buf0, so that the first fused
@@ -231,7 +239,14 @@ lbm_status lbm_set_open_faces(lbm_sim *sim, const int32_t open[6], const double 
 lbm_status lbm_init_equilibrium(lbm_sim *sim, const void *rho, const void *u);
 
 /* Advance n >= 0 time steps (one fused kernel launch each, plus one small
- * launch per open face of a NEUMANN or ZOU_HE kind); t += n. */
+ * launch per open face of a NEUMANN or ZOU_HE kind); t += n.  Each step is
+ * f(t+1) = S(C(f(t))): C is the BGK collision of PortLBM section 3.1, Eq. 1
+ * (relaxation with omega = 1/tau toward Eq. 2's equilibrium, plus the Guo
+ * forcing term (1 - omega/2) w_q [3 (c_q - u) + 9 (c_q.u) c_q] . F when a
+ * force is set), S the streaming of section 3.3, Eq. 3, with halfway
+ * bounce-back (section 3.1, last paragraph); gather and scatter follow the
+ * scheme's address rule (fieldcraft page, first section, for AA).
+ * LBM_ERR_INVALID_ARGUMENT for n < 0; LBM_ERR_BAD_STATE before init. */
 lbm_status lbm_step(lbm_sim *sim, int64_t n);
 
 /* Advance n >= 1 time steps like lbm_step; the last step also writes the
@@ -243,12 +258,19 @@ lbm_status lbm_step(lbm_sim *sim, int64_t n);
  *   rho   device T[N], u device T[3][N] (component-major, u includes F/2);
  *         0 on solid cells.  The values equal what lbm_moments returns
  *         before the last step, bit for bit.
- * The compact layout first zeroes rho and u on the solid cells, then its step
- * writes the fluid cells.  LBM_ERR_INVALID_ARGUMENT for n < 1 or NULL
- * outputs. */
+ * On the compact layout each wave of the last step writes its whole range of
+ * box cells (from its first fluid cell to the next wave's) in chunks of 64
+ * consecutive cells: the fluid cells' values, moved by a cross-lane shuffle
+ * from the lanes that computed them, and zeros at the solid cells between
+ * them; the step's first and last waves also cover the solid cells before
+ * the first and after the last fluid cell.  Only a box without any fluid
+ * cell gets a separate pass that writes zeros.  LBM_ERR_INVALID_ARGUMENT for
+ * n < 1 or NULL outputs. */
 lbm_status lbm_step_moments(lbm_sim *sim, int64_t n, void *rho, void *u);
 
-/* Density and velocity of the canonical state f(t):
+/* Density and velocity of the canonical state f(t) (PortLBM section 3.1: the
+ * macroscopic velocity is the first moment of the populations; with Guo
+ * forcing it includes half the force):
  * rho = sum_q f_q, u = (sum_q c_q f_q + F/2) / rho; 0 on solid cells.
  *   rho   device T[N];   u   device T[3][N] (component-major). */
 lbm_status lbm_moments(lbm_sim *sim, void *rho, void *u);
@@ -306,7 +328,10 @@ lbm_status lbm_momentum_exchange(lbm_sim *sim, void *force, void *scratch, size_
  * Errors as lbm_momentum_exchange, and LBM_ERR_INVALID_ARGUMENT for n < 1. */
 lbm_status lbm_step_momentum_exchange(lbm_sim *sim, int64_t n, void *force, void *scratch, size_t scratch_bytes);
 
-/* Release the handle (host memory only); NULL is a no-op. */
+/* Release the handle (host memory only); NULL is a no-op.  The caller's
+ * population buffers, workspace and mask are not freed (the caller owns all
+ * device memory, as lbm_create states); no GPU work is enqueued, so the
+ * caller may free them once the stream's enqueued steps have completed. */
 lbm_status lbm_destroy(lbm_sim *sim);
 
 /* Current time step t, or -1 for a NULL handle. */

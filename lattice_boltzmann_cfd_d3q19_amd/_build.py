@@ -4,6 +4,8 @@
 
 Each translation unit is compiled to an object in parallel, then linked into
 lattice_boltzmann_cfd_d3q19_amd/liblbm.so (in-tree, next to the binding).
+The bandwidth probes the benchmark compares against (csrc/probes.hip) go
+into a library of their own, libprobes.so, which the lattice never loads.
 Floating-point contraction is off so the collision arithmetic is fixed by the
 source (every layout and scheme then agrees bit for bit); packed fp32
 instructions are disabled.
@@ -19,7 +21,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblbm.so")
+PROBES_LIB = os.path.join(HERE, "libprobes.so")
 SOURCES = ["launch_f32.hip", "launch_f64.hip", "compact_build.hip", "capi.cpp"]
+PROBE_SOURCES = ["probes.hip"]
 ARCH = os.environ.get("LBM_OFFLOAD_ARCH", "gfx950")
 
 
@@ -50,15 +54,22 @@ def _compile(src, verbose, defines=()):
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, defines), SOURCES))
+def _link(objs, out, verbose):
     cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", out + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False, out: str = LIB, defines=(), probes: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + (PROBE_SOURCES if probes else [])
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose, defines), srcs)))
+    _link([objs[s] for s in SOURCES], out, verbose)
+    if probes:
+        _link([objs[s] for s in PROBE_SOURCES], PROBES_LIB, verbose)
     return out
 
 

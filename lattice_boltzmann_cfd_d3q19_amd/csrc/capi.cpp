@@ -14,7 +14,13 @@
 //   ESOPULL: the single buffer holds f(t) in the slots of the esoteric pull
 //       of parity t % 2 (each pair's own-cell and neighbour slots swap roles
 //       every step).
-// Either way the values are stored shifted by the lattice weights (f - w).
+//   ESOTWIST: the single buffer holds f(t) in the slots of the esoteric twist
+//       of parity t % 2: f_q(x) at the location x - max(c_q, 0), in plane q
+//       when t is even and plane opposite(q) when t is odd (dense layouts: a
+//       halo layer below each low face; compact layout: ghost cells after the
+//       fluid ones).
+// In every scheme the values are stored shifted by the lattice weights
+// (f - w).
 #include <hip/hip_runtime.h>
 
 #include <cmath>

@@ -205,13 +205,20 @@ def test_checkpoint_resume_bit_exact():
 
 # ----------------------------------- full-size boxes: sampled one-step checks
 
-def _sample_cells(mask, n, k, seed):
+def _sample_cells(mask, shape, k, seed):
     rng = np.random.default_rng(seed)
+    n = int(np.prod(shape))
     cells = rng.choice(n, size=min(k, n), replace=False)
     if mask is not None:
-        # add fluid cells touching a solid (where bounce-back acts)
-        m = mask.astype(bool)
-        near = np.nonzero(~m & (np.roll(m, 1) | np.roll(m, -1)))[0]
+        # add fluid cells with a solid cell at one of the 18 lattice offsets
+        # (where bounce-back acts), periodic wrap on the 3-D mask
+        nx, ny, nz = shape
+        m = mask.astype(bool).reshape(nz, ny, nx)
+        hit = np.zeros_like(m)
+        for dz, dy, dx in [(dz, dy, dx) for dz in (-1, 0, 1) for dy in (-1, 0, 1) for dx in (-1, 0, 1)
+                           if 0 < dx * dx + dy * dy + dz * dz <= 2]:
+            hit |= np.roll(m, (dz, dy, dx), axis=(0, 1, 2))
+        near = np.nonzero((hit & ~m).reshape(-1))[0]
         if near.size:
             cells = np.concatenate([cells, rng.choice(near, size=min(2048, near.size), replace=False)])
     return np.unique(cells).astype(np.int64)
@@ -253,7 +260,7 @@ def test_full_size_sampled_steps(name, layout, scheme):
                rho=cast(rho, prec), u=cast(u, prec))
     box = oracle.Box(*shape, periodic=per, tau=tau, force=F)
     n = int(np.prod(shape))
-    cells = _sample_cells(mask, n, 4096, seed=sum(name.encode()))
+    cells = _sample_cells(mask, shape, 4096, seed=sum(name.encode()))
     lat.step(5)
     prev = host_f(lat)
     for _ in range(2):
@@ -404,7 +411,7 @@ def test_full_size_open_channel_sampled_steps(layout, scheme):
     lat.init(None, torch.from_numpy(u))
     box = oracle.Box(nx, ny, nz, periodic=(0, 0, 1), tau=tau, open_faces=faces)
     rng = np.random.default_rng(7)
-    cells = [_sample_cells(mask, n, 4096, seed=11)]
+    cells = [_sample_cells(mask, (nx, ny, nz), 4096, seed=11)]
     for x in (0, nx - 1):
         y = np.concatenate([rng.integers(0, ny, 600), [0, ny - 1] * 20])
         z = rng.integers(0, nz, y.size)
@@ -513,7 +520,7 @@ def test_full_size_512_sampled_steps(layout, scheme):
     say("full-size 512", layout, scheme)
     lat = make(shape, "f32", layout, scheme, tau=tau, force=F, mask=mask)
     box = oracle.Box(*shape, periodic=(1, 1, 1), tau=tau, force=F)
-    cells = _sample_cells(mask, n, 3000, seed=512)
+    cells = _sample_cells(mask, shape, 3000, seed=512)
     near = _neighbourhood(cells, shape)
     near_t = torch.from_numpy(near).cuda()
     cells_t = torch.from_numpy(cells).cuda()

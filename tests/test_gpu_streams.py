@@ -49,3 +49,33 @@ def test_two_streams_interleaved_equal_alone():
     for (shape, layout, scheme, _), a, b in zip(cfg, alone, outs):
         say("two streams", shape, layout, scheme)
         assert torch.equal(a, b), (layout, scheme)
+
+
+def test_handle_stream_differs_from_current_stream():
+    """The handle runs on its own stream while the caller stays on the default
+    stream: inputs made on the current stream, outputs read on it, and
+    temporaries freed right after each call must all be ordered (the binding
+    makes each stream wait for the other and records tensor use)."""
+    need_gpu()
+    shape, layout, scheme, seed = (40, 30, 20), "compact", "aa", 47
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ref = _lattice(shape, layout, scheme, s, seed)
+        ref.step(31)
+        want_f = ref.read_populations()
+        want_r, want_u = ref.moments()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    lat = _lattice(shape, layout, scheme, side, seed)      # called on the default stream
+    for _ in range(31):
+        lat.step(1)
+        junk = torch.empty(1 << 22, device="cuda").fill_(float("nan"))  # reuse freed blocks
+        del junk
+    f = lat.read_populations()
+    r, u = lat.moments()
+    f2 = f.clone()          # default-stream work that reads the outputs right away
+    r2, u2 = r.clone(), u.clone()
+    torch.cuda.synchronize()
+    say("handle on a side stream", shape, layout, scheme)
+    assert torch.equal(f2, want_f)
+    assert torch.equal(r2, want_r) and torch.equal(u2, want_u)
