@@ -328,6 +328,25 @@ lbm_status lbm_momentum_exchange(lbm_sim *sim, void *force, void *scratch, size_
  * Errors as lbm_momentum_exchange, and LBM_ERR_INVALID_ARGUMENT for n < 1. */
 lbm_status lbm_step_momentum_exchange(lbm_sim *sim, int64_t n, void *force, void *scratch, size_t scratch_bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * lbm_step_momentum_exchange without a scratch argument.  The partial rows
+ * live in a fixed array inside the library, LBM_STATIC_SCRATCH_BYTES per GPU,
+ * held by every GPU the library runs on until the process ends; the call
+ * allocates nothing.  Results and state equal those of
+ * lbm_step_momentum_exchange bit for bit.
+ *   force  device double[6], 8-byte aligned.
+ * LBM_ERR_UNSUPPORTED when lbm_momentum_exchange_scratch_bytes() of the
+ * handle's box exceeds LBM_STATIC_SCRATCH_BYTES (48 bytes per 256-cell tile
+ * of the box: a 256^3 box needs 3 MiB and fits, a 512^3 box does not);
+ * other errors as lbm_step_momentum_exchange.  Every call on one
+ * GPU uses that GPU's one array: calls that overlap in time on one GPU (two
+ * handles on two streams, or two host threads) race and give wrong forces;
+ * serialise them.  The first call on a device looks up the array's device
+ * address (hipGetSymbolAddress) with that device current. */
+#define LBM_STATIC_SCRATCH_BYTES ((size_t)4 << 20)
+lbm_status lbm_step_momentum_exchange_noalloc(lbm_sim *sim, int64_t n, void *force);
+
 /* Release the handle (host memory only); NULL is a no-op.  The caller's
  * population buffers, workspace and mask are not freed (the caller owns all
  * device memory, as lbm_create states); no GPU work is enqueued, so the

@@ -27,7 +27,8 @@ EXPORTED = ["lbm_buffer_bytes", "lbm_workspace_bytes", "lbm_create", "lbm_set_wo
             "lbm_moments", "lbm_read_populations", "lbm_write_populations", "lbm_save_state",
             "lbm_load_state", "lbm_destroy", "lbm_time", "lbm_fluid_cells", "lbm_last_hip_error",
             "lbm_status_string", "lbm_momentum_exchange_scratch_bytes", "lbm_momentum_exchange",
-            "lbm_set_open_faces", "lbm_step_moments", "lbm_step_momentum_exchange"]
+            "lbm_set_open_faces", "lbm_step_moments", "lbm_step_momentum_exchange",
+            "lbm_step_momentum_exchange_noalloc"]
 
 
 class lbm_desc(ctypes.Structure):
@@ -96,6 +97,8 @@ _lib.lbm_momentum_exchange.argtypes = [_vp, _vp, _vp, ctypes.c_size_t]
 _lib.lbm_momentum_exchange.restype = _st
 _lib.lbm_step_momentum_exchange.argtypes = [_vp, ctypes.c_int64, _vp, _vp, ctypes.c_size_t]
 _lib.lbm_step_momentum_exchange.restype = _st
+_lib.lbm_step_momentum_exchange_noalloc.argtypes = [_vp, ctypes.c_int64, _vp]
+_lib.lbm_step_momentum_exchange_noalloc.restype = _st
 _lib.lbm_destroy.argtypes = [_vp]
 _lib.lbm_destroy.restype = _st
 _lib.lbm_time.argtypes = [_vp]
@@ -233,6 +236,13 @@ def lbm_momentum_exchange(sim, force, scratch, nbytes):
 
 def lbm_step_momentum_exchange(sim, n, force, scratch, nbytes):
     return _lib.lbm_step_momentum_exchange(sim, int(n), _ptr(force), _ptr(scratch), int(nbytes))
+
+
+def lbm_step_momentum_exchange_noalloc(sim, n, force):
+    return _lib.lbm_step_momentum_exchange_noalloc(sim, int(n), _ptr(force))
+
+
+LBM_STATIC_SCRATCH_BYTES = 4 << 20
 
 
 def lbm_destroy(sim):

@@ -26,6 +26,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 
 #include "../../include/lbm.h"
@@ -57,6 +58,16 @@ struct lbm_sim {
     double face_rho[6];
     double face_u[6][3];
 };
+
+// Device scratch of lbm_step_momentum_exchange_noalloc: the per-workgroup
+// partial rows of the momentum-exchange sums (6 doubles per row), for callers
+// that cannot allocate.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device memory: its device address comes from hipGetSymbolAddress,
+// once per device (static_scratch below), and only that address is used.
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;  // 4 MiB: 87,381 rows
+static __device__ __align__(256) double scratch[kStaticScratchBytes / sizeof(double)];
+static_assert(kStaticScratchBytes == LBM_STATIC_SCRATCH_BYTES, "the header states the scratch size");
 
 namespace {
 
@@ -414,6 +425,34 @@ lbm_status lbm_init_equilibrium(lbm_sim* sim, const void* rho, const void* u)
 
 namespace {
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device dev: looked up on the first call for
+// that device, with that device current, and kept.  nullptr (and the HIP
+// error in *err) if the lookup fails.
+void* static_scratch(int dev, hipError_t* err)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] != nullptr) return g_scratch_ptr[dev];
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e == hipSuccess && prev != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (prev >= 0 && prev != dev) {
+        const hipError_t back = hipSetDevice(prev);
+        if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess || ptr == nullptr) {
+        *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+        return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+    return ptr;
+}
+
 // n steps; the last one also writes the density and velocity its collision
 // used into rho / u when they are given, or sums its momentum exchange into
 // force (partial: the scratch rows) when that is given.
@@ -494,6 +533,23 @@ lbm_status lbm_step_momentum_exchange(lbm_sim* sim, int64_t n, void* force, void
     if ((uintptr_t)scratch % kAlign != 0 || (uintptr_t)force % sizeof(double) != 0) return LBM_ERR_MISALIGNED;
     if (!sim->initialized) return LBM_ERR_BAD_STATE;
     return run_steps(sim, n, nullptr, nullptr, (double*)force, (double*)scratch);
+}
+
+lbm_status lbm_step_momentum_exchange_noalloc(lbm_sim* sim, int64_t n, void* force)
+{
+    if (sim == nullptr || n < 1 || force == nullptr) return LBM_ERR_INVALID_ARGUMENT;
+    if ((uintptr_t)force % sizeof(double) != 0) return LBM_ERR_MISALIGNED;
+    size_t need = 0;
+    lbm_momentum_exchange_scratch_bytes(&sim->d, &need);
+    if (need > kStaticScratchBytes) return LBM_ERR_UNSUPPORTED;
+    if (!sim->initialized) return LBM_ERR_BAD_STATE;
+    int dev = 0;
+    hipError_t e = sim->stream != nullptr ? hipStreamGetDevice(sim->stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(sim, e);
+    if (dev < 0 || dev >= kMaxDevices) return LBM_ERR_UNSUPPORTED;
+    void* ptr = static_scratch(dev, &e);
+    if (ptr == nullptr) return hip_status(sim, e);
+    return run_steps(sim, n, nullptr, nullptr, (double*)force, (double*)ptr);
 }
 
 lbm_status lbm_moments(lbm_sim* sim, void* rho, void* u)

@@ -210,6 +210,28 @@ def test_momentum_exchange_arguments_before_any_launch():
     assert capi.lbm_step_momentum_exchange(None, 1, FAKE, FAKE, nb) == capi.LBM_ERR_INVALID_ARGUMENT
 
 
+def test_noalloc_momentum_exchange_arguments_before_any_launch():
+    # the variant with the library's fixed scratch: the same argument rules,
+    # and boxes whose partial rows exceed the fixed size are refused up front
+    noalloc = capi.lbm_step_momentum_exchange_noalloc
+    assert noalloc(None, 1, FAKE) == capi.LBM_ERR_INVALID_ARGUMENT
+    for shape, fits in (((256, 256, 256), True), ((40, 8, 8), True), ((512, 512, 512), False),
+                        ((256, 256, 341), True), ((256, 256, 342), False)):
+        d = capi.make_desc(*shape)
+        st, nb = capi.lbm_momentum_exchange_scratch_bytes(d)
+        assert st == capi.LBM_OK and (nb <= capi.LBM_STATIC_SCRATCH_BYTES) == fits, (shape, nb)
+        st, h = capi.lbm_create(d, FAKE)
+        assert st == capi.LBM_OK
+        try:
+            assert noalloc(h, 0, FAKE) == capi.LBM_ERR_INVALID_ARGUMENT
+            assert noalloc(h, 1, None) == capi.LBM_ERR_INVALID_ARGUMENT
+            assert noalloc(h, 1, FAKE + 4) == capi.LBM_ERR_MISALIGNED
+            assert noalloc(h, 1, FAKE) == (capi.LBM_ERR_BAD_STATE if fits else capi.LBM_ERR_UNSUPPORTED)
+            assert capi.lbm_time(h) == 0
+        finally:
+            capi.lbm_destroy(h)
+
+
 def test_open_faces_arguments():
     st, h = capi.lbm_create(capi.make_desc(8, 8, 8), FAKE)
     assert st == capi.LBM_OK
