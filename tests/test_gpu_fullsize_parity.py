@@ -79,7 +79,7 @@ def _run_gpu(name, layout, scheme):
 
 @pytest.mark.parametrize("name,layout,scheme", [
     ("tgv128", "stream", "aa"), ("tgv128", "stream", "ab"), ("tgv128", "compact", "aa"),
-    ("tgv128", "collision", "ab"),
+    ("tgv128", "collision", "ab"), ("tgv128", "collision", "aa"), ("tgv128", "bundle", "aa"), ("tgv128", "bundle", "ab"),
     ("sphere128", "stream", "aa"), ("sphere128", "bundle", "aa"), ("sphere128", "collision", "aa"),
     ("sphere128", "compact", "aa"), ("sphere128", "stream", "ab"),
     ("channel_f64", "stream", "aa"), ("channel_f64", "stream", "ab"), ("channel_f64", "compact", "aa"),
