@@ -135,14 +135,26 @@ __device__ __forceinline__ T ld_pop_own(const T* p)
     }
 }
 
-template <typename T>
-__device__ __forceinline__ void st_pop(T* p, T v)
+// The AoS layout stores plain: each cache line of its records is written in
+// pieces by the cells of several rows, which the L2 merges only if the pieces
+// stay there (nontemporal stores measured 1.93 vs 1.71 ms for the odd
+// in-place step and 1.32 vs 0.93 ms for the pull on a periodic 256^3 box,
+// 0.84 vs 0.74 ms for the pull on the porous one; the other layouts lose
+// 3-25% with plain stores).
+template <int L>
+constexpr bool nt_store()
 {
-#if LBM_NT_STORE
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
+    return LBM_NT_STORE && L != kCollision;
+}
+
+template <int L, typename V>
+__device__ __forceinline__ void st_pop(V* p, V v)
+{
+    if constexpr (nt_store<L>()) {
+        __builtin_nontemporal_store(v, p);
+    } else {
+        *p = v;
+    }
 }
 
 // ----------------------------------------------------------- tile mapping
@@ -850,18 +862,18 @@ __device__ __forceinline__ void step_cell(T* __restrict__ a, T* __restrict__ b, 
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
         if constexpr (K == kAB) {
-            st_pop(slot<L>(b, n, q, c.id), f[q]);
+            st_pop<L>(slot<L>(b, n, q, c.id), f[q]);
         } else if constexpr (K == kAAEven) {
-            st_pop(slot<L>(a, n, opp(q), c.id), f[q]);
+            st_pop<L>(slot<L>(a, n, opp(q), c.id), f[q]);
         } else if constexpr (is_eso(K)) {
             // into the slot f_opp(q) was read from
-            st_pop(a + eso_off<K, L>(n, c, bits, obits, opp(q)), f[q]);
+            st_pop<L>(a + eso_off<K, L>(n, c, bits, obits, opp(q)), f[q]);
         } else if constexpr (is_twist(K)) {
             // where f_opp(q) was read from; bounced back (x + c_q solid or
             // beyond a wall: the upstream bit of opp q), the other plane there
             constexpr int P = K == kTwOdd ? 1 : 0;
             const uint64_t normal = twist_off<P, L>(g, c, opp(q)), back = twist_off<1 - P, L>(g, c, opp(q));
-            st_pop(a + (((bits >> opp(q)) & 1u) ? back : normal), f[q]);
+            st_pop<L>(a + (((bits >> opp(q)) & 1u) ? back : normal), f[q]);
         } else {
             // toward x + c_q, or straight back into (opp q, x) if that cell is
             // solid or beyond a wall (its upstream bit for opp q is set); if
@@ -871,7 +883,7 @@ __device__ __forceinline__ void step_cell(T* __restrict__ a, T* __restrict__ b, 
             const bool own_slot = ((bits | obits) >> opp(q)) & 1u;
             const uint64_t own = slot_off<L>(n, opp(q), c.id);
             const uint64_t far = slot_off<L>(n, q, nbr(c, kCx[q], kCy[q], kCz[q]));
-            st_pop(a + (own_slot ? own : far), f[q]);
+            st_pop<L>(a + (own_slot ? own : far), f[q]);
         }
     }
     if constexpr (MEX && !kMexEarly) add_links(acc, f, c, link_bounced);
@@ -901,7 +913,8 @@ __device__ __forceinline__ void step_cell(T* __restrict__ a, T* __restrict__ b, 
 // no-mask periodic instance), for the odd in-place step of both layouts and
 // the pull of the bundle layout (periodic 256^3, fp32, per launch: AoS odd
 // 2.114 -> 1.948 ms, SoAoS odd 0.515 -> 0.471 ms, SoAoS pull 0.458 -> 0.450
-// ms; the AoS pull lost, 1.315 -> 1.885 ms).  With solid cells every lane
+// ms).  The AoS pull is left out: with plain stores it went 0.930 -> 0.910
+// ms on the 256^3 box but 0.109 -> 0.117 ms at 128^3.  With solid cells every lane
 // must still load for its neighbours and the bounced links add own-record
 // accesses and per-slot stores: on the 256^3 porous box the AoS odd step
 // took 1.43 ms against 1.19 ms, the SoAoS one 0.80 against 0.59 ms.
@@ -927,16 +940,6 @@ struct Vec3 {
 typedef float f32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
 typedef double f64x2_a8 __attribute__((ext_vector_type(2), aligned(8)));
 
-template <typename V>
-__device__ __forceinline__ void st_nt(V* p, V v)
-{
-#if LBM_NT_STORE
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
-}
-
 template <typename T>
 __device__ __forceinline__ Vec3<T> ld3(const T* p)
 {
@@ -955,7 +958,7 @@ __device__ __forceinline__ Vec3<T> ld3(const T* p)
     return r;
 }
 
-template <typename T>
+template <int L, typename T>
 __device__ __forceinline__ void st3(T* p, Vec3<T> v)
 {
     if constexpr (sizeof(T) == 4) {
@@ -963,25 +966,25 @@ __device__ __forceinline__ void st3(T* p, Vec3<T> v)
         w.x = v.x;
         w.y = v.y;
         w.z = v.z;
-        st_nt((f32x3_a4*)p, w);
+        st_pop<L>((f32x3_a4*)p, w);
     } else {
         f64x2_a8 w;
         w.x = v.x;
         w.y = v.y;
-        st_nt((f64x2_a8*)p, w);
-        st_nt(p + 2, v.z);
+        st_pop<L>((f64x2_a8*)p, w);
+        st_pop<L>(p + 2, v.z);
     }
 }
 
 // two consecutive slots
-template <typename T>
+template <int L, typename T>
 __device__ __forceinline__ void st2(T* p, T a, T b)
 {
     typedef T v2 __attribute__((ext_vector_type(2), aligned(sizeof(T))));
     v2 w;
     w.x = a;
     w.y = b;
-    st_nt((v2*)p, w);
+    st_pop<L>((v2*)p, w);
 }
 
 // A row of three directions q0 = B, q1 = B + 1, q2 = B + 2 (c_x = -1, 0, +1);
@@ -1033,20 +1036,20 @@ __device__ __forceinline__ void scatter_row3_odd(T* __restrict__ a, const Geom& 
         w.x = w0;
         w.y = f[R::q1];
         w.z = w2;
-        st3(t, w);
+        st3<L>(t, w);
     } else {
         // a segment end: the slot whose writer lies beyond the segment is
         // that writer's, and this lane's value bound beyond the segment is
         // stored here
         if (!first) {
-            st2(t + 1, f[R::q1], w2);
+            st2<L>(t + 1, f[R::q1], w2);
         } else if (!last) {
-            st2(t, w0, f[R::q1]);
+            st2<L>(t, w0, f[R::q1]);
         } else {
-            st_pop(t + 1, f[R::q1]);
+            st_pop<L>(t + 1, f[R::q1]);
         }
-        if (first) st_pop(a + slot_off<L>(n, R::q0, nbr(c, -1, R::cy, R::cz)), f[R::q0]);
-        if (last) st_pop(a + slot_off<L>(n, R::q2, nbr(c, 1, R::cy, R::cz)), f[R::q2]);
+        if (first) st_pop<L>(a + slot_off<L>(n, R::q0, nbr(c, -1, R::cy, R::cz)), f[R::q0]);
+        if (last) st_pop<L>(a + slot_off<L>(n, R::q2, nbr(c, 1, R::cy, R::cz)), f[R::q2]);
     }
 }
 
@@ -1085,7 +1088,7 @@ __device__ __forceinline__ void step_cell_bundled(T* __restrict__ a, T* __restri
         w.x = f[B];                                         \
         w.y = f[B + 1];                                     \
         w.z = f[B + 2];                                     \
-        st3(b + slot_off<L>(n, B, c.id), w);                \
+        st3<L>(b + slot_off<L>(n, B, c.id), w);                \
     }
         LBM_AB_STORE3(1)
         LBM_AB_STORE3(5)
@@ -1093,20 +1096,20 @@ __device__ __forceinline__ void step_cell_bundled(T* __restrict__ a, T* __restri
         LBM_AB_STORE3(11)
         LBM_AB_STORE3(15)
 #undef LBM_AB_STORE3
-        st_pop(b + slot_off<L>(n, 0, c.id), f[0]);
-        st_pop(b + slot_off<L>(n, 4, c.id), f[4]);
-        st_pop(b + slot_off<L>(n, 14, c.id), f[14]);
-        st_pop(b + slot_off<L>(n, 18, c.id), f[18]);
+        st_pop<L>(b + slot_off<L>(n, 0, c.id), f[0]);
+        st_pop<L>(b + slot_off<L>(n, 4, c.id), f[4]);
+        st_pop<L>(b + slot_off<L>(n, 14, c.id), f[14]);
+        st_pop<L>(b + slot_off<L>(n, 18, c.id), f[18]);
     } else {
         scatter_row3_odd<1, L>(a, g, c, first, last, f);
         scatter_row3_odd<5, L>(a, g, c, first, last, f);
         scatter_row3_odd<8, L>(a, g, c, first, last, f);
         scatter_row3_odd<11, L>(a, g, c, first, last, f);
         scatter_row3_odd<15, L>(a, g, c, first, last, f);
-        st_pop(a + slot_off<L>(n, 0, nbr(c, kCx[0], kCy[0], kCz[0])), f[0]);
-        st_pop(a + slot_off<L>(n, 4, nbr(c, kCx[4], kCy[4], kCz[4])), f[4]);
-        st_pop(a + slot_off<L>(n, 14, nbr(c, kCx[14], kCy[14], kCz[14])), f[14]);
-        st_pop(a + slot_off<L>(n, 18, nbr(c, kCx[18], kCy[18], kCz[18])), f[18]);
+        st_pop<L>(a + slot_off<L>(n, 0, nbr(c, kCx[0], kCy[0], kCz[0])), f[0]);
+        st_pop<L>(a + slot_off<L>(n, 4, nbr(c, kCx[4], kCy[4], kCz[4])), f[4]);
+        st_pop<L>(a + slot_off<L>(n, 14, nbr(c, kCx[14], kCy[14], kCz[14])), f[14]);
+        st_pop<L>(a + slot_off<L>(n, 18, nbr(c, kCx[18], kCy[18], kCz[18])), f[18]);
     }
 }
 
