@@ -57,6 +57,7 @@ struct lbm_sim {
     int32_t face_kind[6]; // 0 closed, 1 reservoir, 2 Neumann, 3 Zou-He pressure, 4 Zou-He velocity
     double face_rho[6];
     double face_u[6][3];
+    int xcd8;  // the device has 8 XCDs: -1 not asked yet, then 0 or 1
 };
 
 // Device scratch of lbm_step_momentum_exchange_noalloc: the per-workgroup
@@ -154,7 +155,21 @@ lbm::LaunchGeom geom_of(const lbm_sim* s)
     g.open = s->open;
     g.res = reservoir_bits(s);
     g.mask = s->mask;
+    g.xcd8 = s->xcd8 == 1;
     return g;
+}
+
+// Whether the current device has the 8 XCDs the chunked workgroup orders are
+// laid out for (asked once, at the first initialisation); 0 if the runtime
+// cannot tell.
+void ask_xcd8(lbm_sim* s)
+{
+    if (s->xcd8 >= 0) return;
+    int dev = 0, n = 0;
+    s->xcd8 = hipGetDevice(&dev) == hipSuccess &&
+                      hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && n == 8
+                  ? 1
+                  : 0;
 }
 
 lbm::LaunchPhys phys_of(const lbm_sim* s)
@@ -328,6 +343,7 @@ lbm_status lbm_create(const lbm_desc* desc, void* buf0, void* buf1, void* hip_st
     s->initialized = false;
     s->t = 0;
     s->cur = 0;
+    s->xcd8 = -1;
     s->omega = std::isinf(desc->tau) ? 0.0 : 1.0 / desc->tau;
     s->last_hip = hipSuccess;
     *out = s;
@@ -411,6 +427,7 @@ lbm_status lbm_init_equilibrium(lbm_sim* sim, const void* rho, const void* u)
     sim->t = 0;
     sim->cur = 0;
     sim->initialized = false;
+    ask_xcd8(sim);
     if (compact(sim->d)) {
         const lbm_status b = build_compact(sim);
         if (b != LBM_OK) return b;

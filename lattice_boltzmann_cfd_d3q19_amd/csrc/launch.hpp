@@ -12,6 +12,10 @@ struct LaunchGeom {
     uint32_t open;  // bit k: face k (-x, +x, -y, +y, -z, +z) is open (its axis is not periodic)
     uint32_t res;   // bit k: open face k is an equilibrium reservoir (the others have face rules)
     const uint8_t* mask;
+    // the device has 8 XCDs, over which the dispatcher deals workgroups
+    // round robin: the XCD-chunked workgroup orders assume that layout and
+    // are used only then (otherwise the hardware order)
+    bool xcd8;
 };
 
 struct LaunchPhys {

@@ -40,7 +40,7 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
     g.n = (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz;
     g.mask = lg.mask;
     g.xk = 1;
-    if (xcd_chunks) {
+    if (xcd_chunks && lg.xcd8) {
         // an eighth of a z-plane's tiles per chunk: the tiles of rows y +- 1
         // and of the planes z +- 1 then run on the same XCD
         g.xk = (g.ntx * g.nty + 7) / 8;
@@ -251,7 +251,7 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     // workgroups were no better on any of them.
     const uint64_t wg_plane = ((uint64_t)t.nf / (uint64_t)lg.nz + kGatherThreads - 1) / kGatherThreads;
     g.xk = (uint32_t)((wg_plane + 7) / 8);
-    if (g.xk < 1) g.xk = 1;
+    if (g.xk < 1 || !lg.xcd8) g.xk = 1;
     return g;
 }
 
