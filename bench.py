@@ -187,14 +187,18 @@ def probe_ceilings(n_cells, reps=20):
     """Bandwidth (GB/s, bytes read + written) of the two probe kernels on the
     launch stream: a float4 copy of 1 GiB (the best of plain and nontemporal
     accesses with 1, 2, 4 or 8 elements per work-item) and the 19-plane
-    in-place swap over n_cells cells (the better of plain and nontemporal)."""
+    in-place swap over n_cells cells (the better of plain and nontemporal),
+    each also with its workgroups per CU capped at 4, 3 and 2."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "lattice_boltzmann_cfd_d3q19_amd", "libprobes.so"))
     lib.probe_copy_f4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_void_p]
+                                  ctypes.c_size_t, ctypes.c_void_p]
     lib.probe_swap19.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_void_p]
+                                 ctypes.c_size_t, ctypes.c_void_p]
+    # workgroups per CU: all that fit, or 4, 3, 2 (reserved, unused LDS; the
+    # step kernels cap theirs the same way)
+    caps = [0] + [2 * 160 * 1024 // (2 * w + 1) for w in (4, 3, 2)]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
@@ -218,24 +222,24 @@ def probe_ceilings(n_cells, reps=20):
     dst = torch.empty_like(src)
     n4 = src.numel() // 4
     out["copy_float4_GBps"] = max(
-        timed(lambda nt=nt, per=per: check(lib.probe_copy_f4(src.data_ptr(), dst.data_ptr(), n4, nt, per, sp)),
-              2 * n4 * 16)
-        for nt in (0, 1) for per in (1, 2, 4, 8))
+        timed(lambda nt=nt, per=per, lds=lds: check(lib.probe_copy_f4(src.data_ptr(), dst.data_ptr(), n4, nt, per,
+                                                                      lds, sp)), 2 * n4 * 16)
+        for nt in (0, 1) for per in (1, 2, 4, 8) for lds in caps)
     del src, dst
     stride = (n_cells + 63) // 64 * 64
     buf = torch.zeros(19 * stride, dtype=torch.float32, device="cuda")
     out["swap19_inplace_GBps"] = max(
-        timed(lambda nt=nt: check(lib.probe_swap19(buf.data_ptr(), stride, n_cells, nt, 1, sp)),
+        timed(lambda nt=nt, lds=lds: check(lib.probe_swap19(buf.data_ptr(), stride, n_cells, nt, 1, lds, sp)),
               2 * 19 * 4 * n_cells)
-        for nt in (0, 1))
+        for nt in (0, 1) for lds in caps)
     # the same pattern with 2 and 4 cells per work-item (8- and 16-byte
     # accesses per plane), over the largest multiple of 4 cells
     n4c = n_cells // 4 * 4
     for per in (2, 4):
         out[f"swap19_{per}cells_GBps"] = max(
-            timed(lambda nt=nt, per=per: check(lib.probe_swap19(buf.data_ptr(), stride, n4c, nt, per, sp)),
-                  2 * 19 * 4 * n4c)
-            for nt in (0, 1))
+            timed(lambda nt=nt, per=per, lds=lds: check(lib.probe_swap19(buf.data_ptr(), stride, n4c, nt, per, lds,
+                                                                         sp)), 2 * 19 * 4 * n4c)
+            for nt in (0, 1) for lds in caps)
     del buf
     out["swap19_cells"] = n_cells
     return {k: (round(v, 1) if isinstance(v, float) else v) for k, v in out.items()}

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cmath>
+#include <cstdlib>
 
 #include "kernels.hpp"
 #include "kernels_compact.hpp"
@@ -50,6 +51,104 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
     const uint32_t chunk = 8 * g.xk;
     s.grid = dim3(g.xk > 1 ? (g.ntiles + chunk - 1) / chunk * chunk : g.ntiles, 1, 1);
     return s;
+}
+
+// Resident workgroups per CU of the step kernels.  A step kernel's CU holds
+// as many workgroups as registers allow (the compact gathers: four of 512
+// work-items); together with the XCD-chunked order that puts about a dozen
+// z-planes of an XCD's slab of the box in flight at once, more than its 4 MB
+// L2 keeps, so the lines that neighbouring rows and planes share (read by
+// one cell, written by another) are fetched and written back more than
+// once.  Fewer resident workgroups narrow that front.  The cap is applied by
+// reserving LDS the kernels do not use (160 KiB per CU on gfx950):
+// floor(160 KiB / (w + 1/2)) bytes per workgroup leaves room for w of them.
+// Targets per kernel class, measured on the 256^3 porous and periodic boxes
+// (fp32, mean launch time, reserved LDS 0 / 27 / 33 / 41 / 54 / 82 KB):
+//   compact odd in-place step: 2 (porous 0.389 -> 0.367 ms, periodic 0.494
+//     -> 0.491); compact even step: 3 (0.270 -> 0.255, 0.450 -> 0.410);
+//     compact pull: 3 (0.336 -> 0.330, 0.504 -> 0.498); compact esoteric
+//     twist: 2 (0.428 -> 0.408, 0.554 -> 0.550); compact esoteric pull: no
+//     cap (no gain);
+//   even in-place steps of the dense layouts: SoA 2 without solids (0.438 ->
+//     0.405), 3 with (0.555 -> 0.535); SoAoS 2 without (0.478 -> 0.432), 3
+//     with (0.476 -> 0.456); AoS 3 without (0.554 -> 0.541), none with;
+//   SoA odd step: 2 without solids (0.449 -> 0.418), 4 with (0.586 ->
+//     0.574); SoA pull: 2 without (0.450 -> 0.420), 3 with (0.651 -> 0.566);
+//   SoAoS pull with solids: 5 (0.519 -> 0.497); SoAoS odd step: no cap;
+//   AoS odd step without solids: 2 (1.709 -> 1.044); AoS pull: 2 without
+//     (0.929 -> 0.824), 3 with (0.743 -> 0.718); AoS odd step with solids:
+//     no cap (1.18 -> 1.27 at 2).
+// The caps apply only to lattices larger than the 256 MB last-level cache:
+// at 128^3 (159 MB, cache-resident) the kernels are latency-bound and lost
+// up to 12% with them (Taylor-Green stream odd step 0.059 -> 0.066 ms),
+// while every 256^3 and 512^3 box (fp32 and fp64) gained or tied (512^3
+// porous: compact even 2.26 -> 2.14 ms, odd 3.24 -> 3.06, SoA pull 5.80 ->
+// 4.61).
+// An experiment build (LBM_LDS_FROM_ENV) takes the bytes from the
+// environment instead (LBM_LDS for the gathers, LBM_LDS_EVEN for the even
+// in-place steps), to measure other caps without rebuilding.
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr uint64_t kLastLevelCache = 256ull << 20;
+
+// a lattice of `cells` stored cells does not fit in the last-level cache
+template <typename T>
+constexpr bool beyond_llc(uint64_t cells)
+{
+    return cells * (uint64_t)kQ * sizeof(T) > kLastLevelCache;
+}
+
+constexpr size_t lds_for_workgroups(int w)
+{
+    return w <= 0 ? 0 : (size_t)(2 * kLdsPerCu / (size_t)(2 * w + 1));
+}
+
+// target for a dense step kernel of layout L, kind K, boundary instance bnd
+// (0: no solids or walls); 0 = no cap
+template <int L, int K>
+constexpr int dense_step_workgroups(int bnd)
+{
+    if constexpr (K == kAAEven) {
+        if constexpr (L == kCollision) return bnd == 0 ? 3 : 0;
+        return bnd == 0 ? 2 : 3;
+    } else if constexpr (K == kAAOdd) {
+        if constexpr (L == kStream) return bnd == 0 ? 2 : 4;
+        if constexpr (L == kCollision) return bnd == 0 ? 2 : 0;
+        return 0;
+    } else if constexpr (K == kAB) {
+        if constexpr (L == kStream) return bnd == 0 ? 2 : 3;
+        if constexpr (L == kCollision) return bnd == 0 ? 2 : 3;
+        return bnd == 0 ? 0 : 5;
+    } else {
+        return 0;
+    }
+}
+
+template <int K>
+constexpr int compact_step_workgroups()
+{
+    return K == kAAOdd ? 2 : K == kAAEven ? 3 : K == kAB ? 3 : is_twist(K) ? 2 : 0;
+}
+
+#ifdef LBM_LDS_FROM_ENV
+inline size_t lds_env(const char* name, size_t dflt)
+{
+    const char* v = getenv(name);
+    return v ? (size_t)strtoul(v, nullptr, 10) : dflt;
+}
+#endif
+
+// reserved LDS of a launch: even = an even in-place step (AA even or the
+// esoteric schemes' even steps are gathers too; only the AA even step is
+// purely local), w = the class's target
+inline size_t step_lds(bool even, int w, bool big)
+{
+    const size_t dflt = big ? lds_for_workgroups(w) : 0;
+#ifdef LBM_LDS_FROM_ENV
+    return lds_env(even ? "LBM_LDS_EVEN" : "LBM_LDS", dflt);
+#else
+    (void)even;
+    return dflt;
+#endif
 }
 
 template <typename T>
@@ -109,7 +208,8 @@ hipError_t launch_step_t(T* a, T* b, const Shape& s, const Phys<T>& p, const Mom
     }
     k = mo.rho != nullptr ? (const void*)&step_kernel<T, L, K, BND, FORCE, true>
                           : (const void*)&step_kernel<T, L, K, BND, FORCE, false>;
-    return hipLaunchKernel(k, s.grid, s.block, args, 0, st);
+    const size_t lds = step_lds(K == kAAEven, dense_step_workgroups<L, K>(BND), beyond_llc<T>(g.n));
+    return hipLaunchKernel(k, s.grid, s.block, args, lds, st);
 }
 
 template <typename T, int L, int K>
@@ -274,7 +374,8 @@ hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, MomOut<T>
                                   : (const void*)&step_compact_kernel<T, K, FORCE, true, false>)
                            : (out ? (const void*)&step_compact_kernel<T, K, FORCE, false, true>
                                   : (const void*)&step_compact_kernel<T, K, FORCE, false, false>);
-    return hipLaunchKernel(k, grid, block, args, 0, st);
+    const size_t lds = step_lds(false, compact_step_workgroups<K>(), beyond_llc<T>(g.nf));
+    return hipLaunchKernel(k, grid, block, args, lds, st);
 }
 
 template <typename T, bool FORCE>
@@ -293,7 +394,8 @@ hipError_t launch_even_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, h
     const dim3 grid((s + kEvenThreads - 1) / kEvenThreads), block(kEvenThreads);
     const void* k = mo.rho != nullptr ? (const void*)&even_compact_kernel<T, FORCE, true>
                                       : (const void*)&even_compact_kernel<T, FORCE, false>;
-    return hipLaunchKernel(k, grid, block, args, 0, st);
+    const size_t lds = step_lds(true, compact_step_workgroups<kAAEven>(), beyond_llc<T>(g.nf));
+    return hipLaunchKernel(k, grid, block, args, lds, st);
 }
 
 template <typename T, int K, bool FORCE>
@@ -315,7 +417,8 @@ hipError_t launch_eso_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, hi
                                   : (const void*)&eso_compact_kernel<T, K, FORCE, true, false>)
                            : (out ? (const void*)&eso_compact_kernel<T, K, FORCE, false, true>
                                   : (const void*)&eso_compact_kernel<T, K, FORCE, false, false>);
-    return hipLaunchKernel(k, grid, block, args, 0, st);
+    const size_t lds = step_lds(false, compact_step_workgroups<K>(), beyond_llc<T>(g.nf));
+    return hipLaunchKernel(k, grid, block, args, lds, st);
 }
 
 template <typename T, int K, bool FORCE>
@@ -337,7 +440,8 @@ hipError_t launch_twist_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, 
                                   : (const void*)&twist_compact_kernel<T, K, FORCE, true, false>)
                            : (out ? (const void*)&twist_compact_kernel<T, K, FORCE, false, true>
                                   : (const void*)&twist_compact_kernel<T, K, FORCE, false, false>);
-    return hipLaunchKernel(k, grid, block, args, 0, st);
+    const size_t lds = step_lds(false, compact_step_workgroups<K>(), beyond_llc<T>(g.nf));
+    return hipLaunchKernel(k, grid, block, args, lds, st);
 }
 
 template <typename T, int K>

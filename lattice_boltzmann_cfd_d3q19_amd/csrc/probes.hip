@@ -59,10 +59,10 @@ __global__ __launch_bounds__(kBlock) void copy_f4_kernel(const float4* __restric
 }
 
 template <bool NT, int PER>
-int launch_copy(const void* src, void* dst, size_t n, void* stream) {
+int launch_copy(const void* src, void* dst, size_t n, size_t lds, void* stream) {
     const size_t per = (size_t)kBlock * PER;
     const dim3 grid((unsigned)((n + per - 1) / per));
-    copy_f4_kernel<NT, PER><<<grid, kBlock, 0, (hipStream_t)stream>>>((const float4*)src, (float4*)dst, n);
+    copy_f4_kernel<NT, PER><<<grid, kBlock, lds, (hipStream_t)stream>>>((const float4*)src, (float4*)dst, n);
     return (int)hipGetLastError();
 }
 
@@ -103,10 +103,10 @@ __global__ __launch_bounds__(kBlock) void swap19_kernel(float* __restrict__ buf,
 }
 
 template <bool NT, int PER>
-int launch_swap(void* buf, size_t stride, size_t n, void* stream) {
+int launch_swap(void* buf, size_t stride, size_t n, size_t lds, void* stream) {
     const size_t cells = (size_t)kBlock * PER;
     const dim3 grid((unsigned)((n + cells - 1) / cells));
-    swap19_kernel<NT, PER><<<grid, kBlock, 0, (hipStream_t)stream>>>((float*)buf, stride, n);
+    swap19_kernel<NT, PER><<<grid, kBlock, lds, (hipStream_t)stream>>>((float*)buf, stride, n);
     return (int)hipGetLastError();
 }
 
@@ -117,34 +117,37 @@ extern "C" {
 // 0 on success, else the hipError_t of the launch.  n = 16-byte elements;
 // src and dst device pointers, 16-byte aligned, not overlapping.  per: 16-byte
 // elements per work-item, 1, 2, 4 or 8 (other values: hipErrorInvalidValue).
-int probe_copy_f4(const void* src, void* dst, size_t n, int nontemporal, int per, void* stream) {
+// lds: bytes of LDS reserved per workgroup and not used (caps the workgroups
+// a CU holds at once; at most 160 KiB).
+int probe_copy_f4(const void* src, void* dst, size_t n, int nontemporal, int per, size_t lds, void* stream) {
     if (n == 0) return 0;
+    if (lds > 160 * 1024) return (int)hipErrorInvalidValue;
     switch (per * 2 + (nontemporal ? 1 : 0)) {
-    case 2: return launch_copy<false, 1>(src, dst, n, stream);
-    case 3: return launch_copy<true, 1>(src, dst, n, stream);
-    case 4: return launch_copy<false, 2>(src, dst, n, stream);
-    case 5: return launch_copy<true, 2>(src, dst, n, stream);
-    case 8: return launch_copy<false, 4>(src, dst, n, stream);
-    case 9: return launch_copy<true, 4>(src, dst, n, stream);
-    case 16: return launch_copy<false, 8>(src, dst, n, stream);
-    case 17: return launch_copy<true, 8>(src, dst, n, stream);
+    case 2: return launch_copy<false, 1>(src, dst, n, lds, stream);
+    case 3: return launch_copy<true, 1>(src, dst, n, lds, stream);
+    case 4: return launch_copy<false, 2>(src, dst, n, lds, stream);
+    case 5: return launch_copy<true, 2>(src, dst, n, lds, stream);
+    case 8: return launch_copy<false, 4>(src, dst, n, lds, stream);
+    case 9: return launch_copy<true, 4>(src, dst, n, lds, stream);
+    case 16: return launch_copy<false, 8>(src, dst, n, lds, stream);
+    case 17: return launch_copy<true, 8>(src, dst, n, lds, stream);
     default: return (int)hipErrorInvalidValue;
     }
 }
 
 // buf: device float[19 * stride], stride >= n.  per: cells per work-item,
 // 1, 2 or 4; for 2 and 4, n and stride must be multiples of per (else
-// hipErrorInvalidValue) and buf 4 * per-byte aligned.
-int probe_swap19(void* buf, size_t stride, size_t n, int nontemporal, int per, void* stream) {
+// hipErrorInvalidValue) and buf 4 * per-byte aligned.  lds as for the copy.
+int probe_swap19(void* buf, size_t stride, size_t n, int nontemporal, int per, size_t lds, void* stream) {
     if (n == 0) return 0;
-    if (stride < n || per < 1 || n % per || stride % per) return (int)hipErrorInvalidValue;
+    if (stride < n || per < 1 || n % per || stride % per || lds > 160 * 1024) return (int)hipErrorInvalidValue;
     switch (per * 2 + (nontemporal ? 1 : 0)) {
-    case 2: return launch_swap<false, 1>(buf, stride, n, stream);
-    case 3: return launch_swap<true, 1>(buf, stride, n, stream);
-    case 4: return launch_swap<false, 2>(buf, stride, n, stream);
-    case 5: return launch_swap<true, 2>(buf, stride, n, stream);
-    case 8: return launch_swap<false, 4>(buf, stride, n, stream);
-    case 9: return launch_swap<true, 4>(buf, stride, n, stream);
+    case 2: return launch_swap<false, 1>(buf, stride, n, lds, stream);
+    case 3: return launch_swap<true, 1>(buf, stride, n, lds, stream);
+    case 4: return launch_swap<false, 2>(buf, stride, n, lds, stream);
+    case 5: return launch_swap<true, 2>(buf, stride, n, lds, stream);
+    case 8: return launch_swap<false, 4>(buf, stride, n, lds, stream);
+    case 9: return launch_swap<true, 4>(buf, stride, n, lds, stream);
     default: return (int)hipErrorInvalidValue;
     }
 }
