@@ -86,7 +86,14 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
 // 4.61).
 // An experiment build (LBM_LDS_FROM_ENV) takes the bytes from the
 // environment instead (LBM_LDS for the gathers, LBM_LDS_EVEN for the even
-// in-place steps), to measure other caps without rebuilding.
+// in-place steps), and scales the compact gathers' XCD chunk by
+// LBM_XK_NUM / LBM_XK_DEN, to measure other settings without rebuilding.
+// Measured with it on the 256^3 and 512^3 porous boxes: 256-work-item
+// workgroups for the compact gathers (best 0.373 ms at four per CU) and
+// chunks of 1/16, 1/4 or 1/2 plane were slower than 512 work-items, two per
+// CU, an eighth of a plane per chunk (0.367 ms); chunked orders for the SoA
+// and SoAoS layouts stayed slower under the caps too (256^3 porous SoA
+// pull 0.567 -> 0.681 ms).
 constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr uint64_t kLastLevelCache = 256ull << 20;
 
@@ -351,6 +358,9 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     // workgroups were no better on any of them.
     const uint64_t wg_plane = ((uint64_t)t.nf / (uint64_t)lg.nz + kGatherThreads - 1) / kGatherThreads;
     g.xk = (uint32_t)((wg_plane + 7) / 8);
+#ifdef LBM_LDS_FROM_ENV
+    g.xk = (uint32_t)(g.xk * lds_env("LBM_XK_NUM", 8) / lds_env("LBM_XK_DEN", 8));
+#endif
     if (g.xk < 1 || !lg.xcd8) g.xk = 1;
     return g;
 }
