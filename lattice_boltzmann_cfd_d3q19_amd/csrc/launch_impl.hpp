@@ -72,6 +72,7 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
 //   even in-place steps of the dense layouts: SoA 2 without solids (0.438 ->
 //     0.405), 3 with (0.555 -> 0.535); SoAoS 2 without (0.478 -> 0.432), 3
 //     with (0.476 -> 0.456); AoS 3 without (0.554 -> 0.541), none with;
+//   the dense gathers of boxes with open faces: no cap (see below);
 //   SoA odd step: 2 without solids (0.449 -> 0.418), 4 with (0.586 ->
 //     0.574); SoA pull: 2 without (0.450 -> 0.420), 3 with (0.651 -> 0.566);
 //   SoAoS pull with solids: 5 (0.519 -> 0.497); SoAoS odd step: no cap;
@@ -114,6 +115,9 @@ constexpr size_t lds_for_workgroups(int w)
 template <int L, int K>
 constexpr int dense_step_workgroups(int bnd)
 {
+    // the open-face instance's gathers: no cap (768 x 192 x 96 open channel,
+    // SoA pull 0.419 -> 0.481 ms at three workgroups per CU, 0.440 at four)
+    if (bnd == 2 && K != kAAEven) return 0;
     if constexpr (K == kAAEven) {
         if constexpr (L == kCollision) return bnd == 0 ? 3 : 0;
         return bnd == 0 ? 2 : 3;
