@@ -30,7 +30,7 @@
  *                  slots, whose roles swap every step.  Bounce-back links keep
  *                  their value in slots no other link uses (a solid
  *                  neighbour's, the wrapped cell's beyond a face; in the
- *                  compact layout a packed region after the 19 planes).
+ *                  compact layout a packed region after the blocks).
  *   LBM_SCHEME_ESOTWIST  one lattice, in place, the esoteric twist that
  *                  PortLBM (section 3.3) names with AA and the esoteric pull
  *                  (Geier and Schoenherr, Computation 5, 19, 2017): with
@@ -52,18 +52,20 @@
  *                         (c_y, c_z) (one stencil row each); cell-major
  *                         inside a bundle.
  *   LBM_LAYOUT_COLLISION  AoS: the 19 populations of a cell are contiguous.
- *   LBM_LAYOUT_COMPACT    SoA over fluid cells only: population q of the i-th
- *                         fluid cell (in cell order) at P(q) * S + i, S = the
- *                         fluid count rounded up to 64, with the planes of
- *                         opposite directions side by side: P(q) = 2q for
- *                         q < 9, 2(18 - q) + 1 for q > 9, P(9) = 18.  Needs
- *                         a workspace (lbm_set_workspace) for its neighbour
- *                         tables; in porous media it moves only fluid bytes.
- *                         Limits (else LBM_ERR_UNSUPPORTED): 4 (nx+2)(ny+2)
- *                         (nz+2) < 2^32 and 2 * 64-rounded N * sizeof(T) <
- *                         2^32 (32-bit byte offsets inside the kernels).
+ *   LBM_LAYOUT_COMPACT    fluid cells only, in cell order, in blocks of 64
+ *                         cells that each hold the cells' 19 planes side by
+ *                         side (AoSoA): population q of the i-th fluid cell
+ *                         at element (i / 64) * 19 * 64 + P(q) * 64 + i % 64,
+ *                         with the planes of opposite directions adjacent:
+ *                         P(q) = 2q for q < 9, 2(18 - q) + 1 for q > 9,
+ *                         P(9) = 18.  The blocks fill 19 * S elements, S = the
+ *                         fluid count rounded up to 64.  Needs a workspace
+ *                         (lbm_set_workspace) for its neighbour tables; in
+ *                         porous media it moves only fluid bytes.  Limit
+ *                         (else LBM_ERR_UNSUPPORTED): 4 (nx+2)(ny+2)(nz+2) <
+ *                         2^32 (32-bit offsets into the neighbour table).
  *                         ESOPULL keeps the bounce-back values of its
- *                         neighbour-side links after the 19 planes, one slot
+ *                         neighbour-side links after the 19 S elements, one slot
  *                         per link packed in cell order (9 more planes of
  *                         room, 4 workspace bytes more per cell).
  *

@@ -114,11 +114,9 @@ lbm_status validate_desc(const lbm_desc* d)
     if (!compact(*d) && d->scheme == LBM_SCHEME_ESOTWIST &&
         (double)(d->nx + 1) * (double)(d->ny + 1) * (double)(d->nz + 1) >= 2147483648.0)
         return LBM_ERR_UNSUPPORTED;
-    // the compact kernels address the padded index table and each two-plane
-    // block of populations with 32-bit byte offsets
+    // the compact kernels address the padded index table with 32-bit byte
+    // offsets (the populations with 64-bit ones)
     if (compact(*d) && 4.0 * (double)(d->nx + 2) * (double)(d->ny + 2) * (double)(d->nz + 2) >= 4294967296.0)
-        return LBM_ERR_UNSUPPORTED;
-    if (compact(*d) && 2.0 * (d->precision == LBM_F64 ? 8.0 : 4.0) * (double)compact_capacity(*d) >= 4294967296.0)
         return LBM_ERR_UNSUPPORTED;
     return LBM_OK;
 }

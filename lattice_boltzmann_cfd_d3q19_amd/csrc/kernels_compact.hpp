@@ -1,12 +1,21 @@
-// kernels_compact.hpp -- the fluid-compacted SoA layout ("compact").
+// kernels_compact.hpp -- the fluid-compacted layout ("compact").
 //
-// Only fluid cells are stored: population q of the i-th fluid cell (fluid
-// cells ranked in cell order) lives at P(q) * S + i, S = the fluid count
-// rounded up to 64, P(q) the storage plane of q (opposite directions side by
-// side, below).  In a porous medium a dense layout moves whole cache lines that
-// are mostly solid (in the 256^3, 62%-porous benchmark medium 98.6% of
-// 128-byte lines hold some fluid, so a dense step moves ~1.6x the fluid
-// bytes); here every population line is fully used.
+// Only fluid cells are stored, ranked in cell order, in blocks of 64: block b
+// holds the 19 storage planes of fluid cells 64 b .. 64 b + 63 one after the
+// other, so population q of the i-th fluid cell lives at element
+// (i / 64) * 19 * 64 + P(q) * 64 + i % 64, P(q) the storage plane of q
+// (opposite directions side by side, below).  In a porous medium a dense
+// layout moves whole cache lines that are mostly solid (in the 256^3,
+// 62%-porous benchmark medium 98.6% of 128-byte lines hold some fluid, so a
+// dense step moves ~1.6x the fluid bytes); here every population line is
+// fully used.  A wave's 64 cells are one block: its 19 slots of a direction
+// are one 256-byte run and its whole state one contiguous 4864-byte region
+// (fp32), so a step streams one region per wave instead of 19 planes that
+// lie S elements apart.  Measured on MI355X, 256^3 porous box, fp32, against
+// 19 planes of S cells: even in-place step 0.256 -> 0.243 ms, odd step 0.367
+// -> 0.342 ms, fused pull 0.331 -> 0.307 ms (an in-place swap probe with the
+// even step's pattern: 6.0 -> 6.8 TB/s); the all-fluid periodic 256^3 box
+// tied (0.903 -> 0.904 ms per step pair).
 //
 // Geometry tables (caller-owned workspace, built on the device at init):
 //   idxp[p]   for every cell of the box padded by one halo layer on each side,
@@ -88,7 +97,7 @@ struct CompactGeom {
     uint32_t nf;   // fluid cells
     uint32_t px;   // nx + 2
     uint32_t pxy;  // (nx + 2)(ny + 2)
-    uint32_t s;    // population stride (fluid cells rounded up to 64); 2 s sizeof(T) < 2^32
+    uint32_t s;    // stored cells (fluid, and the esoteric twist's ghosts) rounded up to 64
     uint32_t xk;   // workgroup chunk per XCD turn of the gather kernels (1 = hardware order)
     uint32_t open; // bit k: face k is an open reservoir (table entries kOpen + k mark
                    // every open face; the rule faces act as walls to the steps)
@@ -189,12 +198,34 @@ __device__ __forceinline__ void add_links_nb(double (&acc)[6], const T (&s)[kQ],
 // Storage order of the populations: opposite directions side by side.  Pair
 // k = 0..8 holds directions k and 18 - k in planes 2k and 2k + 1 (sub-planes
 // 0 and 1); the rest population is plane 18.  Every access of a step kernel
-// then lies in the two-plane block of its pair, so it is one uniform base
-// (the block, a scalar register) plus a 32-bit byte offset per lane, and a
-// bounce-back select only chooses between two offsets inside that block.
+// then lies in the two planes of its pair, so it is one uniform base (the
+// pair's first plane, a scalar register) plus a byte offset per lane, and a
+// bounce-back select only chooses between two offsets inside that pair.
 constexpr int pair_of(int q) { return q < 9 ? q : q > 9 ? kQ - 1 - q : 9; }
 constexpr int sub_of(int q) { return q > 9 ? 1 : 0; }
 constexpr int plane_of(int q) { return 2 * pair_of(q) + sub_of(q); }
+
+// Element (plane pl, compact index j) of the population store: blocks of 64
+// cells, each holding its 19 planes side by side.  The esoteric pull's
+// bounce-back region follows the 19 S elements of the blocks.  Offsets are 64
+// bits wide (a store of more than 4 GB is addressed like a small one).
+constexpr uint32_t kCBlock = 64;
+typedef uint64_t coff_t;
+__device__ __forceinline__ uint64_t celem(int pl, uint32_t j)
+{
+    return (uint64_t)(j >> 6) * (uint64_t)(kQ * kCBlock) + (uint64_t)pl * kCBlock + (j & (kCBlock - 1u));
+}
+// byte offset of cell j in plane 0, and the bytes from one plane to the next
+template <typename T>
+__device__ __forceinline__ coff_t cbytes(uint32_t j)
+{
+    return celem(0, j) * sizeof(T);
+}
+template <typename T>
+__device__ __forceinline__ constexpr coff_t cplane()
+{
+    return kCBlock * sizeof(T);
+}
 
 // Esoteric pull on the compact store: pair k < 9 keeps its two slots in the
 // planes of the other schemes, S0 = P(k) and S1 = P(18 - k), and the rest
@@ -202,7 +233,7 @@ constexpr int plane_of(int q) { return 2 * pair_of(q) + sub_of(q); }
 // pair k is (S_P, i), or (S0, i) if x - c_k is not fluid; the neighbour side
 // is (S_{1-P}, nb[k]) for a fluid neighbour.  Solid cells and the halo have
 // no storage here, so a neighbour-side bounce-back link keeps its value in a
-// region after the 19 planes, at element 19 S + bbase[i] + (the cell's
+// region after the blocks, at element 19 S + bbase[i] + (the cell's
 // bounce-back links of the pairs before k): one slot per such link, packed in
 // cell order, so that a wave's bounced links share one or two lines.
 constexpr int kEsoPlanes = 28;     // 19 planes and up to 9 S bounce-back slots
@@ -252,24 +283,24 @@ template <int S>
 __device__ __forceinline__ uint64_t compact_state_off(const CompactGeom& g, uint32_t i, const uint32_t (&nb)[kQ],
                                                       int q)
 {
-    const uint64_t s = g.s;
+    const uint64_t s = g.s;  // the bounce-back region follows 19 s elements
     const uint32_t up = nb[opp(q)];
     if constexpr (is_twist(S)) {
         const int pl = S == kTwOdd ? opp(q) : q;
-        return (uint64_t)plane_of(pl) * s + twist_compact_loc(g, i, kCx[q] > 0, kCy[q] > 0, kCz[q] > 0);
+        return celem(plane_of(pl), twist_compact_loc(g, i, kCx[q] > 0, kCy[q] > 0, kCz[q] > 0));
     } else if constexpr (is_eso(S)) {
         constexpr bool odd = S == kEsoOdd;
-        if (q == 9) return (uint64_t)plane_of(9) * s + i;
-        if (q < 9) return (uint64_t)plane_of((no_fluid(up) || !odd) ? q : opp(q)) * s + i;
+        if (q == 9) return celem(plane_of(9), i);
+        if (q < 9) return celem(plane_of((no_fluid(up) || !odd) ? q : opp(q)), i);
         const int k = opp(q);  // neighbour side: x + c_k = x - c_q
-        if (!no_fluid(up)) return (uint64_t)plane_of(odd ? k : q) * s + up;
+        if (!no_fluid(up)) return celem(plane_of(odd ? k : q), up);
         return (uint64_t)kEsoBouncePlane * s + eso_bounce_slot(g.bbase[i], eso_bounce_mask(nb), k);
     } else if constexpr (S == kAB) {
-        return no_fluid(up) ? (uint64_t)plane_of(opp(q)) * s + i : (uint64_t)plane_of(q) * s + up;
+        return no_fluid(up) ? celem(plane_of(opp(q)), i) : celem(plane_of(q), up);
     } else if constexpr (S == kAAEven) {
-        return (uint64_t)plane_of(q) * s + i;
+        return celem(plane_of(q), i);
     } else {
-        return no_fluid(up) ? (uint64_t)plane_of(q) * s + i : (uint64_t)plane_of(opp(q)) * s + up;
+        return no_fluid(up) ? celem(plane_of(q), i) : celem(plane_of(opp(q)), up);
     }
 }
 
@@ -291,13 +322,13 @@ __device__ __forceinline__ T* compact_state_slot(T* buf, const CompactGeom& g, u
 //   - fused pull: plain loads, nontemporal stores (the destination lattice is
 //     not read in the same step), 3% faster than plain stores.
 template <typename T>
-__device__ __forceinline__ T ld_at(const char* blk, uint32_t off)
+__device__ __forceinline__ T ld_at(const char* blk, coff_t off)
 {
     return *(const T*)(blk + off);
 }
 
 template <bool NT, typename T>
-__device__ __forceinline__ void st_at(char* blk, uint32_t off, T v)
+__device__ __forceinline__ void st_at(char* blk, coff_t off, T v)
 {
     if constexpr (NT) {
         __builtin_nontemporal_store(v, (T*)(blk + off));
@@ -325,9 +356,9 @@ __device__ __forceinline__ void open_outflow(T (&f)[kQ], const uint32_t (&nb)[kQ
 // Written as a select of two cheap values so it compiles to v_cndmask, not
 // to a divergent branch.
 template <typename T>
-__device__ __forceinline__ uint32_t link_off(uint32_t nbv, uint32_t nb_sub_bytes, uint32_t own_bytes)
+__device__ __forceinline__ coff_t link_off(uint32_t nbv, coff_t nb_sub_bytes, coff_t own_bytes)
 {
-    const uint32_t via_nb = nbv * (uint32_t)sizeof(T) + nb_sub_bytes;
+    const coff_t via_nb = cbytes<T>(nbv) + nb_sub_bytes;
     return no_fluid(nbv) ? own_bytes : via_nb;
 }
 
@@ -341,8 +372,9 @@ __device__ __forceinline__ uint32_t link_off(uint32_t nbv, uint32_t nb_sub_bytes
 // find no cells and exit.
 
 
-// block of pair k inside a buffer: planes 2k, 2k + 1 (a uniform 64-bit base)
-__device__ __forceinline__ char* pair_block(char* base, int k, uint32_t plane_bytes)
+// planes 2k, 2k + 1 of pair k in the first block (a uniform 64-bit base; a
+// cell's block comes with its per-lane offset)
+__device__ __forceinline__ char* pair_block(char* base, int k, coff_t plane_bytes)
 {
     return base + (uint64_t)(2 * k) * plane_bytes;
 }
@@ -388,9 +420,9 @@ template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
 __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restrict__ b, const CompactGeom& g,
                                                   const Phys<T>& p, uint32_t i, double (&acc)[6], T (&fo)[4])
 {
-    const uint32_t sb = g.s * (uint32_t)sizeof(T);  // bytes per plane; 2 sb < 2^32 (host check)
-    const uint32_t own0 = i * (uint32_t)sizeof(T);  // own slot in sub-plane 0 / 1 of a block
-    const uint32_t own1 = own0 + sb;
+    const coff_t sb = cplane<T>();  // bytes from one plane of a block to the next
+    const coff_t own0 = cbytes<T>(i);  // own slot in sub-plane 0 / 1 of a block
+    const coff_t own1 = own0 + sb;
     char* const A = (char*)a;
     char* const B = (char*)b;
     uint32_t nb[kQ];
@@ -403,8 +435,8 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
         // reservoir's value if x - c_q lies beyond an open face
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            const uint32_t off = q == 9 ? own0
-                                        : link_off<T>(nb[opp(q)], sub_of(q) ? sb : 0u, sub_of(opp(q)) ? own1 : own0);
+            const coff_t off = q == 9 ? own0
+                                      : link_off<T>(nb[opp(q)], sub_of(q) ? sb : (coff_t)0, sub_of(opp(q)) ? own1 : own0);
             f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), off);
         }
         if constexpr (OPEN) apply_open_nb(f, nb, p);
@@ -422,10 +454,10 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
     } else {
         // slot of direction d: (d, x + c_d), or (opp d, x) if x + c_d is solid.
         // The odd step reads f_{opp d} from it and writes f*_d into it.
-        uint32_t off[kQ];
+        coff_t off[kQ];
 #pragma unroll
         for (int d = 0; d < kQ; ++d)
-            off[d] = d == 9 ? own0 : link_off<T>(nb[d], sub_of(d) ? sb : 0u, sub_of(opp(d)) ? own1 : own0);
+            off[d] = d == 9 ? own0 : link_off<T>(nb[d], sub_of(d) ? sb : (coff_t)0, sub_of(opp(d)) ? own1 : own0);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), off[opp(q)]);
         if constexpr (OPEN) apply_open_nb(f, nb, p);
@@ -486,8 +518,8 @@ __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const Compac
                                                  uint32_t i, double (&acc)[6], T (&fo)[4])
 {
     constexpr uint32_t P = K == kEsoOdd ? 1u : 0u;
-    const uint32_t sb = g.s * (uint32_t)sizeof(T);
-    const uint32_t own = i * (uint32_t)sizeof(T);
+    const coff_t sb = cplane<T>();
+    const coff_t own = cbytes<T>(i);
     char* const A = (char*)a;
     uint32_t nb[kQ];
     neighbours_rows(g, g.cellp[i], nb);
@@ -495,14 +527,14 @@ __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const Compac
     if constexpr (MEX) link_masks(nb, bm, wm);
     const uint32_t bmask = eso_bounce_mask(nb);
     const uint32_t bbase = bmask != 0u ? g.bbase[i] : 0u;
-    T* const B = (T*)(A + (uint64_t)kEsoBouncePlane * sb);
-    uint32_t own_off[9];
+    T* const B = a + (uint64_t)kEsoBouncePlane * g.s;  // after the blocks
+    coff_t own_off[9];
     T* nb_ptr[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
         own_off[k] = (P == 0u || no_fluid(nb[opp(k)])) ? own : own + sb;
         char* const blk = pair_block(A, k, sb);
-        T* const via_nb = (T*)(blk + (1u - P) * sb + nb[k] * (uint32_t)sizeof(T));
+        T* const via_nb = (T*)(blk + (1u - P) * sb + cbytes<T>(nb[k]));
         nb_ptr[k] = ((bmask >> k) & 1u) ? B + eso_bounce_slot(bbase, bmask, k) : via_nb;
     }
     char* const rest = pair_block(A, 9, sb);
@@ -566,7 +598,7 @@ __device__ __forceinline__ void twist_compact_cell(T* __restrict__ a, const Comp
                                                    uint32_t i, double (&acc)[6], T (&fo)[4])
 {
     constexpr int P = K == kTwOdd ? 1 : 0;
-    const uint32_t sb = g.s * (uint32_t)sizeof(T);
+    const coff_t sb = cplane<T>();
     char* const A = (char*)a;
     const uint32_t pc = g.cellp[i];
     uint32_t nb[kQ];
@@ -587,7 +619,7 @@ __device__ __forceinline__ void twist_compact_cell(T* __restrict__ a, const Comp
     for (int q = 0; q < kQ; ++q) {
         const int o = (kCx[q] > 0 ? 1 : 0) + (kCy[q] > 0 ? 2 : 0) + (kCz[q] > 0 ? 4 : 0);
         const int pl = P == 0 ? q : opp(q);
-        f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), (sub_of(pl) ? sb : 0u) + loc[o] * (uint32_t)sizeof(T));
+        f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), (sub_of(pl) ? sb : (coff_t)0) + cbytes<T>(loc[o]));
     }
     if constexpr (OPEN) apply_open_nb(f, nb, p);
     T rho, ux, uy, uz;
@@ -606,8 +638,8 @@ __device__ __forceinline__ void twist_compact_cell(T* __restrict__ a, const Comp
         const int o = (kCx[q] < 0 ? 1 : 0) + (kCy[q] < 0 ? 2 : 0) + (kCz[q] < 0 ? 4 : 0);
         const bool back = no_fluid(nb[q]) && !is_res(nb[q], g.open);
         const int pn = P == 0 ? opp(q) : q, pb = P == 0 ? q : opp(q);
-        const uint32_t sub = back ? (sub_of(pb) ? sb : 0u) : (sub_of(pn) ? sb : 0u);
-        st_at<false>(pair_block(A, pair_of(q), sb), sub + loc[o] * (uint32_t)sizeof(T), f[q]);
+        const coff_t sub = back ? (sub_of(pb) ? sb : (coff_t)0) : (sub_of(pn) ? sb : (coff_t)0);
+        st_at<false>(pair_block(A, pair_of(q), sb), sub + cbytes<T>(loc[o]), f[q]);
     }
     if constexpr (MEX) add_links_mask(acc, f, bm, wm);
 }
@@ -649,9 +681,9 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_kernel(T* __restric
 {
     const uint32_t i = blockIdx.x * kEvenThreads + threadIdx.x;
     if (i >= s) return;
-    const uint32_t sb = s * (uint32_t)sizeof(T);
-    const uint32_t own0 = i * (uint32_t)sizeof(T);
-    const uint32_t own1 = own0 + sb;
+    const coff_t sb = cplane<T>();
+    const coff_t own0 = cbytes<T>(i);
+    const coff_t own1 = own0 + sb;
     char* const A = (char*)a;
     T f[kQ];
 #pragma unroll
@@ -679,9 +711,9 @@ __global__ void __launch_bounds__(kEvenThreads) even_compact_mex_kernel(T* __res
     const uint32_t i = blockIdx.x * kEvenThreads + threadIdx.x;
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     if (i < g.nf) {
-        const uint32_t sb = g.s * (uint32_t)sizeof(T);
-        const uint32_t own0 = i * (uint32_t)sizeof(T);
-        const uint32_t own1 = own0 + sb;
+        const coff_t sb = cplane<T>();
+        const coff_t own0 = cbytes<T>(i);
+        const coff_t own1 = own0 + sb;
         char* const A = (char*)a;
         uint32_t nb[kQ];
         neighbours_rows(g, g.cellp[i], nb);

@@ -56,9 +56,9 @@ __global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restric
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     const uint32_t i = blockIdx.x * kBlockThreads + threadIdx.x;
     if (i < g.nf) {
-        const uint32_t sb = g.s * (uint32_t)sizeof(T);
-        const uint32_t own0 = i * (uint32_t)sizeof(T);
-        const uint32_t own1 = own0 + sb;
+        const coff_t sb = cplane<T>();
+        const coff_t own0 = cbytes<T>(i);
+        const coff_t own1 = own0 + sb;
         char* const A = (char*)a;
         uint32_t nb[kQ];
         neighbours_rows(g, g.cellp[i], nb);
@@ -69,13 +69,13 @@ __global__ void __launch_bounds__(kBlockThreads) mex_compact_kernel(T* __restric
                 f[q] = a[compact_state_off<S>(g, i, nb, q)];
                 continue;
             }
-            uint32_t off;
+            coff_t off;
             if constexpr (S == kAAEven) {
                 off = sub_of(q) ? own1 : own0;
             } else if constexpr (S == kAB) {
-                off = q == 9 ? own0 : link_off<T>(nb[opp(q)], sub_of(q) ? sb : 0u, sub_of(opp(q)) ? own1 : own0);
+                off = q == 9 ? own0 : link_off<T>(nb[opp(q)], sub_of(q) ? sb : (coff_t)0, sub_of(opp(q)) ? own1 : own0);
             } else {
-                off = q == 9 ? own0 : link_off<T>(nb[opp(q)], sub_of(opp(q)) ? sb : 0u, sub_of(q) ? own1 : own0);
+                off = q == 9 ? own0 : link_off<T>(nb[opp(q)], sub_of(opp(q)) ? sb : (coff_t)0, sub_of(q) ? own1 : own0);
             }
             f[q] = ld_at<T>(pair_block(A, pair_of(q), sb), off);
         }

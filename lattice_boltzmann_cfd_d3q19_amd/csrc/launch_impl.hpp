@@ -67,9 +67,11 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
 // (fp32, mean launch time, reserved LDS 0 / 27 / 33 / 41 / 54 / 82 KB):
 //   compact odd in-place step: 2 (porous 0.389 -> 0.367 ms, periodic 0.494
 //     -> 0.491); compact even step: 3 (0.270 -> 0.255, 0.450 -> 0.410);
-//     compact pull: 3 (0.336 -> 0.330, 0.504 -> 0.498); compact esoteric
-//     twist: 2 (0.428 -> 0.408, 0.554 -> 0.550); compact esoteric pull: no
-//     cap (no gain);
+//     compact esoteric twist: 2 (0.428 -> 0.408, 0.554 -> 0.550); compact
+//     esoteric pull: no cap (no gain); re-measured with the blocked compact
+//     store (porous, no cap / 2 / 3 / 4): odd 0.348 / 0.342 / 0.348 / 0.348,
+//     even 0.264 / 0.247 / 0.242 / 0.253, pull 0.312 / 0.302 / 0.307 / 0.313
+//     (the pull's target is 2 since);
 //   even in-place steps of the dense layouts: SoA 2 without solids (0.438 ->
 //     0.405), 3 with (0.555 -> 0.535); SoAoS 2 without (0.478 -> 0.432), 3
 //     with (0.476 -> 0.456); AoS 3 without (0.554 -> 0.541), none with;
@@ -138,7 +140,7 @@ constexpr int dense_step_workgroups(int bnd)
 template <int K>
 constexpr int compact_step_workgroups()
 {
-    return K == kAAOdd ? 2 : K == kAAEven ? 3 : K == kAB ? 3 : is_twist(K) ? 2 : 0;
+    return K == kAAOdd ? 2 : K == kAAEven ? 3 : K == kAB ? 2 : is_twist(K) ? 2 : 0;
 }
 
 #ifdef LBM_LDS_FROM_ENV

@@ -80,22 +80,21 @@ def test_too_many_cells_unsupported():
 
 
 def test_compact_offset_limits():
-    # the compact kernels address one two-plane block with a 32-bit byte
-    # offset: 2 * roundup(N, 64) * sizeof(T) < 2^32
+    # the compact kernels address the populations with 64-bit offsets (a
+    # store beyond 4 GB is fine) and the padded neighbour table with 32-bit
+    # ones: 4 (nx+2)(ny+2)(nz+2) < 2^32 (and N < 2^31)
     big = dict(layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_AA)
     assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F32, **big))[0] == capi.LBM_OK
-    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F64, **big))[0] == capi.LBM_ERR_UNSUPPORTED
-    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 255, capi.LBM_F64, **big))[0] == capi.LBM_OK
-    # the same box in a dense layout is fine
-    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F64))[0] == capi.LBM_OK
-    # the padded neighbour table: 4 (nx+2)(ny+2)(nz+2) < 2^32 (and N < 2^31)
+    st, nbytes, _ = capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F64, **big))
+    assert st == capi.LBM_OK and nbytes == 19 * 1024 * 1024 * 256 * 8
+    assert capi.lbm_buffer_bytes(capi.make_desc(1022, 1022, 1020, capi.LBM_F32, **big))[0] == capi.LBM_OK
     assert capi.lbm_buffer_bytes(capi.make_desc(1022, 1022, 1022, capi.LBM_F32, **big))[0] == capi.LBM_ERR_UNSUPPORTED
 
 
 def test_esoteric_pull_buffers():
-    # one buffer; 19 planes in the dense layouts, 28 in the compact one (three
-    # per pair: two swapping slots and a bounce-back slot, and the rest
-    # population), whose three-plane blocks are addressed with 32-bit offsets
+    # one buffer; 19 planes in the dense layouts, 28 in the compact one (the
+    # 19 of the blocks, then room for one bounce-back slot per link of the
+    # nine pairs)
     for layout, planes in ((capi.LBM_LAYOUT_STREAM, 19), (capi.LBM_LAYOUT_COLLISION, 19),
                            (capi.LBM_LAYOUT_COMPACT, 28)):
         d = capi.make_desc(16, 8, 5, capi.LBM_F32, layout=layout, scheme=capi.LBM_SCHEME_ESOPULL)
@@ -107,9 +106,10 @@ def test_esoteric_pull_buffers():
         assert st == capi.LBM_OK
         capi.lbm_destroy(h)
     big = dict(layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_ESOPULL)
-    # the same two-plane offset limit as the other compact schemes
+    # 64-bit population offsets here too
     assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F32, **big))[0] == capi.LBM_OK
-    assert capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F64, **big))[0] == capi.LBM_ERR_UNSUPPORTED
+    st, nbytes, _ = capi.lbm_buffer_bytes(capi.make_desc(1024, 1024, 256, capi.LBM_F64, **big))
+    assert st == capi.LBM_OK and nbytes == 28 * 1024 * 1024 * 256 * 8
     # its workspace holds one more 4-byte table per cell (the bounce-back slots)
     aa = capi.make_desc(16, 8, 5, capi.LBM_F32, layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_AA)
     eso = capi.make_desc(16, 8, 5, capi.LBM_F32, layout=capi.LBM_LAYOUT_COMPACT, scheme=capi.LBM_SCHEME_ESOPULL)
