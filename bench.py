@@ -188,7 +188,8 @@ def probe_ceilings(n_cells, reps=20):
     launch stream: a float4 copy of 1 GiB (the best of plain and nontemporal
     accesses with 1, 2, 4 or 8 elements per work-item) and the 19-plane
     in-place swap over n_cells cells (the better of plain and nontemporal),
-    each also with its workgroups per CU capped at 4, 3 and 2."""
+    each also with its workgroups per CU capped at 4, 3 and 2; and the swap in
+    64-cell blocks of 19 planes (the compact layout's store)."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "lattice_boltzmann_cfd_d3q19_amd", "libprobes.so"))
@@ -196,6 +197,8 @@ def probe_ceilings(n_cells, reps=20):
                                   ctypes.c_size_t, ctypes.c_void_p]
     lib.probe_swap19.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_size_t, ctypes.c_void_p]
+    lib.probe_swap19_blocked.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_size_t,
+                                         ctypes.c_void_p]
     # workgroups per CU: all that fit, or 4, 3, 2 (reserved, unused LDS; the
     # step kernels cap theirs the same way)
     caps = [0] + [2 * 160 * 1024 // (2 * w + 1) for w in (4, 3, 2)]
@@ -240,6 +243,12 @@ def probe_ceilings(n_cells, reps=20):
             timed(lambda nt=nt, per=per, lds=lds: check(lib.probe_swap19(buf.data_ptr(), stride, n4c, nt, per, lds,
                                                                          sp)), 2 * 19 * 4 * n4c)
             for nt in (0, 1) for lds in caps)
+    # the same swap in the compact layout's store (64-cell blocks, each with
+    # its 19 planes side by side)
+    out["swap19_blocked_GBps"] = max(
+        timed(lambda nt=nt, lds=lds: check(lib.probe_swap19_blocked(buf.data_ptr(), n_cells, nt, lds, sp)),
+              2 * 19 * 4 * n_cells)
+        for nt in (0, 1) for lds in caps)
     del buf
     out["swap19_cells"] = n_cells
     return {k: (round(v, 1) if isinstance(v, float) else v) for k, v in out.items()}
@@ -264,6 +273,8 @@ def main():
     ap.add_argument("--per-kernel-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reps", type=int, default=10, help="segments of the timed region (median, min, max)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the probe-kernel ceilings (profiling runs): their keys are then absent")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -349,7 +360,7 @@ def main():
     del rho, u
 
     # measured ceilings: the probe kernels
-    ceilings = probe_ceilings(n_fluid)
+    ceilings = None if args.no_probes else probe_ceilings(n_fluid)
 
     # plain copy reference (torch copy kernel, 2 GiB moved)
     src = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
@@ -392,16 +403,18 @@ def main():
                      "traffic_over_alg": None if traffic is None else round(traffic / alg_bytes, 4),
                      "kernel": dominant, "alg_bytes_per_launch": alg_bytes,
                      "kernel_ms": {k: round(v, 5) for k, v in per_ms.items()},
-                     "frac_of_copy_float4": round(achieved / ceilings["copy_float4_GBps"], 4),
-                     "frac_of_swap19": round(achieved / ceilings["swap19_inplace_GBps"], 4)},
+                     **({} if ceilings is None else {
+                         "frac_of_copy_float4": round(achieved / ceilings["copy_float4_GBps"], 4),
+                         "frac_of_swap19": round(achieved / ceilings["swap19_inplace_GBps"], 4),
+                         "frac_of_swap19_blocked": round(achieved / ceilings["swap19_blocked_GBps"], 4)})},
         "reps": reps,
         "steps_per_rep": seg,
         "reps_mlups": {"median": round(float(np.median(seg_mlups)), 1), "min": round(seg_mlups[0], 1),
                        "max": round(seg_mlups[-1], 1)},
         "mflups": round(n_fluid * args.steps / sec / 1e6, 1),
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
-        "step_frac_of_copy_float4": round(step_gbps / ceilings["copy_float4_GBps"], 4),
-        **ceilings,
+        **({} if ceilings is None else {
+            "step_frac_of_copy_float4": round(step_gbps / ceilings["copy_float4_GBps"], 4), **ceilings}),
         "copy_GBps": round(copy_gbps, 1),
         "state_finite": finite,
         "state_bounded": bounded,

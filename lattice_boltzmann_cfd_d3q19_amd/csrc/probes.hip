@@ -10,6 +10,10 @@
 //                     access pattern of the in-place (AA) even step without
 //                     its arithmetic (19 coalesced planes read and written
 //                     per cell, in place), with 1, 2 or 4 cells per work-item.
+//   probe_swap19_blocked  the same swap in the compact layout's store: cells in
+//                     blocks of 64, each block holding its 19 planes side by
+//                     side (value q of cell i at (i / 64) * 19 * 64 + q * 64 +
+//                     i % 64), one cell per work-item.
 // Both move 2 bytes per byte of payload (one read, one write).  `nt` selects
 // nontemporal loads and stores (streaming data that is not reused).
 #include <hip/hip_runtime.h>
@@ -110,6 +114,23 @@ int launch_swap(void* buf, size_t stride, size_t n, size_t lds, void* stream) {
     return (int)hipGetLastError();
 }
 
+template <bool NT>
+__global__ __launch_bounds__(kBlock) void swap19_blocked_kernel(float* __restrict__ buf, size_t n) {
+    const size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n) return;
+    const size_t base = (i / 64) * (19 * 64) + i % 64;
+    float v[19];
+#pragma unroll
+    for (int q = 0; q < 19; ++q) v[q] = NT ? __builtin_nontemporal_load(&buf[base + q * 64]) : buf[base + q * 64];
+#pragma unroll
+    for (int q = 0; q < 19; ++q) {
+        if (NT)
+            __builtin_nontemporal_store(v[q], &buf[base + (18 - q) * 64]);
+        else
+            buf[base + (18 - q) * 64] = v[q];
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,6 +171,18 @@ int probe_swap19(void* buf, size_t stride, size_t n, int nontemporal, int per, s
     case 9: return launch_swap<true, 4>(buf, stride, n, lds, stream);
     default: return (int)hipErrorInvalidValue;
     }
+}
+
+// buf: device float[19 * roundup(n, 64)].  lds as for the copy.
+int probe_swap19_blocked(void* buf, size_t n, int nontemporal, size_t lds, void* stream) {
+    if (n == 0) return 0;
+    if (lds > 160 * 1024) return (int)hipErrorInvalidValue;
+    const dim3 grid((unsigned)((n + kBlock - 1) / kBlock));
+    if (nontemporal)
+        swap19_blocked_kernel<true><<<grid, kBlock, lds, (hipStream_t)stream>>>((float*)buf, n);
+    else
+        swap19_blocked_kernel<false><<<grid, kBlock, lds, (hipStream_t)stream>>>((float*)buf, n);
+    return (int)hipGetLastError();
 }
 
 }  // extern "C"
