@@ -101,6 +101,7 @@ struct CompactGeom {
     uint32_t xk;   // workgroup chunk per XCD turn of the gather kernels (1 = hardware order)
     uint32_t open; // bit k: face k is an open reservoir (table entries kOpen + k mark
                    // every open face; the rule faces act as walls to the steps)
+    uint32_t full; // every cell of the box is fluid (host-side launch choices only)
 };
 
 // Compact indices of the 18 neighbours x + c_d (kInvalid: solid, kWall: wall),
