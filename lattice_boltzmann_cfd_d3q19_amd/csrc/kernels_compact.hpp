@@ -102,6 +102,8 @@ struct CompactGeom {
     uint32_t open; // bit k: face k is an open reservoir (table entries kOpen + k mark
                    // every open face; the rule faces act as walls to the steps)
     uint32_t full; // every cell of the box is fluid (host-side launch choices only)
+    uint32_t nx, ny, nz, nxy;  // the box (the direct-neighbour instances)
+    uint32_t direct;           // every cell fluid and every axis periodic (host-side)
 };
 
 // Compact indices of the 18 neighbours x + c_d (kInvalid: solid, kWall: wall),
@@ -158,6 +160,21 @@ __device__ __forceinline__ void neighbours_rows(const CompactGeom& g, uint32_t p
             nb[d] = kCx[d] < 0 ? v.x : kCx[d] == 0 ? v.y : v.z;
         }
     }
+}
+
+// The same 18 indices on a box whose every cell is fluid and whose every axis
+// is periodic: the compact index of a cell is then its cell index, and the
+// neighbours follow from its coordinates with periodic wrap, with no table
+// reads (the gather kernels' DIRECT instances).
+__device__ __forceinline__ void neighbours_direct(const CompactGeom& g, uint32_t i, uint32_t (&nb)[kQ])
+{
+    const uint32_t nx = g.nx, ny = g.ny, nz = g.nz, nxy = g.nxy;
+    const uint32_t z = i / nxy, r = i - z * nxy, y = r / nx, x = r - y * nx;
+    const uint32_t X[3] = {x == 0 ? nx - 1 : x - 1, x, x + 1 == nx ? 0 : x + 1};
+    const uint32_t Y[3] = {(y == 0 ? ny - 1 : y - 1) * nx, y * nx, (y + 1 == ny ? 0 : y + 1) * nx};
+    const uint32_t Z[3] = {(z == 0 ? nz - 1 : z - 1) * nxy, z * nxy, (z + 1 == nz ? 0 : z + 1) * nxy};
+#pragma unroll
+    for (int d = 0; d < kQ; ++d) nb[d] = d == 9 ? kInvalid : X[kCx[d] + 1] + Y[kCy[d] + 1] + Z[kCz[d] + 1];
 }
 
 // Bit q of bm: link q is bounced back (x + c_q solid or beyond a wall); of
@@ -417,7 +434,7 @@ __device__ __forceinline__ void write_fields_range(const MomOut<T>& mo, const ui
 // step of the in-place pattern (K = kAAOdd, a = the lattice).  OPEN: some
 // faces are open (a separate instance: the reservoir selects would cost the
 // other cases registers).
-template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX, bool DIRECT>
 __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restrict__ b, const CompactGeom& g,
                                                   const Phys<T>& p, uint32_t i, double (&acc)[6], T (&fo)[4])
 {
@@ -427,7 +444,11 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
     char* const A = (char*)a;
     char* const B = (char*)b;
     uint32_t nb[kQ];
-    neighbours_rows(g, g.cellp[i], nb);
+    if constexpr (DIRECT) {
+        neighbours_direct(g, i, nb);
+    } else {
+        neighbours_rows(g, g.cellp[i], nb);
+    }
     uint32_t bm = 0u, wm = 0u;
     if constexpr (MEX) link_masks(nb, bm, wm);
     T f[kQ];
@@ -483,8 +504,9 @@ __device__ __forceinline__ void step_compact_cell(T* __restrict__ a, T* __restri
 
 // Gather step over the fluid cells, one work-item per fluid cell (see
 // step_compact_cell).  MEX: also sum the momentum exchange of the step over
-// the workgroup into mo.partial (row = the logical workgroup).
-template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false>
+// the workgroup into mo.partial (row = the logical workgroup).  DIRECT: an
+// all-fluid, fully periodic box (neighbours from coordinates).
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false, bool DIRECT = false>
 __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restrict__ a, T* __restrict__ b,
                                                                      CompactGeom g, Phys<T> p, MomOut<T> mo)
 {
@@ -496,14 +518,14 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
     if constexpr (OUT) {
         static_assert(!MEX, "no fields output in a momentum-exchange step");
         fo[0] = fo[1] = fo[2] = fo[3] = T(0);
-        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, true, false>(a, b, g, p, i, acc, fo);
+        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, true, false, DIRECT>(a, b, g, p, i, acc, fo);
         const uint32_t i0 = i - (threadIdx.x & 63u);
         if (i0 < g.nf) write_fields_range(mo, g.cellid, g.nf, i0, fo);
     } else if constexpr (!MEX) {
         if (i >= g.nf) return;
-        step_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, b, g, p, i, acc, fo);
+        step_compact_cell<T, K, FORCE, OPEN, OUT, false, DIRECT>(a, b, g, p, i, acc, fo);
     } else {
-        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, b, g, p, i, acc, fo);
+        if (i < g.nf) step_compact_cell<T, K, FORCE, OPEN, OUT, true, DIRECT>(a, b, g, p, i, acc, fo);
         if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
             block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
     }

@@ -396,6 +396,13 @@ hipError_t launch_io(int layout, int state, int op, T* a, T* b, const LaunchGeom
 
 // ------------------------------------------------------------ compact
 
+// The gathers of an all-fluid, fully periodic box compute their neighbours
+// from coordinates instead of reading the index tables (an experiment build
+// can turn this off).
+#ifndef LBM_COMPACT_DIRECT
+#define LBM_COMPACT_DIRECT 1
+#endif
+
 inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
 {
     CompactGeom g{};
@@ -410,6 +417,12 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     g.s = (uint32_t)t.stride;
     g.open = lg.res;
     g.full = (uint64_t)t.nf == (uint64_t)lg.nx * (uint64_t)lg.ny * (uint64_t)lg.nz;
+    g.nx = (uint32_t)lg.nx;
+    g.ny = (uint32_t)lg.ny;
+    g.nz = (uint32_t)lg.nz;
+    g.nxy = (uint32_t)(lg.nx * lg.ny);
+    // (open faces and face rules sit on non-periodic faces only)
+    g.direct = LBM_COMPACT_DIRECT && g.full && lg.periodic[0] && lg.periodic[1] && lg.periodic[2];
     // XCD chunk of the gather kernels: an eighth of the workgroups of an
     // average z-plane, so the rows at z +- 1 fall on the same XCD as the
     // rows they are gathered by.  Measured (odd in-place step): 256^3 porous
@@ -440,8 +453,12 @@ hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, MomOut<T>
                                : (const void*)&step_compact_kernel<T, K, FORCE, false, false, true>;
         return hipLaunchKernel(k, grid, block, args, 0, st);
     }
+    // an all-fluid, fully periodic box: neighbours from coordinates
+    const bool direct = g.direct && !g.open;
     const void* k = g.open ? (out ? (const void*)&step_compact_kernel<T, K, FORCE, true, true>
                                   : (const void*)&step_compact_kernel<T, K, FORCE, true, false>)
+                    : direct ? (out ? (const void*)&step_compact_kernel<T, K, FORCE, false, true, false, true>
+                                    : (const void*)&step_compact_kernel<T, K, FORCE, false, false, false, true>)
                            : (out ? (const void*)&step_compact_kernel<T, K, FORCE, false, true>
                                   : (const void*)&step_compact_kernel<T, K, FORCE, false, false>);
     const size_t lds = step_lds(false, compact_step_workgroups<K>(), beyond_llc<T>(g.nf));
