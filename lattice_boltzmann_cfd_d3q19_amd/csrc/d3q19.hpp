@@ -22,6 +22,14 @@ constexpr int kCz[kQ] = {-1, -1, -1, -1, -1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 1, 1,
 
 constexpr int opp(int q) { return kQ - 1 - q; }
 
+// the direction with velocity (cx, cy, cz); -1 if it is not in the set
+constexpr int dir_of(int cx, int cy, int cz)
+{
+    for (int q = 0; q < kQ; ++q)
+        if (kCx[q] == cx && kCy[q] == cy && kCz[q] == cz) return q;
+    return -1;
+}
+
 // |c|^2 class -> weight numerator over 36.
 constexpr int kW36[kQ] = {1, 1, 2, 1, 1, 1, 2, 1, 2, 12, 2, 1, 2, 1, 1, 1, 2, 1, 1};
 
@@ -49,6 +57,8 @@ constexpr bool table_is_consistent()
     return true;
 }
 static_assert(table_is_consistent(), "D3Q19 table inconsistent");
+static_assert(dir_of(0, 0, 0) == 9 && dir_of(-1, 0, -1) == 1 && dir_of(0, -1, -1) == 0 && dir_of(1, 1, 1) == -1,
+              "dir_of");
 
 enum Layout : int { kStream = 0, kBundle = 1, kCollision = 2 };
 // What a kernel does with the stored populations:

@@ -533,10 +533,11 @@ __global__ void __launch_bounds__(kGatherThreads) step_compact_kernel(T* __restr
 
 // Esoteric-pull step on the compact store (K = kEsoEven / kEsoOdd; the
 // slot map is described at compact_state_off).  The own side of pair k and
-// a fluid neighbour side lie in the pair's two-plane block (a uniform base
-// plus a 32-bit byte offset, as in the other compact kernels); a bounced
+// a fluid neighbour side lie in the pair's two planes of the blocks (a
+// uniform base plus a per-lane byte offset, as in the other compact
+// kernels); a bounced
 // neighbour side goes to the packed bounce-back region instead.
-template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX, bool DIRECT>
 __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const CompactGeom& g, const Phys<T>& p,
                                                  uint32_t i, double (&acc)[6], T (&fo)[4])
 {
@@ -545,7 +546,11 @@ __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const Compac
     const coff_t own = cbytes<T>(i);
     char* const A = (char*)a;
     uint32_t nb[kQ];
-    neighbours_rows(g, g.cellp[i], nb);
+    if constexpr (DIRECT) {
+        neighbours_direct(g, i, nb);
+    } else {
+        neighbours_rows(g, g.cellp[i], nb);
+    }
     uint32_t bm = 0u, wm = 0u;
     if constexpr (MEX) link_masks(nb, bm, wm);
     const uint32_t bmask = eso_bounce_mask(nb);
@@ -586,7 +591,7 @@ __device__ __forceinline__ void eso_compact_cell(T* __restrict__ a, const Compac
     if constexpr (MEX) add_links_mask(acc, f, bm, wm);
 }
 
-template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false>
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false, bool DIRECT = false>
 __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restrict__ a, CompactGeom g, Phys<T> p,
                                                                     MomOut<T> mo)
 {
@@ -598,14 +603,14 @@ __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restri
     if constexpr (OUT) {
         static_assert(!MEX, "no fields output in a momentum-exchange step");
         fo[0] = fo[1] = fo[2] = fo[3] = T(0);
-        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, true, false>(a, g, p, i, acc, fo);
+        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, true, false, DIRECT>(a, g, p, i, acc, fo);
         const uint32_t i0 = i - (threadIdx.x & 63u);
         if (i0 < g.nf) write_fields_range(mo, g.cellid, g.nf, i0, fo);
     } else if constexpr (!MEX) {
         if (i >= g.nf) return;
-        eso_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, i, acc, fo);
+        eso_compact_cell<T, K, FORCE, OPEN, OUT, false, DIRECT>(a, g, p, i, acc, fo);
     } else {
-        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, g, p, i, acc, fo);
+        if (i < g.nf) eso_compact_cell<T, K, FORCE, OPEN, OUT, true, DIRECT>(a, g, p, i, acc, fo);
         if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
             block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
     }
@@ -613,30 +618,41 @@ __global__ void __launch_bounds__(kGatherThreads) eso_compact_kernel(T* __restri
 
 // Esoteric-twist step on the compact store (K = kTwEven / kTwOdd; the map is
 // described at twist_compact_loc and twist_off).  Every population of the
-// pair (q, opp q) stays in the pair's two-plane block: reads and both
-// candidate writes are a uniform base plus a 32-bit offset, and a bounced
+// pair (q, opp q) stays in the pair's two planes of the blocks: reads and
+// both candidate writes are a uniform base plus a per-lane offset, and a bounced
 // link only selects the other sub-plane at the same location.
-template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX>
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX, bool DIRECT>
 __device__ __forceinline__ void twist_compact_cell(T* __restrict__ a, const CompactGeom& g, const Phys<T>& p,
                                                    uint32_t i, double (&acc)[6], T (&fo)[4])
 {
     constexpr int P = K == kTwOdd ? 1 : 0;
     const coff_t sb = cplane<T>();
     char* const A = (char*)a;
-    const uint32_t pc = g.cellp[i];
     uint32_t nb[kQ];
-    neighbours_rows(g, pc, nb);
-    uint32_t bm = 0u, wm = 0u;
-    if constexpr (MEX) link_masks(nb, bm, wm);
     // stored indices of x - o, o = (ox, oy, oz) in {0, 1}^3, at [ox + 2 oy + 4 oz]
     uint32_t loc[7];
     loc[0] = i;
-    loc[1] = twist_ghost_index(g, g.tidx[pc - 1u]);
-    loc[2] = twist_ghost_index(g, g.tidx[pc - g.px]);
-    loc[3] = twist_ghost_index(g, g.tidx[pc - 1u - g.px]);
-    loc[4] = twist_ghost_index(g, g.tidx[pc - g.pxy]);
-    loc[5] = twist_ghost_index(g, g.tidx[pc - 1u - g.pxy]);
-    loc[6] = twist_ghost_index(g, g.tidx[pc - g.px - g.pxy]);
+    if constexpr (DIRECT) {
+        // no ghosts: x - o is the neighbour along -o, a direction of the stencil
+        neighbours_direct(g, i, nb);
+        loc[1] = nb[dir_of(-1, 0, 0)];
+        loc[2] = nb[dir_of(0, -1, 0)];
+        loc[3] = nb[dir_of(-1, -1, 0)];
+        loc[4] = nb[dir_of(0, 0, -1)];
+        loc[5] = nb[dir_of(-1, 0, -1)];
+        loc[6] = nb[dir_of(0, -1, -1)];
+    } else {
+        const uint32_t pc = g.cellp[i];
+        neighbours_rows(g, pc, nb);
+        loc[1] = twist_ghost_index(g, g.tidx[pc - 1u]);
+        loc[2] = twist_ghost_index(g, g.tidx[pc - g.px]);
+        loc[3] = twist_ghost_index(g, g.tidx[pc - 1u - g.px]);
+        loc[4] = twist_ghost_index(g, g.tidx[pc - g.pxy]);
+        loc[5] = twist_ghost_index(g, g.tidx[pc - 1u - g.pxy]);
+        loc[6] = twist_ghost_index(g, g.tidx[pc - g.px - g.pxy]);
+    }
+    uint32_t bm = 0u, wm = 0u;
+    if constexpr (MEX) link_masks(nb, bm, wm);
     T f[kQ];
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
@@ -667,7 +683,7 @@ __device__ __forceinline__ void twist_compact_cell(T* __restrict__ a, const Comp
     if constexpr (MEX) add_links_mask(acc, f, bm, wm);
 }
 
-template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false>
+template <typename T, int K, bool FORCE, bool OPEN, bool OUT, bool MEX = false, bool DIRECT = false>
 __global__ void __launch_bounds__(kGatherThreads) twist_compact_kernel(T* __restrict__ a, CompactGeom g, Phys<T> p,
                                                                       MomOut<T> mo)
 {
@@ -679,14 +695,14 @@ __global__ void __launch_bounds__(kGatherThreads) twist_compact_kernel(T* __rest
     if constexpr (OUT) {
         static_assert(!MEX, "no fields output in a momentum-exchange step");
         fo[0] = fo[1] = fo[2] = fo[3] = T(0);
-        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, true, false>(a, g, p, i, acc, fo);
+        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, true, false, DIRECT>(a, g, p, i, acc, fo);
         const uint32_t i0 = i - (threadIdx.x & 63u);
         if (i0 < g.nf) write_fields_range(mo, g.cellid, g.nf, i0, fo);
     } else if constexpr (!MEX) {
         if (i >= g.nf) return;
-        twist_compact_cell<T, K, FORCE, OPEN, OUT, false>(a, g, p, i, acc, fo);
+        twist_compact_cell<T, K, FORCE, OPEN, OUT, false, DIRECT>(a, g, p, i, acc, fo);
     } else {
-        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, OUT, true>(a, g, p, i, acc, fo);
+        if (i < g.nf) twist_compact_cell<T, K, FORCE, OPEN, OUT, true, DIRECT>(a, g, p, i, acc, fo);
         if (wg < (g.nf + kGatherThreads - 1) / kGatherThreads)
             block_sum6<kGatherThreads>(acc, mo.partial + 6 * (size_t)wg);
     }

@@ -81,7 +81,8 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
 //   SoAoS pull with solids: 5 (0.519 -> 0.497); SoAoS odd step: no cap;
 //   AoS odd step without solids: 2 (1.709 -> 1.044); AoS pull: 2 without
 //     (0.929 -> 0.824), 3 with (0.743 -> 0.718); AoS odd step with solids:
-//     no cap (1.18 -> 1.27 at 2).
+//     no cap (1.18 -> 1.27 at 2; it now runs on the plane tiles, whose own
+//     LDS leaves room for three workgroups per CU).
 // The caps apply only to lattices larger than the 256 MB last-level cache:
 // at 128^3 (159 MB, cache-resident) the kernels are latency-bound and lost
 // up to 12% with them (Taylor-Green stream odd step 0.059 -> 0.066 ms),
@@ -421,7 +422,7 @@ inline CompactGeom compact_geom(const LaunchGeom& lg, const CompactTables& t)
     g.ny = (uint32_t)lg.ny;
     g.nz = (uint32_t)lg.nz;
     g.nxy = (uint32_t)(lg.nx * lg.ny);
-    // (open faces and face rules sit on non-periodic faces only)
+    // (open faces and face rules sit on non-periodic faces only: such a box has none)
     g.direct = LBM_COMPACT_DIRECT && g.full && lg.periodic[0] && lg.periodic[1] && lg.periodic[2];
     // XCD chunk of the gather kernels: an eighth of the workgroups of an
     // average z-plane, so the rows at z +- 1 fall on the same XCD as the
@@ -454,10 +455,9 @@ hipError_t launch_step_compact_t(T* a, T* b, CompactGeom g, Phys<T> p, MomOut<T>
         return hipLaunchKernel(k, grid, block, args, 0, st);
     }
     // an all-fluid, fully periodic box: neighbours from coordinates
-    const bool direct = g.direct && !g.open;
     const void* k = g.open ? (out ? (const void*)&step_compact_kernel<T, K, FORCE, true, true>
                                   : (const void*)&step_compact_kernel<T, K, FORCE, true, false>)
-                    : direct ? (out ? (const void*)&step_compact_kernel<T, K, FORCE, false, true, false, true>
+                    : g.direct ? (out ? (const void*)&step_compact_kernel<T, K, FORCE, false, true, false, true>
                                     : (const void*)&step_compact_kernel<T, K, FORCE, false, false, false, true>)
                            : (out ? (const void*)&step_compact_kernel<T, K, FORCE, false, true>
                                   : (const void*)&step_compact_kernel<T, K, FORCE, false, false>);
@@ -505,6 +505,8 @@ hipError_t launch_eso_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, hi
     }
     const void* k = g.open ? (out ? (const void*)&eso_compact_kernel<T, K, FORCE, true, true>
                                   : (const void*)&eso_compact_kernel<T, K, FORCE, true, false>)
+                    : g.direct ? (out ? (const void*)&eso_compact_kernel<T, K, FORCE, false, true, false, true>
+                                      : (const void*)&eso_compact_kernel<T, K, FORCE, false, false, false, true>)
                            : (out ? (const void*)&eso_compact_kernel<T, K, FORCE, false, true>
                                   : (const void*)&eso_compact_kernel<T, K, FORCE, false, false>);
     const size_t lds = step_lds(false, compact_step_workgroups<K>(), beyond_llc<T>(g.nf));
@@ -528,6 +530,8 @@ hipError_t launch_twist_compact_t(T* a, CompactGeom g, Phys<T> p, MomOut<T> mo, 
     }
     const void* k = g.open ? (out ? (const void*)&twist_compact_kernel<T, K, FORCE, true, true>
                                   : (const void*)&twist_compact_kernel<T, K, FORCE, true, false>)
+                    : g.direct ? (out ? (const void*)&twist_compact_kernel<T, K, FORCE, false, true, false, true>
+                                      : (const void*)&twist_compact_kernel<T, K, FORCE, false, false, false, true>)
                            : (out ? (const void*)&twist_compact_kernel<T, K, FORCE, false, true>
                                   : (const void*)&twist_compact_kernel<T, K, FORCE, false, false>);
     const size_t lds = step_lds(false, compact_step_workgroups<K>(), beyond_llc<T>(g.nf));
