@@ -279,4 +279,95 @@ __global__ void __launch_bounds__(AosTile<T>::kThreads) aos_odd_tile_kernel(T* _
     }
 }
 
+// Even in-place step of the AoS layout, staged through LDS.  The even step is
+// purely local: a fluid cell reads slot q of its own record and writes f*_q
+// to slot opp q of the same record.  One lane per cell straight from memory
+// reads and writes 76-byte records at a 76-byte stride, so every wave
+// instruction spreads over ~38 cache lines.  Here a workgroup takes the
+// records of kCells consecutive cells, one contiguous run of memory (its
+// start is 16-byte aligned: kCells * 19 * sizeof(T) is a multiple of 16),
+// copies it into LDS with consecutive 16-byte accesses (8 lines per
+// instruction), updates the fluid cells' records in LDS, and copies the run
+// back.  A 16-byte piece that lies in solid records only is neither read nor
+// written (nobody touches solid records in this step, and a porous medium's
+// solid lines then stay out of the traffic).  NT: nontemporal accesses (for
+// lattices beyond the last-level cache; a cache-resident lattice keeps its
+// lines for the odd step that follows).  OUT: also the density and velocity
+// (0 on solid cells).
+
+template <typename T>
+struct AosEven {
+    static constexpr int kCells = 256;                // one per work-item
+    static constexpr int kVec = 16 / (int)sizeof(T);  // elements per 16-byte access
+    static constexpr int kElems = kCells * kQ;
+    static constexpr int kChunks = kElems / kVec;
+    static_assert(kElems % kVec == 0, "whole 16-byte accesses per workgroup");
+};
+
+template <typename T, bool NT, bool FORCE, bool OUT>
+__global__ void __launch_bounds__(AosEven<T>::kCells) aos_even_staged_kernel(T* __restrict__ a, Geom g, Phys<T> p,
+                                                                            MomOut<T> mo)
+{
+    using E = AosEven<T>;
+    typedef T vec __attribute__((ext_vector_type(E::kVec)));
+    __shared__ vec S[E::kChunks];
+    __shared__ uint8_t solid[E::kCells];
+    T* const R = (T*)S;
+    const uint64_t c0 = (uint64_t)blockIdx.x * E::kCells;
+    const uint32_t nc = (uint32_t)min((uint64_t)E::kCells, g.n - c0);  // cells of this workgroup
+    const uint32_t ne = nc * (uint32_t)kQ, nch = ne / (uint32_t)E::kVec;
+    const bool masked = g.mask != nullptr;
+    if (masked) {
+        if (threadIdx.x < nc) solid[threadIdx.x] = g.mask[c0 + threadIdx.x] != 0;
+        __syncthreads();
+    }
+    // element e (of this workgroup's run) lies in a fluid record
+    const auto live = [&](uint32_t e0, uint32_t e1) {
+        return !masked || !solid[e0 / kQ] || !solid[e1 / kQ];
+    };
+    T* const base = a + c0 * kQ;
+    const vec* const src = (const vec*)base;
+    for (uint32_t k = threadIdx.x; k < nch; k += E::kCells) {
+        if (live(k * E::kVec, k * E::kVec + E::kVec - 1)) {
+            if constexpr (NT) {
+                S[k] = __builtin_nontemporal_load(src + k);
+            } else {
+                S[k] = src[k];
+            }
+        }
+    }
+    for (uint32_t e = nch * E::kVec + threadIdx.x; e < ne; e += E::kCells)
+        if (live(e, e)) R[e] = base[e];
+    __syncthreads();
+    if (threadIdx.x < nc) {
+        const uint64_t cell = c0 + threadIdx.x;
+        T* const rec = R + threadIdx.x * kQ;
+        if (!masked || !solid[threadIdx.x]) {
+            T f[kQ];
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) f[q] = rec[q];
+            T rho, ux, uy, uz;
+            collide<T, FORCE>(f, p, rho, ux, uy, uz);
+            if constexpr (OUT) write_moments(mo, cell, rho, ux, uy, uz);
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) rec[opp(q)] = f[q];
+        } else if constexpr (OUT) {
+            write_moments(mo, cell, T(0), T(0), T(0), T(0));
+        }
+    }
+    __syncthreads();
+    vec* const dst = (vec*)base;
+    for (uint32_t k = threadIdx.x; k < nch; k += E::kCells) {
+        if (live(k * E::kVec, k * E::kVec + E::kVec - 1)) {
+            if constexpr (NT) {
+                __builtin_nontemporal_store(S[k], dst + k);
+            } else {
+                dst[k] = S[k];
+            }
+        }
+    }
+    for (uint32_t e = nch * E::kVec + threadIdx.x; e < ne; e += E::kCells)
+        if (live(e, e)) base[e] = R[e];
+}
+
 }  // namespace lbm

@@ -312,6 +312,42 @@ hipError_t launch_aos_odd(T* a, const LaunchGeom& lg, const Phys<T>& p, const Mo
     return force ? launch_aos_odd_t<T, true>(a, s, p, mo, st) : launch_aos_odd_t<T, false>(a, s, p, mo, st);
 }
 
+// The even in-place step of the AoS layout staged through LDS
+// (kernels_aos.hpp); the fused momentum exchange takes step_kernel.  An
+// experiment build can turn it off (LBM_AOS_EVEN_STAGED=0).
+#ifndef LBM_AOS_EVEN_STAGED
+#define LBM_AOS_EVEN_STAGED 1
+#endif
+
+template <typename T>
+hipError_t launch_aos_even(T* a, const LaunchGeom& lg, const Phys<T>& p, const MomOut<T>& mo, bool force,
+                           hipStream_t st)
+{
+    using E = AosEven<T>;
+    Geom g = make_shape(lg, false).g;
+    Phys<T> ph = p;
+    MomOut<T> m = mo;
+    void* args[] = {&a, &g, &ph, &m};
+    const bool out = mo.rho != nullptr;
+    // nontemporal beyond the last-level cache (measured: 256^3 porous 0.327
+    // -> 0.289 ms; a cache-resident 128^3 box keeps plain accesses, its odd
+    // step then reads the even step's lines from the cache: 0.175 -> 0.158)
+    const void* k;
+    if (beyond_llc<T>(g.n)) {
+        k = force ? (out ? (const void*)&aos_even_staged_kernel<T, true, true, true>
+                         : (const void*)&aos_even_staged_kernel<T, true, true, false>)
+                  : (out ? (const void*)&aos_even_staged_kernel<T, true, false, true>
+                         : (const void*)&aos_even_staged_kernel<T, true, false, false>);
+    } else {
+        k = force ? (out ? (const void*)&aos_even_staged_kernel<T, false, true, true>
+                         : (const void*)&aos_even_staged_kernel<T, false, true, false>)
+                  : (out ? (const void*)&aos_even_staged_kernel<T, false, false, true>
+                         : (const void*)&aos_even_staged_kernel<T, false, false, false>);
+    }
+    const dim3 grid((uint32_t)((g.n + E::kCells - 1) / E::kCells)), block(E::kCells);
+    return hipLaunchKernel(k, grid, block, args, 0, st);
+}
+
 template <typename T>
 hipError_t launch_step_mo(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp,
                           const MomOut<T>& mo, hipStream_t st)
@@ -322,6 +358,8 @@ hipError_t launch_step_mo(int layout, int kind, T* a, T* b, const LaunchGeom& lg
     const Shape s = make_shape(lg, layout == kCollision);
     const Phys<T> p = make_phys<T>(lp);
     const int bnd = boundary_instance(lg);
+    if (LBM_AOS_EVEN_STAGED && layout == kCollision && kind == kAAEven && mo.partial == nullptr)
+        return launch_aos_even<T>(a, lg, p, mo, lp.has_force, st);
     if (LBM_AOS_TILED && layout == kCollision && kind == kAAOdd && bnd == 1 && mo.partial == nullptr)
         return launch_aos_odd<T>(a, lg, p, mo, lp.has_force, st);
     switch (layout) {
