@@ -74,7 +74,10 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
 //     (the pull's target is 2 since);
 //   even in-place steps of the dense layouts: SoA 2 without solids (0.438 ->
 //     0.405), 3 with (0.555 -> 0.535); SoAoS 2 without (0.478 -> 0.432), 3
-//     with (0.476 -> 0.456); AoS 3 without (0.554 -> 0.541), none with;
+//     with (0.476 -> 0.456); AoS 3 without (0.554 -> 0.541), none with
+//     (measured on step_kernel, which the AoS even step now takes only in a
+//     fused momentum-exchange step: otherwise it is staged through LDS,
+//     aos_even_staged_kernel, eight workgroups per CU);
 //   the dense gathers of boxes with open faces: no cap (see below);
 //   SoA odd step: 2 without solids (0.449 -> 0.418), 4 with (0.586 ->
 //     0.574); SoA pull: 2 without (0.450 -> 0.420), 3 with (0.651 -> 0.566);
