@@ -1,5 +1,7 @@
-// kernels_aos.hpp -- the odd in-place step of the AoS (collision) layout on
-// boxes with solid cells or walls, staged through LDS one plane tile at a time.
+// kernels_aos.hpp -- the in-place steps of the AoS (collision) layout staged
+// through LDS: the odd step on boxes with solid cells or walls, one plane tile
+// at a time, and the even step, one run of consecutive records at a time (at
+// the end of this file).
 //
 // In the AoS layout (PortLBM page, section 3.2, Fig. 2: the 19 populations of
 // a cell side by side, a 76-byte record in fp32) the odd step of the in-place
@@ -321,7 +323,8 @@ __global__ void __launch_bounds__(AosEven<T>::kCells) aos_even_staged_kernel(T* 
         if (threadIdx.x < nc) solid[threadIdx.x] = g.mask[c0 + threadIdx.x] != 0;
         __syncthreads();
     }
-    // element e (of this workgroup's run) lies in a fluid record
+    // the elements e0 .. e1 of this workgroup's run (one or two records)
+    // touch a fluid record
     const auto live = [&](uint32_t e0, uint32_t e1) {
         return !masked || !solid[e0 / kQ] || !solid[e1 / kQ];
     };
