@@ -68,3 +68,32 @@ def test_stored_populations_at_documented_addresses(layout, precision):
             assert got == want, (layout, precision, int(cell), rank, q, got, want)
             checked += 1
     assert checked == Q * len(fluid)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+@pytest.mark.parametrize("scheme", ["aa", "ab"])
+@pytest.mark.parametrize("layout", ["stream", "bundle", "collision"])
+def test_solid_records_stay_cleared(layout, scheme, precision):
+    """Solid cells are never updated: in the in-place and two-lattice schemes
+    their slots of a dense layout hold 0 after the initialisation and keep it
+    through every step, whatever the kernels around them do with the lines
+    they share (the AoS even step copies runs of records through LDS; the
+    odd step rewrites views of neighbouring records)."""
+    need_gpu()
+    shape = (70, 5, 3)  # a ragged last block of 256 records, solids in mixed lines
+    n = int(np.prod(shape))
+    mask = li.random_mask(*shape, fraction=0.3, seed=43)
+    rho, u = li.random_fields(*shape, seed=44)
+    say("solid records", layout, scheme, precision, shape)
+    lat = make(shape, precision=precision, layout=layout, scheme=scheme, mask=mask, rho=rho, u=u,
+               force=(1e-5, 0.0, 0.0))
+    solid = np.flatnonzero(mask != 0)
+    assert solid.size > 0
+    idx = np.array([[address(layout, q, int(c), 0, n) for q in range(Q)] for c in solid]).ravel()
+    for steps in (1, 2, 3):
+        lat.step(steps)
+        torch.cuda.synchronize()
+        for buf in lat.buffers:
+            raw = buf.cpu().numpy()
+            assert np.all(raw[idx] == 0), (layout, scheme, precision, steps)
