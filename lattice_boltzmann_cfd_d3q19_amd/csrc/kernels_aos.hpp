@@ -373,4 +373,80 @@ __global__ void __launch_bounds__(AosEven<T>::kCells) aos_even_staged_kernel(T* 
         if (live(e, e)) base[e] = R[e];
 }
 
+// Two-lattice pull of the AoS layout with its writes staged through LDS: a
+// cell gathers f_q from slot q of the record at x - c_q of the source (or
+// from its own opposite slot if that cell is solid or beyond a wall), as in
+// step_kernel, and writes its 19 post-collision values into its own record of
+// the destination.  The records of kCells consecutive cells are one
+// contiguous run there, so the workgroup assembles them in LDS and writes
+// the run with consecutive 16-byte accesses instead of 76-byte-strided ones.
+// A solid cell's record gets 0, the value every solid record of a dense
+// layout holds in the in-place and two-lattice schemes (the initialisation
+// and the state transfers write it, no step changes it); a piece that lies
+// in solid records only is not written at all.  BND: 1 if the box has a
+// mask or a wall (no open faces here).  Workgroups are renumbered in XCD
+// chunks (g.xk) so that the rows a chunk gathers from share an L2.
+template <typename T, int BND, bool NT, bool FORCE, bool OUT>
+__global__ void __launch_bounds__(AosEven<T>::kCells) aos_pull_staged_kernel(const T* __restrict__ a,
+                                                                            T* __restrict__ b, Geom g, Phys<T> p,
+                                                                            MomOut<T> mo)
+{
+    using E = AosEven<T>;
+    typedef T vec __attribute__((ext_vector_type(E::kVec)));
+    __shared__ vec S[E::kChunks];
+    __shared__ uint8_t solid[E::kCells];
+    T* const R = (T*)S;
+    const uint32_t wg = g.xk > 1 ? xcd_chunked(blockIdx.x, g.xk) : blockIdx.x;
+    const uint64_t c0 = (uint64_t)wg * E::kCells;
+    if (c0 >= g.n) return;  // whole workgroups only: before any barrier
+    const uint32_t nc = (uint32_t)min((uint64_t)E::kCells, g.n - c0);  // cells of this workgroup
+    const uint32_t ne = nc * (uint32_t)kQ, nch = ne / (uint32_t)E::kVec;
+    const bool masked = BND != 0 && g.mask != nullptr;
+    if (threadIdx.x < nc) {
+        Cell c;
+        const uint32_t id = (uint32_t)(c0 + threadIdx.x);
+        c.z = id / g.nxy;
+        const uint32_t r = id - c.z * g.nxy;
+        c.y = r / g.nx;
+        c.x = r - c.y * g.nx;
+        fill_cell(g, c);
+        T* const rec = R + threadIdx.x * kQ;
+        const bool is_solid = masked && g.mask[c.id] != 0;
+        solid[threadIdx.x] = is_solid;
+        if (!is_solid) {
+            const uint32_t bits = link_bits<BND != 0>(g, c);
+            T f[kQ];
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) f[q] = ld_pop(state_slot<kAB, kCollision>(a, g, c, bits, q));
+            T rho, ux, uy, uz;
+            collide<T, FORCE>(f, p, rho, ux, uy, uz);
+            if constexpr (OUT) write_moments(mo, c.id, rho, ux, uy, uz);
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) rec[q] = f[q];
+        } else {
+            if constexpr (OUT) write_moments(mo, c.id, T(0), T(0), T(0), T(0));
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) rec[q] = T(0);
+        }
+    }
+    __syncthreads();
+    // the elements e0 .. e1 of this workgroup's run touch a fluid record
+    const auto live = [&](uint32_t e0, uint32_t e1) {
+        return !masked || !solid[e0 / kQ] || !solid[e1 / kQ];
+    };
+    T* const base = b + c0 * kQ;
+    vec* const dst = (vec*)base;
+    for (uint32_t k = threadIdx.x; k < nch; k += E::kCells) {
+        if (live(k * E::kVec, k * E::kVec + E::kVec - 1)) {
+            if constexpr (NT) {
+                __builtin_nontemporal_store(S[k], dst + k);
+            } else {
+                dst[k] = S[k];
+            }
+        }
+    }
+    for (uint32_t e = nch * E::kVec + threadIdx.x; e < ne; e += E::kCells)
+        if (live(e, e)) base[e] = R[e];
+}
+
 }  // namespace lbm

@@ -351,6 +351,48 @@ hipError_t launch_aos_even(T* a, const LaunchGeom& lg, const Phys<T>& p, const M
     return hipLaunchKernel(k, grid, block, args, 0, st);
 }
 
+// The AoS two-lattice pull with its writes staged through LDS
+// (kernels_aos.hpp); boxes with open faces and the fused momentum exchange
+// take step_kernel.  An experiment build can turn it off
+// (LBM_AOS_PULL_STAGED=0).
+#ifndef LBM_AOS_PULL_STAGED
+#define LBM_AOS_PULL_STAGED 1
+#endif
+#ifndef LBM_AOS_PULL_NT
+#define LBM_AOS_PULL_NT 1
+#endif
+
+template <typename T, int BND, bool NT>
+const void* aos_pull_kernel(bool force, bool out)
+{
+    return force ? (out ? (const void*)&aos_pull_staged_kernel<T, BND, NT, true, true>
+                        : (const void*)&aos_pull_staged_kernel<T, BND, NT, true, false>)
+                 : (out ? (const void*)&aos_pull_staged_kernel<T, BND, NT, false, true>
+                        : (const void*)&aos_pull_staged_kernel<T, BND, NT, false, false>);
+}
+
+template <typename T>
+hipError_t launch_aos_pull(const T* a, T* b, const LaunchGeom& lg, const Phys<T>& p, const MomOut<T>& mo,
+                           int bnd, bool force, hipStream_t st)
+{
+    using E = AosEven<T>;
+    Geom g = make_shape(lg, false).g;
+    // an eighth of a z-plane's workgroups per XCD chunk, as for the tiles
+    const uint64_t nwg = (g.n + E::kCells - 1) / E::kCells;
+    const uint64_t wg_plane = ((uint64_t)g.nxy + E::kCells - 1) / E::kCells;
+    g.xk = lg.xcd8 ? (uint32_t)((wg_plane + 7) / 8) : 1;
+    if (g.xk < 1) g.xk = 1;
+    const uint64_t chunk = 8ull * g.xk;
+    const dim3 grid((uint32_t)(g.xk > 1 ? (nwg + chunk - 1) / chunk * chunk : nwg)), block(E::kCells);
+    Phys<T> ph = p;
+    MomOut<T> m = mo;
+    void* args[] = {&a, &b, &g, &ph, &m};
+    const bool out = mo.rho != nullptr, nt = LBM_AOS_PULL_NT && beyond_llc<T>(g.n);
+    const void* k = bnd == 0 ? (nt ? aos_pull_kernel<T, 0, true>(force, out) : aos_pull_kernel<T, 0, false>(force, out))
+                             : (nt ? aos_pull_kernel<T, 1, true>(force, out) : aos_pull_kernel<T, 1, false>(force, out));
+    return hipLaunchKernel(k, grid, block, args, 0, st);
+}
+
 template <typename T>
 hipError_t launch_step_mo(int layout, int kind, T* a, T* b, const LaunchGeom& lg, const LaunchPhys& lp,
                           const MomOut<T>& mo, hipStream_t st)
@@ -363,6 +405,8 @@ hipError_t launch_step_mo(int layout, int kind, T* a, T* b, const LaunchGeom& lg
     const int bnd = boundary_instance(lg);
     if (LBM_AOS_EVEN_STAGED && layout == kCollision && kind == kAAEven && mo.partial == nullptr)
         return launch_aos_even<T>(a, lg, p, mo, lp.has_force, st);
+    if (LBM_AOS_PULL_STAGED && layout == kCollision && kind == kAB && bnd != 2 && mo.partial == nullptr)
+        return launch_aos_pull<T>(a, b, lg, p, mo, bnd, lp.has_force, st);
     if (LBM_AOS_TILED && layout == kCollision && kind == kAAOdd && bnd == 1 && mo.partial == nullptr)
         return launch_aos_odd<T>(a, lg, p, mo, lp.has_force, st);
     switch (layout) {
