@@ -83,7 +83,9 @@ inline Shape make_shape(const LaunchGeom& lg, bool xcd_chunks = false)
 //     0.574); SoA pull: 2 without (0.450 -> 0.420), 3 with (0.651 -> 0.566);
 //   SoAoS pull with solids: 5 (0.519 -> 0.497); SoAoS odd step: no cap;
 //   AoS odd step without solids: 2 (1.709 -> 1.044); AoS pull: 2 without
-//     (0.929 -> 0.824), 3 with (0.743 -> 0.718); AoS odd step with solids:
+//     (0.929 -> 0.824), 3 with (0.743 -> 0.718) (step_kernel; the AoS pull
+//     now runs with staged writes, aos_pull_staged_kernel, except on boxes
+//     with open faces and in fused momentum-exchange steps); AoS odd step with solids:
 //     no cap (1.18 -> 1.27 at 2; it now runs on the plane tiles, whose own
 //     LDS leaves room for three workgroups per CU).
 // The caps apply only to lattices larger than the 256 MB last-level cache:
