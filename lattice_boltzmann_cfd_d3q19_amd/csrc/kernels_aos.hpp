@@ -1,7 +1,8 @@
-// kernels_aos.hpp -- the in-place steps of the AoS (collision) layout staged
-// through LDS: the odd step on boxes with solid cells or walls, one plane tile
-// at a time, and the even step, one run of consecutive records at a time (at
-// the end of this file).
+// kernels_aos.hpp -- steps of the AoS (collision) layout staged through LDS:
+// the odd in-place step on boxes with solid cells or walls, one plane tile at
+// a time; the even in-place step, one run of consecutive records at a time;
+// and the two-lattice pull, whose writes are staged the same way (the last
+// two at the end of this file).
 //
 // In the AoS layout (PortLBM page, section 3.2, Fig. 2: the 19 populations of
 // a cell side by side, a 76-byte record in fp32) the odd step of the in-place
